@@ -1,0 +1,202 @@
+/*
+ * attn_mi355x.h -- C ABI of the exact tiled attention forward library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The library computes exact attention forward
+ *
+ *     O = softmax(scale * Q K^T [softcapped] + mask) V,   LSE = ln sum exp(...)
+ *
+ * in tiles with an online softmax that keeps a running row max and row sum
+ * (FlashAttention-2 structure).  The rescale of the running output and sum
+ * is skipped whenever the row max rises by no more than `rescale_threshold`
+ * in log2 units of the scaled score; on a skip the running max keeps its
+ * previous value ("max lagging"), so output, row sum and probabilities stay
+ * on one base and the result is exact.  Sources: release page "v1.7 /
+ * flash_attn 2.9.2.post1" of the ussoewwin flash-attention fork, section 1.2
+ * (threshold 8.0 for 16-bit inputs, lagging, P <= exp2(8) = 256) and
+ * section 2 (public features: causal, window, softcap, varlen, kv-cache);
+ * release page "FA2 2.9.0 Kernel Changes in v1.2", sections 1-3 (the
+ * rescale step, the exp2-domain softmax and its -inf guard, the split-KV
+ * kernel).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors are device pointers owned by the caller.  The library never
+ *    allocates, frees or synchronises; every call only enqueues kernels on
+ *    `stream` (a hipStream_t; NULL = the default stream) and returns.
+ *  - Q, K, V and O share one 16-bit dtype (ATTN_DTYPE_F16 or _BF16); LSE and
+ *    all workspace partials are fp32.
+ *  - Strides are in elements (not bytes), int64.  The head dimension is
+ *    contiguous (stride 1).  Every pointer must be 16-byte aligned and every
+ *    stride a multiple of 8 elements; row strides must be below 2^24.
+ *  - head_dim must be 64, 128 or 256.  heads_q must be a multiple of
+ *    heads_kv; query head h reads KV head h / (heads_q / heads_kv).
+ *  - Masks are aligned to the bottom-right corner: with off = Sk - Sq, key j
+ *    is visible to query row i iff (!causal || j <= i + off) and
+ *    (window_left < 0 || j >= i + off - window_left) and
+ *    (window_right < 0 || j <= i + off + window_right).  -1 means unbounded;
+ *    0 is a real (zero-width) bound, so window (0, 0) selects the diagonal.
+ *  - softcap > 0 replaces each scaled score t by softcap * tanh(t / softcap)
+ *    before masking; 0 disables it.
+ *  - softmax_scale <= 0 selects 1/sqrt(head_dim).
+ *  - rescale_threshold < 0 selects the default 8.0 (16-bit inputs); 0 gives
+ *    the classic always-rescale online softmax.  Any value >= 0 gives the
+ *    same exact result up to rounding.
+ *  - LSE is natural-log, fp32.  A query row with no visible key gets O = 0
+ *    and LSE = -inf.  `lse` may be NULL.
+ *  - Results are deterministic: identical inputs give bit-identical outputs.
+ *  - Return value: ATTN_OK (0) or a negative ATTN_E_* code.  All arguments
+ *    are validated on the host before anything is enqueued; on error nothing
+ *    is launched and outputs are untouched.  An empty problem (no query
+ *    rows) returns ATTN_OK and launches nothing.
+ */
+#ifndef ATTN_MI355X_H
+#define ATTN_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_VERSION 100
+
+enum attn_status {
+  ATTN_OK = 0,
+  ATTN_E_NULL = -1,        /* a required pointer is NULL */
+  ATTN_E_SHAPE = -2,       /* negative or inconsistent sizes, bad cu_seqlens host hints */
+  ATTN_E_HEADS = -3,       /* heads_q % heads_kv != 0 or a head count < 1 */
+  ATTN_E_UNSUPPORTED = -4, /* dtype or head_dim not supported */
+  ATTN_E_WINDOW = -5,      /* window bound < -1 */
+  ATTN_E_WORKSPACE = -6,   /* workspace missing or smaller than required */
+  ATTN_E_LAUNCH = -7,      /* the HIP runtime reported an error at launch */
+  ATTN_E_ALIGN = -8,       /* pointer or stride alignment / stride range violated */
+  ATTN_E_ARG = -9          /* other invalid scalar argument (scale, softcap, splits) */
+};
+
+enum attn_dtype { ATTN_DTYPE_F16 = 0, ATTN_DTYPE_BF16 = 1 };
+
+/* Fields shared by the three entry points: features of the softmax. */
+typedef struct attn_softmax_opts {
+  float softmax_scale;     /* <= 0: 1/sqrt(head_dim) */
+  int32_t causal;          /* 0 or 1 */
+  int32_t window_left;     /* -1 unbounded, >= 0 bound */
+  int32_t window_right;    /* -1 unbounded, >= 0 bound */
+  float softcap;           /* 0: off, > 0: tanh cap */
+  float rescale_threshold; /* < 0: default 8.0 */
+} attn_softmax_opts;
+
+/*
+ * attn_fwd -- dense batched attention forward.
+ *   q [batch, seqlen_q, heads_q, head_dim]
+ *   k, v [batch, seqlen_k, heads_kv, head_dim]
+ *   o like q (written), lse [batch, heads_q, seqlen_q] contiguous fp32 (written, may be NULL)
+ * Source: "v1.7 / flash_attn 2.9.2.post1" sections 1.2 and 2 (flash_attn_func
+ * features); section 4.6 gives the LSE shape [B, H, S].
+ */
+typedef struct attn_fwd_args {
+  int32_t dtype;
+  int32_t batch, seqlen_q, seqlen_k, heads_q, heads_kv, head_dim;
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int64_t q_batch_stride, q_row_stride, q_head_stride;
+  int64_t k_batch_stride, k_row_stride, k_head_stride;
+  int64_t v_batch_stride, v_row_stride, v_head_stride;
+  int64_t o_batch_stride, o_row_stride, o_head_stride;
+  attn_softmax_opts opts;
+} attn_fwd_args;
+
+int attn_fwd(const attn_fwd_args* args, void* stream);
+
+/*
+ * attn_fwd_varlen -- packed variable-length attention forward
+ * (flash_attn_varlen_func in "v1.7 / flash_attn 2.9.2.post1" section 2).
+ *   q [total_q, heads_q, head_dim], k, v [total_k, heads_kv, head_dim]
+ *   cu_seqlens_q, cu_seqlens_k: device int32 [batch + 1], prefix sums from 0,
+ *     non-decreasing; sequence b owns rows cu[b] .. cu[b+1]-1 and attends only
+ *     within itself (masks apply per sequence).
+ *   max_seqlen_q / max_seqlen_k: host upper bounds of the per-sequence lengths
+ *     (used for the grid; a sequence longer than its bound is truncated).
+ *   o like q, lse [heads_q, total_q] contiguous fp32 (may be NULL).
+ *   workspace: attn_varlen_workspace_bytes() bytes of device memory for the
+ *     tile schedule (may be NULL when that size is 0).
+ */
+typedef struct attn_varlen_args {
+  int32_t dtype;
+  int32_t batch, total_q, total_k, max_seqlen_q, max_seqlen_k, heads_q, heads_kv, head_dim;
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const int32_t* cu_seqlens_q;
+  const int32_t* cu_seqlens_k;
+  int64_t q_row_stride, q_head_stride;
+  int64_t k_row_stride, k_head_stride;
+  int64_t v_row_stride, v_head_stride;
+  int64_t o_row_stride, o_head_stride;
+  attn_softmax_opts opts;
+} attn_varlen_args;
+
+size_t attn_varlen_workspace_bytes(int32_t batch, int32_t max_seqlen_q, int32_t heads_q,
+                                   int32_t heads_kv, int32_t head_dim);
+int attn_fwd_varlen(const attn_varlen_args* args, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/*
+ * attn_fwd_kvcache -- attention of new queries against a KV cache, through
+ * the split-KV kernel plus a log-sum-exp combine (flash_attn_with_kvcache in
+ * "v1.7 / flash_attn 2.9.2.post1" section 2; the split-KV kernel is the
+ * compute_attn_1rowblock_splitkv row of the call-site table in "FA2 2.9.0
+ * Kernel Changes in v1.2" section 3).
+ *   q [batch, seqlen_q, heads_q, head_dim]
+ *   k_cache, v_cache [batch, seqlen_k (capacity), heads_kv, head_dim]
+ *   cache_seqlens: device int32 [batch] valid lengths (<= seqlen_k), or NULL
+ *     for "all seqlen_k rows valid".  Rows at or past a sequence's valid
+ *     length are never read, so they may hold anything (even NaN).
+ *   num_splits: number of KV splits (0 = attn_kvcache_num_splits()).
+ *   o like q, lse [batch, heads_q, seqlen_q] contiguous fp32 (may be NULL).
+ *   workspace: attn_kvcache_workspace_bytes() bytes (fp32 partial outputs and
+ *     LSEs of every split); may be NULL when that size is 0 (one split).
+ * The result is independent of num_splits up to fp32 rounding.
+ */
+typedef struct attn_kvcache_args {
+  int32_t dtype;
+  int32_t batch, seqlen_q, seqlen_k, heads_q, heads_kv, head_dim;
+  int32_t num_splits;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* cache_seqlens;
+  void* o;
+  float* lse;
+  int64_t q_batch_stride, q_row_stride, q_head_stride;
+  int64_t k_batch_stride, k_row_stride, k_head_stride;
+  int64_t v_batch_stride, v_row_stride, v_head_stride;
+  int64_t o_batch_stride, o_row_stride, o_head_stride;
+  attn_softmax_opts opts;
+} attn_kvcache_args;
+
+/* Split count the library picks when num_splits == 0 (never forced to 1
+ * when the problem is too small to fill the GPU). */
+int32_t attn_kvcache_num_splits(int32_t batch, int32_t seqlen_q, int32_t heads_q,
+                                int32_t heads_kv, int32_t seqlen_k, int32_t head_dim);
+size_t attn_kvcache_workspace_bytes(int32_t batch, int32_t seqlen_q, int32_t heads_q,
+                                    int32_t head_dim, int32_t num_splits);
+int attn_fwd_kvcache(const attn_kvcache_args* args, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/* Human-readable text of a status code (static storage). */
+const char* attn_status_string(int status);
+/* ATTN_VERSION of the built library. */
+int attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_MI355X_H */

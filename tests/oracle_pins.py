@@ -1,0 +1,470 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each ``pin_*`` function raises AssertionError (or any exception) when the
+oracle disagrees with a closed form, an invariant, a brute-force evaluation,
+a library routine or a number printed on the pages.  ``test_oracle_pins.py``
+runs them; ``test_oracle_mutations.py`` plants plausible mistakes in the
+oracle and checks that some pin catches each one.
+
+Page citations: [v1.7] = release page "v1.7 / flash_attn 2.9.2.post1";
+[v1.2] = release page "FA2 2.9.0 Kernel Changes in v1.2"; [aichaai] =
+Dao-AILab/flash-attention project page (release notes).
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+import oracle
+from oracle import attention as oatt
+from oracle import tiled as otiled
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _visible_count(i, sq, sk, causal, left, right):
+    """Closed-form number of visible keys of row i (bottom-right aligned band)."""
+    off = sk - sq
+    hi = sk - 1
+    lo = 0
+    if causal:
+        hi = min(hi, i + off)
+    if right >= 0:
+        hi = min(hi, i + off + right)
+    if left >= 0:
+        lo = max(lo, i + off - left)
+    return max(0, hi - lo + 1), lo, hi
+
+
+# ---------------------------------------------------------------- closed forms
+
+def pin_uniform_scores():
+    """Q = 0 makes every score 0 (and tanh(0) = 0): O_i = mean of the visible V_j, LSE_i = ln n_i."""
+    rng = _rng(1)
+    cases = [
+        dict(sq=24, sk=24, causal=False, window=(-1, -1), softcap=0.0),
+        dict(sq=24, sk=24, causal=True, window=(-1, -1), softcap=0.0),
+        dict(sq=16, sk=40, causal=True, window=(-1, -1), softcap=30.0),
+        dict(sq=40, sk=16, causal=True, window=(-1, -1), softcap=0.0),
+        dict(sq=30, sk=30, causal=False, window=(5, 3), softcap=0.0),
+        dict(sq=20, sk=33, causal=True, window=(7, -1), softcap=5.0),
+        dict(sq=12, sk=12, causal=False, window=(0, 0), softcap=0.0),
+    ]
+    for c in cases:
+        q = np.zeros((1, c["sq"], 2, 8))
+        k = rng.standard_normal((1, c["sk"], 1, 8))
+        v = rng.standard_normal((1, c["sk"], 1, 8))
+        out, lse = oracle.attention_ref(q, k, v, scale=0.3, causal=c["causal"], window=c["window"],
+                                        softcap=c["softcap"])
+        for i in range(c["sq"]):
+            n, lo, hi = _visible_count(i, c["sq"], c["sk"], c["causal"], *c["window"])
+            for h in range(2):
+                if n == 0:
+                    assert np.all(out[0, i, h] == 0.0) and lse[0, h, i] == -np.inf, (c, i)
+                else:
+                    mean = v[0, lo:hi + 1, 0].sum(axis=0) / n
+                    assert np.allclose(out[0, i, h], mean, rtol=0, atol=1e-13), (c, i)
+                    assert abs(lse[0, h, i] - math.log(n)) < 1e-13, (c, i)
+
+
+def pin_one_hot_scores():
+    """Orthogonal keys with a margin of 800 nats: O_i = V_pi(i), LSE_i = t_i,pi(i)."""
+    rng = _rng(2)
+    sk, d = 16, 32
+    alpha, beta, scale = 4.0, 200.0, 1.0         # margin 800 nats: exp overflows without a max shift
+    k = np.zeros((1, sk, 1, d))
+    for j in range(sk):
+        k[0, j, 0, j] = alpha                        # K_j = alpha * e_j
+    v = rng.standard_normal((1, sk, 1, d))
+    perm = rng.permutation(sk)
+    q = np.zeros((1, sk, 1, d))
+    for i in range(sk):
+        q[0, i, 0, perm[i]] = beta                   # <Q_i, K_j> = alpha*beta*[j == perm[i]]
+    out, lse = oracle.attention_ref(q, k, v, scale=scale)
+    for i in range(sk):
+        assert np.allclose(out[0, i, 0], v[0, perm[i], 0], rtol=0, atol=1e-12)
+        assert abs(lse[0, 0, i] - alpha * beta * scale) < 1e-12
+    # causal: row i sees keys 0..i, and the hot key is i itself
+    q2 = np.zeros((1, sk, 1, d))
+    for i in range(sk):
+        q2[0, i, 0, i] = beta
+    out2, lse2 = oracle.attention_ref(q2, k, v, scale=scale, causal=True)
+    for i in range(sk):
+        assert np.allclose(out2[0, i, 0], v[0, i, 0], rtol=0, atol=1e-12)
+        assert abs(lse2[0, 0, i] - alpha * beta * scale) < 1e-12
+
+
+def pin_softcap_single_key():
+    """Window (0,0) leaves one key, so LSE_i = cap * tanh(scale * <Q_i, K_i> / cap) exactly."""
+    rng = _rng(3)
+    s, d, cap, scale = 10, 16, 2.5, 0.7
+    q = rng.standard_normal((1, s, 1, d)) * 2.0
+    k = rng.standard_normal((1, s, 1, d)) * 2.0
+    v = rng.standard_normal((1, s, 1, d))
+    _, lse = oracle.attention_ref(q, k, v, scale=scale, window=(0, 0), softcap=cap)
+    for i in range(s):
+        dot = math.fsum(float(q[0, i, 0, x]) * float(k[0, i, 0, x]) for x in range(d))
+        assert abs(lse[0, 0, i] - cap * math.tanh(scale * dot / cap)) < 1e-12
+    # |t| < cap always, and cap -> infinity reduces to no softcap
+    out_a, lse_a = oracle.attention_ref(q * 10, k, v, softcap=cap)
+    _, _, p = oracle.attention_ref(q * 10, k, v, softcap=cap, return_probs=True)
+    assert np.all(np.isfinite(lse_a))
+    assert np.all(lse_a <= cap + math.log(s) + 1e-12)
+    out_b, lse_b = oracle.attention_ref(q, k, v, softcap=1e9)
+    out_c, lse_c = oracle.attention_ref(q, k, v)
+    assert np.allclose(out_b, out_c, atol=1e-9) and np.allclose(lse_b, lse_c, atol=1e-9)
+
+
+# ---------------------------------------------------------------- invariants
+
+def pin_rows_sum_to_one():
+    """P >= 0, each row with visible keys sums to 1, and P = 0 exactly off the visible band."""
+    rng = _rng(4)
+    for (sq, sk, causal, window) in [(20, 20, True, (-1, -1)), (13, 29, True, (4, -1)),
+                                     (25, 25, False, (3, 6)), (30, 11, True, (-1, -1))]:
+        q = rng.standard_normal((1, sq, 1, 8))
+        k = rng.standard_normal((1, sk, 1, 8))
+        v = rng.standard_normal((1, sk, 1, 8))
+        _, lse, p = oracle.attention_ref(q, k, v, causal=causal, window=window, return_probs=True)
+        assert np.all(p >= 0)
+        for i in range(sq):
+            n, lo, hi = _visible_count(i, sq, sk, causal, *window)
+            row = p[0, 0, i]
+            if n == 0:
+                assert np.all(row == 0) and lse[0, 0, i] == -np.inf
+                continue
+            assert abs(row.sum() - 1.0) < 1e-13
+            assert np.count_nonzero(row) == n
+            assert np.all(row[:lo] == 0) and np.all(row[hi + 1:] == 0)
+
+
+def pin_permutation_invariance():
+    """Without a mask, permuting the (K_j, V_j) pairs jointly leaves O and LSE unchanged."""
+    rng = _rng(5)
+    q = rng.standard_normal((2, 9, 4, 16))
+    k = rng.standard_normal((2, 23, 2, 16))
+    v = rng.standard_normal((2, 23, 2, 16))
+    perm = rng.permutation(23)
+    o1, l1 = oracle.attention_ref(q, k, v, softcap=3.0)
+    o2, l2 = oracle.attention_ref(q, k[:, perm], v[:, perm], softcap=3.0)
+    assert np.allclose(o1, o2, atol=1e-13) and np.allclose(l1, l2, atol=1e-13)
+
+
+def pin_bruteforce_tiny():
+    """Python-float evaluation (math.fsum, no max shift) of LSE and O for tiny shapes."""
+    rng = _rng(6)
+    for (sq, sk, causal, window, cap) in [(5, 7, True, (-1, -1), 0.0), (6, 6, False, (1, 2), 0.0),
+                                          (4, 9, False, (-1, -1), 1.5), (7, 3, True, (2, -1), 0.0)]:
+        d, scale = 4, 0.9
+        q = rng.standard_normal((1, sq, 1, d))
+        k = rng.standard_normal((1, sk, 1, d))
+        v = rng.standard_normal((1, sk, 1, d))
+        out, lse = oracle.attention_ref(q, k, v, scale=scale, causal=causal, window=window,
+                                        softcap=cap)
+        off = sk - sq
+        for i in range(sq):
+            ws = []
+            for j in range(sk):
+                visible = True
+                if causal and j > i + off:
+                    visible = False
+                if window[0] >= 0 and j < i + off - window[0]:
+                    visible = False
+                if window[1] >= 0 and j > i + off + window[1]:
+                    visible = False
+                if not visible:
+                    continue
+                s = scale * math.fsum(float(q[0, i, 0, x]) * float(k[0, j, 0, x]) for x in range(d))
+                if cap > 0:
+                    s = cap * math.tanh(s / cap)
+                ws.append((math.exp(s), j))
+            if not ws:
+                assert lse[0, 0, i] == -np.inf and np.all(out[0, i, 0] == 0)
+                continue
+            z = math.fsum(w for w, _ in ws)
+            assert abs(lse[0, 0, i] - math.log(z)) < 1e-13
+            for x in range(d):
+                ref = math.fsum(w * float(v[0, j, 0, x]) for w, j in ws) / z
+                assert abs(out[0, i, 0, x] - ref) < 1e-13
+
+
+def pin_lse_reconstructs_output():
+    """exp(LSE) equals the sum of exp(t) by brute force; O equals the LSE-weighted V sum."""
+    rng = _rng(7)
+    q = rng.standard_normal((1, 11, 1, 8))
+    k = rng.standard_normal((1, 11, 1, 8))
+    v = rng.standard_normal((1, 11, 1, 8))
+    out, lse, p = oracle.attention_ref(q, k, v, causal=True, return_probs=True)
+    # P rows are the softmax of the visible scores: P_ij / P_i0 = exp(t_ij - t_i0)
+    for i in range(11):
+        t = (q[0, i, 0] @ k[0, :i + 1, 0].T) / math.sqrt(8)
+        assert np.allclose(p[0, 0, i, :i + 1] / p[0, 0, i, 0], np.exp(t - t[0]), rtol=1e-12)
+        assert abs(lse[0, 0, i] - (t[0] - math.log(p[0, 0, i, 0]))) < 1e-12
+    assert np.allclose(out[0, :, 0], p[0, 0] @ v[0, :, 0], atol=1e-13)
+
+
+# ---------------------------------------------------------------- page special cases
+
+def pin_page_window_00_is_v():
+    """[v1.7] section 4.6: window (0,0) gives output == V (max abs diff 0)."""
+    probe = _golden("page_v17_probes.json")
+    rng = _rng(8)
+    q = rng.standard_normal((2, 64, 4, 16))
+    k = rng.standard_normal((2, 64, 2, 16))
+    v = rng.standard_normal((2, 64, 2, 16))
+    out, _ = oracle.attention_ref(q, k, v, window=(0, 0))
+    vv = np.repeat(v, 2, axis=2)
+    assert np.max(np.abs(out - vv)) == probe["window_0_0_max_abs_diff_vs_v"]
+
+
+def pin_page_single_row_and_causal_row0():
+    """[v1.7] section 4.6 S=1 probe and causal row 0: one visible key, O = V_0 and LSE = t_00."""
+    rng = _rng(9)
+    q = rng.standard_normal((1, 1, 1, 16))
+    k = rng.standard_normal((1, 1, 1, 16))
+    v = rng.standard_normal((1, 1, 1, 16))
+    out, lse = oracle.attention_ref(q, k, v)
+    assert np.array_equal(out[0, 0, 0], v[0, 0, 0])
+    assert abs(lse[0, 0, 0] - float(q[0, 0, 0] @ k[0, 0, 0]) / 4.0) < 1e-13
+    q = rng.standard_normal((1, 32, 1, 16))
+    k = rng.standard_normal((1, 32, 1, 16))
+    v = rng.standard_normal((1, 32, 1, 16))
+    out, _ = oracle.attention_ref(q, k, v, causal=True)
+    assert np.array_equal(out[0, 0, 0], v[0, 0, 0])
+
+
+def pin_page_lse_units():
+    """[v1.7] section 4.6 LSE probe: shape [B, H, S]; its top end fits natural-log units."""
+    probe = _golden("page_v17_probes.json")["lse_probe"]
+    b, h, s, d = probe["batch"], probe["heads"], probe["seqlen"], probe["head_dim"]
+    rng = _rng(10)
+    q = np.zeros((b, s, h, d))
+    k = rng.standard_normal((b, s, h, d))
+    v = rng.standard_normal((b, s, h, d))
+    _, lse = oracle.attention_ref(q, k, v, causal=True)
+    assert list(lse.shape) == probe["shape"]
+    lo, hi = probe["range"]
+    assert abs(lse.max() - hi) < 0.01          # ln(512) = 6.2383; log2 would give 9.0
+    assert abs(lse.min() - lo) < 0.03
+
+
+def pin_decode_is_last_prefill_row():
+    """A one-row query against a cache equals the last row of causal prefill on the same K/V."""
+    rng = _rng(11)
+    q = rng.standard_normal((2, 17, 4, 16))
+    k = rng.standard_normal((2, 17, 2, 16))
+    v = rng.standard_normal((2, 17, 2, 16))
+    out, lse = oracle.attention_ref(q, k, v, causal=True)
+    kc = np.concatenate([k, np.full((2, 5, 2, 16), np.nan)], axis=1)   # NaN past the valid length
+    vc = np.concatenate([v, np.full((2, 5, 2, 16), np.nan)], axis=1)
+    o1, l1 = oracle.attention_kvcache_ref(q[:, -1:], kc, vc, cache_seqlens=[17, 17], causal=True)
+    assert np.allclose(o1[:, 0], out[:, -1], atol=1e-13)
+    assert np.allclose(l1[:, :, 0], lse[:, :, -1], atol=1e-13)
+
+
+# ---------------------------------------------------------------- library routines
+
+def _sdpa_ref(q, k, v, scale, mask_bool):
+    """torch scaled_dot_product_attention in fp64 on the CPU ([B, S, H, D] in, [B, S, H, D] out)."""
+    qt = torch.from_numpy(q).permute(0, 2, 1, 3)
+    g = q.shape[2] // k.shape[2]
+    kt = torch.from_numpy(np.repeat(k, g, axis=2)).permute(0, 2, 1, 3).contiguous()
+    vt = torch.from_numpy(np.repeat(v, g, axis=2)).permute(0, 2, 1, 3).contiguous()
+    m = None if mask_bool is None else torch.from_numpy(mask_bool)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=m, scale=scale)
+    return o.permute(0, 2, 1, 3).numpy()
+
+
+def pin_torch_sdpa():
+    """The pages' own accuracy reference is PyTorch SDPA; cross-check dense, causal, window and GQA."""
+    rng = _rng(12)
+    b, s, hq, hkv, d = 2, 37, 6, 2, 16
+    q = rng.standard_normal((b, s, hq, d))
+    k = rng.standard_normal((b, s, hkv, d))
+    v = rng.standard_normal((b, s, hkv, d))
+    scale = 0.37
+    o, _ = oracle.attention_ref(q, k, v, scale=scale)
+    assert np.allclose(o, _sdpa_ref(q, k, v, scale, None), atol=1e-12)
+    tri = np.tril(np.ones((s, s), dtype=bool))
+    o, _ = oracle.attention_ref(q, k, v, scale=scale, causal=True)
+    assert np.allclose(o, _sdpa_ref(q, k, v, scale, tri), atol=1e-12)
+    ii, jj = np.meshgrid(np.arange(s), np.arange(s), indexing="ij")
+    band = (jj >= ii - 4) & (jj <= ii + 2)
+    o, _ = oracle.attention_ref(q, k, v, scale=scale, window=(4, 2))
+    assert np.allclose(o, _sdpa_ref(q, k, v, scale, band), atol=1e-12)
+
+
+def pin_varlen_block_diagonal():
+    """Packed sequences = one long sequence under a block-diagonal causal mask (torch SDPA)."""
+    rng = _rng(13)
+    lens = [5, 1, 12, 7]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    t = int(cu[-1])
+    q = rng.standard_normal((t, 4, 8))
+    k = rng.standard_normal((t, 2, 8))
+    v = rng.standard_normal((t, 2, 8))
+    o, lse = oracle.attention_varlen_ref(q, k, v, cu, cu, causal=True)
+    mask = np.zeros((t, t), dtype=bool)
+    for a, z in zip(cu[:-1], cu[1:]):
+        mask[a:z, a:z] = np.tril(np.ones((z - a, z - a), dtype=bool))
+    ref = _sdpa_ref(q[None], k[None], v[None], 1.0 / math.sqrt(8), mask)[0]
+    assert np.allclose(o, ref, atol=1e-12)
+    assert lse.shape == (4, t)
+
+
+def pin_gqa_is_repeated_mha():
+    """GQA equals MHA with each KV head repeated for its group of consecutive query heads."""
+    rng = _rng(14)
+    q = rng.standard_normal((1, 19, 8, 16))
+    k = rng.standard_normal((1, 19, 2, 16))
+    v = rng.standard_normal((1, 19, 2, 16))
+    o1, l1 = oracle.attention_ref(q, k, v, causal=True)
+    o2, l2 = oracle.attention_ref(q, np.repeat(k, 4, axis=2), np.repeat(v, 4, axis=2), causal=True)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+# ---------------------------------------------------------------- the tiled method
+
+def _ramp_inputs(seed, s=256, d=32, heads=2):
+    rng = _rng(seed)
+    q = rng.standard_normal((1, s, heads, d))
+    k = rng.standard_normal((1, s, heads, d))
+    ramp = 1.0 + 3.0 * (np.arange(s) // 32) / (s // 32 - 1)
+    k = k * ramp[None, :, None, None]
+    v = rng.standard_normal((1, s, heads, d))
+    return q, k, v
+
+
+def pin_tiled_equals_definition():
+    """[v1.7] section 1.2: with max lagging any threshold gives the exact output and LSE."""
+    q, k, v = _ramp_inputs(15)
+    ref_o, ref_l = oracle.attention_ref(q, k, v, causal=True)
+    seen_skip = seen_rescale = False
+    for tau in (0.0, 8.0):
+        for bk in (16, 64, 128):
+            for order in ("ascending", "descending"):
+                o, l, st = oracle.tiled_ref(q, k, v, causal=True, tau=tau, block_k=bk, order=order,
+                                            return_stats=True)
+                assert np.max(np.abs(o - ref_o)) < 1e-12 and np.max(np.abs(l - ref_l)) < 1e-12
+                if tau == 8.0 and order == "ascending":
+                    seen_skip |= st["skips"] > 0
+                    seen_rescale |= st["rescales"] > 0
+    assert seen_skip and seen_rescale
+    for kw in (dict(window=(40, 0)), dict(softcap=3.0), dict(window=(17, 9), causal=False)):
+        o, l = oracle.tiled_ref(q, k, v, tau=8.0, block_k=32, **kw)
+        ro, rl = oracle.attention_ref(q, k, v, **kw)
+        assert np.max(np.abs(o - ro)) < 1e-12 and np.max(np.abs(rl - l)) < 1e-12
+
+
+def _two_block_case(d_log2):
+    """Two KV blocks, one key each; the second block's score is higher by d_log2 in log2 units."""
+    t1 = 0.3
+    t2 = t1 + d_log2 * math.log(2.0)
+    q = np.zeros((1, 1, 1, 2))
+    q[0, 0, 0, 0] = 1.0
+    k = np.zeros((1, 2, 1, 2))
+    k[0, 0, 0, 0] = t1
+    k[0, 1, 0, 0] = t2
+    v = np.zeros((1, 2, 1, 2))
+    v[0, 0, 0, 0] = 1.0                                  # block 1 writes into component 0
+    v[0, 1, 0, 1] = 1.0                                  # block 2 writes into component 1
+    return q, k, v
+
+
+def pin_page_threshold_numbers():
+    """[v1.7] section 1.2 and [v1.2] section 1: the numbers printed about the threshold.
+
+    A max rise of exactly 8 (log2 units) is skipped at tau = 8.  Keeping the
+    new max (the superseded rule) then overweights the stale block by
+    2^8 = 256; lagging keeps the exact weights and lets P reach exactly 256.
+    At the old 0.01 threshold the stale factor is 2^0.01 (scale >= 0.993, error < 0.7%).
+    """
+    g = _golden("page_v17_threshold.json")
+    for d_log2, tau, key in ((8.0, g["tau_16bit"], "overweight_without_lagging_at_tau8"),
+                             (0.01, -g["old_threshold"], None)):
+        q, k, v = _two_block_case(d_log2)
+        exact_ratio = 2.0 ** (-d_log2)                   # w1 / w2 of the exact softmax
+        o_lag, _, st = oracle.tiled_ref(q, k, v, scale=1.0, tau=tau, block_k=1,
+                                        return_stats=True)
+        assert st["skips"] == 1 and st["rescales"] == 0
+        assert abs(o_lag[0, 0, 0, 0] / o_lag[0, 0, 0, 1] - exact_ratio) < 1e-12
+        o_bad, _ = oracle.tiled_ref(q, k, v, scale=1.0, tau=tau, block_k=1, lagging=False)
+        overweight = (o_bad[0, 0, 0, 0] / o_bad[0, 0, 0, 1]) / exact_ratio
+        if key is not None:
+            assert abs(overweight - g[key]) < 1e-9
+            assert abs(st["max_p"] - g["p_bound_with_lagging_at_tau8"]) < 1e-9
+            assert st["max_p"] < g["fp16_max"] < g["bf16_max"]
+        else:
+            assert 1.0 / overweight >= g["old_threshold_min_scale"]
+            assert overweight - 1.0 < g["old_threshold_max_rel_error"]
+
+
+def pin_nonlagging_is_wrong_at_tau8():
+    """The superseded keep-new-max rule at tau = 8 is far off on a rising-max input."""
+    q, k, v = _ramp_inputs(16)
+    ref_o, ref_l = oracle.attention_ref(q, k, v, causal=True)
+    o, l = oracle.tiled_ref(q, k, v, causal=True, tau=8.0, block_k=32, lagging=False)
+    assert oracle.rel_linf(o, ref_o) > 0.05
+    assert np.max(np.abs(l - ref_l)) > 0.5
+
+
+def pin_p_bound():
+    """[v1.7] section 1.2: with lagging at tau = 8, P never exceeds exp2(8) = 256."""
+    q, k, v = _ramp_inputs(17, s=512)
+    _, _, st = oracle.tiled_ref(q * 3.0, k, v, causal=True, tau=8.0, block_k=32, return_stats=True)
+    assert st["max_p"] <= 256.0 + 1e-9 and st["skips"] > 0
+
+
+def pin_bf16_rounding_helper():
+    """round_to_16bit('bf16') is round-to-nearest-even, as torch's own conversion."""
+    x = np.random.default_rng(18).standard_normal(4096) * 37.0
+    x = np.concatenate([x, [1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -0.0, 256.0, 65504.0]])
+    ours = otiled.round_to_16bit(x, "bf16")
+    ref = torch.from_numpy(x).to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(ours, ref)
+
+
+def pin_metrics():
+    """rel_Linf is max|diff| / max|ref| (the page's max_abs / rel_Linf columns agree with this)."""
+    ref = np.array([0.5, -0.25, 0.1])
+    out = ref + np.array([1e-3, -2e-3, 0.0])
+    assert abs(oracle.rel_linf(out, ref) - 2e-3 / 0.5) < 1e-15
+    assert abs(oracle.cosine(ref, ref) - 1.0) < 1e-15
+    assert oracle.lse_max_abs_err(np.array([-np.inf, 1.0]), np.array([-np.inf, 1.5])) == 0.5
+    assert oracle.lse_max_abs_err(np.array([0.0, 1.0]), np.array([-np.inf, 1.0])) == float("inf")
+
+
+ALL_PINS = [
+    pin_uniform_scores,
+    pin_one_hot_scores,
+    pin_softcap_single_key,
+    pin_rows_sum_to_one,
+    pin_permutation_invariance,
+    pin_bruteforce_tiny,
+    pin_lse_reconstructs_output,
+    pin_page_window_00_is_v,
+    pin_page_single_row_and_causal_row0,
+    pin_page_lse_units,
+    pin_decode_is_last_prefill_row,
+    pin_torch_sdpa,
+    pin_varlen_block_diagonal,
+    pin_gqa_is_repeated_mha,
+    pin_tiled_equals_definition,
+    pin_page_threshold_numbers,
+    pin_nonlagging_is_wrong_at_tau8,
+    pin_p_bound,
+    pin_bf16_rounding_helper,
+    pin_metrics,
+]

@@ -1,0 +1,146 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that some pin catches each.
+
+This shows the pins are strong enough: a dropped scale, an off-by-one mask,
+top-left instead of bottom-right alignment, a wrong GQA head map, a
+transposed operand, softcap on the unscaled score, log2 instead of natural
+log, a missing max shift, a window bound read as unbounded, or the
+superseded keep-new-max skip rule must each make at least one pin fail.
+"""
+
+import contextlib
+
+import numpy as np
+import pytest
+
+import oracle_pins
+from oracle import attention as oatt
+from oracle import tiled as otiled
+
+_orig_mask = oatt.allowed_mask
+_orig_scores = oatt.transformed_scores
+_orig_head = oatt.kv_head_of
+_orig_one_head = oatt._one_head
+_orig_tiled_one = otiled._tiled_one_head
+
+
+def _mask_causal_strict(sq, sk, rows, causal=False, wl=-1, wr=-1):
+    ok = _orig_mask(sq, sk, rows, False, wl, wr)
+    if causal:
+        i = np.asarray(rows)[:, None]
+        j = np.arange(sk)[None, :]
+        ok &= j < i + (sk - sq)
+    return ok
+
+
+def _mask_top_left(sq, sk, rows, causal=False, wl=-1, wr=-1):
+    return _orig_mask(sk, sk, rows, causal, wl, wr)
+
+
+def _mask_window_zero_unbounded(sq, sk, rows, causal=False, wl=-1, wr=-1):
+    return _orig_mask(sq, sk, rows, causal, -1 if wl == 0 else wl, -1 if wr == 0 else wr)
+
+
+def _mask_left_off_by_one(sq, sk, rows, causal=False, wl=-1, wr=-1):
+    return _orig_mask(sq, sk, rows, causal, wl + 1 if wl >= 0 else wl, wr)
+
+
+def _scores_no_scale(qr, km, scale, softcap=0.0):
+    return _orig_scores(qr, km, 1.0, softcap)
+
+
+def _scores_transposed(qr, km, scale, softcap=0.0):
+    s = scale * (qr @ km.T)
+    s = s[:, ::-1]                       # keys read in the wrong order
+    if softcap > 0:
+        s = softcap * np.tanh(s / softcap)
+    return s
+
+
+def _scores_cap_before_scale(qr, km, scale, softcap=0.0):
+    s = qr @ km.T
+    if softcap > 0:
+        s = softcap * np.tanh(s / softcap)
+    return scale * s
+
+
+def _head_modulo(h, hq, hkv):
+    return h % hkv
+
+
+def _one_head_log2(*a, **kw):
+    o, l, p = _orig_one_head(*a, **kw)
+    return o, l / np.log(2.0), p
+
+
+def _one_head_no_max_shift(q_h, k_g, v_g, rows, scale, causal, wl, wr, softcap, chunk, want):
+    out = np.zeros((len(rows), v_g.shape[1]))
+    lse = np.full(len(rows), -np.inf)
+    probs = np.zeros((len(rows), k_g.shape[0])) if want else None
+    t = oatt.transformed_scores(q_h[rows], k_g, scale, softcap)
+    ok = oatt.allowed_mask(q_h.shape[0], k_g.shape[0], rows, causal, wl, wr)
+    with np.errstate(over="ignore", invalid="ignore"):
+        e = np.where(ok, np.exp(t), 0.0)
+        z = e.sum(axis=1)
+        p = e / z[:, None]
+        out[:] = p @ v_g
+        lse[:] = np.log(z)
+    if want:
+        probs[:] = p
+    return out, lse, probs
+
+
+def _tiled_no_lagging(*a, **kw):
+    a = list(a)
+    a[9] = False                          # lagging flag position in _tiled_one_head
+    return _orig_tiled_one(*a, **kw)
+
+
+def _tiled_natural_exp(q_h, k_g, v_g, scale, causal, window, softcap, tau, block_k, lagging,
+                       order, p_round, stats):
+    saved = otiled.LOG2E
+    otiled.LOG2E = 1.0                    # exp2 of the raw score: wrong base
+    try:
+        return _orig_tiled_one(q_h, k_g, v_g, scale, causal, window, softcap, tau, block_k,
+                               lagging, order, p_round, stats)
+    finally:
+        otiled.LOG2E = saved
+
+
+MUTATIONS = {
+    "causal_strict_lt": (oatt, "allowed_mask", _mask_causal_strict),
+    "top_left_alignment": (oatt, "allowed_mask", _mask_top_left),
+    "window_zero_as_unbounded": (oatt, "allowed_mask", _mask_window_zero_unbounded),
+    "window_left_off_by_one": (oatt, "allowed_mask", _mask_left_off_by_one),
+    "dropped_scale": (oatt, "transformed_scores", _scores_no_scale),
+    "keys_reversed": (oatt, "transformed_scores", _scores_transposed),
+    "softcap_before_scale": (oatt, "transformed_scores", _scores_cap_before_scale),
+    "gqa_modulo_map": (oatt, "kv_head_of", _head_modulo),
+    "lse_log2_units": (oatt, "_one_head", _one_head_log2),
+    "no_max_shift": (oatt, "_one_head", _one_head_no_max_shift),
+    "tiled_keep_new_max": (otiled, "_tiled_one_head", _tiled_no_lagging),
+    "tiled_wrong_exp_base": (otiled, "_tiled_one_head", _tiled_natural_exp),
+}
+
+
+@contextlib.contextmanager
+def _patched(mod, name, fn):
+    old = getattr(mod, name)
+    setattr(mod, name, fn)
+    try:
+        yield
+    finally:
+        setattr(mod, name, old)
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name):
+    mod, attr, fn = MUTATIONS[name]
+    caught = []
+    with _patched(mod, attr, fn):
+        for pin in oracle_pins.ALL_PINS:
+            try:
+                with np.errstate(all="ignore"):
+                    pin()
+            except Exception:            # AssertionError or a crash: the pin caught it
+                caught.append(pin.__name__)
+    assert caught, f"mutation {name} passed every pin"
