@@ -1,0 +1,262 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact tiled attention forward on one MI355X.
+
+A step is one pass of the hot path over one batch of synthetic input resident
+in HBM.  Default workload: bf16, B=4, H=16, Sq=Sk=2048, D=128, causal (the
+headline prefill configuration).  Prints ONE JSON line with throughput in
+TFLOP/s of algorithmic work (4*D per visible query/key pair, i.e. causal
+pairs only), the roofline of the dominant kernel against the published dense
+bf16 MFMA peak, the same workload's fp64 CPU-oracle rate on a bounded sample,
+and a secondary decode measurement (split-KV, HBM GB/s).
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                  [--no-cpu-baseline] [--no-secondary] [--mode copy]
+
+``--mode copy`` runs a plain device copy of known size instead; it is the
+calibration kernel for the HBM byte counters (FETCH_SIZE / WRITE_SIZE).
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attn fwd TFLOP/s (4·B·H·Sq·Sk·D) & % MFMA peak; decode HBM GB/s"
+PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0}  # MI355X dense MFMA, published
+PEAK_HBM_GBS = 8000.0                                  # MI355X HBM3E, published
+KERNEL_SRC = os.path.join(ROOT, "exact_tiled_attention_fa2_amd", "csrc", "attn_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_cfg2.json")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def visible_pairs(sq, sk, causal, window):
+    """Number of visible (query, key) pairs of one head (bottom-right aligned band)."""
+    import numpy as np
+
+    i = np.arange(sq, dtype=np.int64)
+    off = sk - sq
+    hi = np.full(sq, sk - 1, dtype=np.int64)
+    lo = np.zeros(sq, dtype=np.int64)
+    if causal:
+        hi = np.minimum(hi, i + off)
+    if window[1] >= 0:
+        hi = np.minimum(hi, i + off + window[1])
+    if window[0] >= 0:
+        lo = np.maximum(lo, i + off - window[0])
+    return int(np.clip(hi - lo + 1, 0, None).sum())
+
+
+def kernel_sha():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def load_traffic():
+    """HBM bytes per launch from the committed counter summary, if the kernel is unchanged."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != kernel_sha():
+        return None
+    return (t["fetch_kib_per_dispatch"] * t["fetch_scale"] + t["write_kib_per_dispatch"] * t["write_scale"]) * 1024.0
+
+
+def time_region(fn, steps, warmup, torch):
+    """W untimed steps, then K timed steps between synchronisations, with HIP events on the
+    current stream (the stream the library launches on).  Returns ms per step."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def cpu_baseline(cfg, budget_s=12.0):
+    """The fp64 NumPy oracle, as is, on a bounded sample of the same workload."""
+    import numpy as np
+    import torch
+
+    import attn_workloads as W
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+    except ImportError:  # pragma: no cover
+        threadpool_info = None
+    q, k, v = W.make_dense(cfg["seed"], 1, cfg["seqlen_q"], cfg["seqlen_k"], cfg["heads_q"],
+                           cfg["heads_kv"], cfg["head_dim"], cfg["dtype"], device="cpu",
+                           k_ramp=cfg.get("k_ramp", False))
+    g = cfg["heads_q"] // cfg["heads_kv"]
+    pairs = visible_pairs(cfg["seqlen_q"], cfg["seqlen_k"], cfg["causal"], cfg["window"])
+    flops_head = 4.0 * cfg["head_dim"] * pairs
+    done, t0 = 0, time.perf_counter()
+    while done < cfg["heads_q"]:
+        h = done
+        oracle.attention_ref(q[:, :, h:h + 1].to(torch.float64).numpy(),
+                             k[:, :, h // g:h // g + 1].to(torch.float64).numpy(),
+                             v[:, :, h // g:h // g + 1].to(torch.float64).numpy(),
+                             scale=cfg.get("scale"), causal=cfg["causal"], window=cfg["window"],
+                             softcap=cfg["softcap"])
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    threads = None
+    if threadpool_info is not None:
+        info = [x for x in threadpool_info() if x.get("user_api") == "blas"]
+        if info:
+            threads = max(x.get("num_threads", 1) for x in info)
+    return {"value": round(done * flops_head / dt / 1e12, 6), "unit": "TFLOP/s",
+            "cores": threads if threads else os.cpu_count(), "kind": "oracle",
+            "sample": f"{done} of {cfg['batch'] * cfg['heads_q']} (batch, head) pairs of the workload, "
+                      f"each a full {cfg['seqlen_q']}x{cfg['seqlen_k']} head, fp64 NumPy, {dt:.1f} s",
+            "host_cpus": os.cpu_count()}
+
+
+def bench_dense(name, steps, warmup, torch, eng, W):
+    c = W.WORKLOADS[name]
+    q, k, v = W.make_dense(c["seed"], c["batch"], c["seqlen_q"], c["seqlen_k"], c["heads_q"],
+                           c["heads_kv"], c["head_dim"], c["dtype"], k_ramp=c.get("k_ramp", False),
+                           device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((c["batch"], c["heads_q"], c["seqlen_q"]), dtype=torch.float32, device="cuda")
+
+    def step():
+        eng.attn_fwd(q, k, v, causal=c["causal"], window=c["window"], softcap=c["softcap"],
+                     softmax_scale=c.get("scale"), out=o, lse=lse)
+
+    ms = time_region(step, steps, warmup, torch)
+    pairs = visible_pairs(c["seqlen_q"], c["seqlen_k"], c["causal"], c["window"])
+    flops = 4.0 * c["head_dim"] * pairs * c["batch"] * c["heads_q"]
+    literal = 4.0 * c["batch"] * c["heads_q"] * c["seqlen_q"] * c["seqlen_k"] * c["head_dim"]
+    config = {"workload": name, "batch": c["batch"], "seqlen_q": c["seqlen_q"], "seqlen_k": c["seqlen_k"],
+              "heads_q": c["heads_q"], "heads_kv": c["heads_kv"], "head_dim": c["head_dim"],
+              "causal": c["causal"], "window": list(c["window"]), "softcap": c["softcap"],
+              "flop_count": "4*D per visible (query, key) pair",
+              "flops_per_step": flops, "literal_formula_flops_per_step": literal,
+              "literal_formula_tflops": round(literal / (ms * 1e-3) / 1e12, 3)}
+    return ms, flops, config, c
+
+
+def bench_kvcache(name, steps, warmup, torch, eng, W):
+    c = W.WORKLOADS[name]
+    q, kc, vc, lens = W.make_kvcache(c["seed"], c["batch"], c["seqlen_q"], c["seqlen_k"], c["heads_q"],
+                                     c["heads_kv"], c["head_dim"], c["dtype"], device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((c["batch"], c["heads_q"], c["seqlen_q"]), dtype=torch.float32, device="cuda")
+    ws = torch.empty(eng.attn_kvcache_workspace_bytes(c["batch"], c["seqlen_q"], c["heads_q"],
+                                                      c["head_dim"], c["num_splits"]),
+                     dtype=torch.uint8, device="cuda")
+
+    def step():
+        eng.attn_fwd_kvcache(q, kc, vc, cache_seqlens=lens, num_splits=c["num_splits"], out=o, lse=lse,
+                             workspace=ws)
+
+    ms = time_region(step, steps, warmup, torch)
+    el = 2  # 16-bit
+    bytes_alg = (2 * c["batch"] * c["seqlen_k"] * c["heads_kv"] * c["head_dim"] * el
+                 + 2 * q.numel() * el + lse.numel() * 4)
+    gbs = bytes_alg / (ms * 1e-3) / 1e9
+    return {"workload": name, "ms_per_step": round(ms, 4), "value": round(gbs, 1), "unit": "GB/s",
+            "bytes_per_step": bytes_alg, "num_splits": c["num_splits"],
+            "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "peak": PEAK_HBM_GBS,
+            "note": "whole step (split kernel + combine); algorithmic bytes = K+V cache + Q + O + LSE"}
+
+
+def run_copy(steps, warmup, torch):
+    n = 1 << 30  # bytes per buffer
+    a = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    ms = time_region(lambda: b.copy_(a), steps, warmup, torch)
+    print(json.dumps({"mode": "copy", "bytes_read": n, "bytes_written": n, "ms_per_copy": round(ms, 4),
+                      "GBps_read_plus_write": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="cfg2_bf16_causal_2k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--mode", default="attn", choices=["attn", "copy"])
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the forward shards over batch x KV-head groups with no exchange; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import attn_workloads as W
+    import exact_tiled_attention_fa2_amd as eng
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    eng.lib()
+    if args.mode == "copy":
+        run_copy(args.steps, args.warmup, torch)
+        return
+
+    c = W.WORKLOADS[args.workload]
+    log(f"workload {args.workload}: warmup {args.warmup}, steps {args.steps}")
+    if c["kind"] == "kvcache":
+        sec = bench_kvcache(args.workload, args.steps, args.warmup, torch, eng, W)
+        line = {"metric": METRIC, "value": sec["value"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+                "warmup": args.warmup, "ms_per_step": sec["ms_per_step"], "higher_is_better": True,
+                "scaling": "weak", "vs_baseline": None, "dtype": c["dtype"], "data": "synthetic",
+                "config": {"workload": args.workload, **{k: c[k] for k in ("batch", "seqlen_q", "seqlen_k",
+                                                                           "heads_q", "heads_kv", "head_dim",
+                                                                           "num_splits")}},
+                "roofline": {"bound": "hbm", "achieved": sec["value"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                             "frac": sec["frac_of_hbm_peak"], "traffic": None}}
+        print(json.dumps(line), flush=True)
+        return
+
+    ms, flops, config, cfg = bench_dense(args.workload, args.steps, args.warmup, torch, eng, W)
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_MFMA_TFLOPS[cfg["dtype"]]
+    log(f"{args.workload}: {ms:.4f} ms/step, {tflops:.1f} TFLOP/s")
+    traffic = load_traffic() if args.workload == "cfg2_bf16_causal_2k" else None
+    line = {"metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg["dtype"],
+            "data": "synthetic", "config": config,
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": peak, "unit": "TFLOP/s",
+                         "frac": round(tflops / peak, 4), "traffic": traffic,
+                         "kernel": "fwd_tile_kernel (one launch per step)"}}
+    if not args.no_secondary:
+        log("secondary: cfg5a decode")
+        torch.cuda.empty_cache()
+        line["secondary"] = [bench_kvcache("cfg5a_bf16_decode", max(5, args.steps // 5),
+                                           max(2, args.warmup // 10), torch, eng, W)]
+        torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle on a bounded sample)")
+        line["cpu_baseline"] = cpu_baseline(cfg)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,233 @@
+"""ctypes binding of libattn_mi355x.so (argument marshalling only).
+
+Every function here maps torch tensors to pointers, strides and the current
+HIP stream and calls the C entry point of the same name; all computation
+happens in the HIP kernels.  There is no fallback: if the library is not
+built, loading fails with an error that says how to build it.
+"""
+
+import ctypes
+import math
+import os
+
+import torch
+
+from .build_lib import LIB_PATH
+
+ATTN_OK = 0
+ATTN_E_NULL = -1
+ATTN_E_SHAPE = -2
+ATTN_E_HEADS = -3
+ATTN_E_UNSUPPORTED = -4
+ATTN_E_WINDOW = -5
+ATTN_E_WORKSPACE = -6
+ATTN_E_LAUNCH = -7
+ATTN_E_ALIGN = -8
+ATTN_E_ARG = -9
+
+ATTN_DTYPE_F16 = 0
+ATTN_DTYPE_BF16 = 1
+_DTYPE_CODES = {torch.float16: ATTN_DTYPE_F16, torch.bfloat16: ATTN_DTYPE_BF16}
+
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_f32 = ctypes.c_float
+_vp = ctypes.c_void_p
+
+
+class SoftmaxOpts(ctypes.Structure):
+    _fields_ = [("softmax_scale", _f32), ("causal", _i32), ("window_left", _i32),
+                ("window_right", _i32), ("softcap", _f32), ("rescale_threshold", _f32)]
+
+
+class FwdArgs(ctypes.Structure):
+    _fields_ = [("dtype", _i32), ("batch", _i32), ("seqlen_q", _i32), ("seqlen_k", _i32),
+                ("heads_q", _i32), ("heads_kv", _i32), ("head_dim", _i32),
+                ("q", _vp), ("k", _vp), ("v", _vp), ("o", _vp), ("lse", _vp),
+                ("q_batch_stride", _i64), ("q_row_stride", _i64), ("q_head_stride", _i64),
+                ("k_batch_stride", _i64), ("k_row_stride", _i64), ("k_head_stride", _i64),
+                ("v_batch_stride", _i64), ("v_row_stride", _i64), ("v_head_stride", _i64),
+                ("o_batch_stride", _i64), ("o_row_stride", _i64), ("o_head_stride", _i64),
+                ("opts", SoftmaxOpts)]
+
+
+class VarlenArgs(ctypes.Structure):
+    _fields_ = [("dtype", _i32), ("batch", _i32), ("total_q", _i32), ("total_k", _i32),
+                ("max_seqlen_q", _i32), ("max_seqlen_k", _i32), ("heads_q", _i32),
+                ("heads_kv", _i32), ("head_dim", _i32),
+                ("q", _vp), ("k", _vp), ("v", _vp), ("o", _vp), ("lse", _vp),
+                ("cu_seqlens_q", _vp), ("cu_seqlens_k", _vp),
+                ("q_row_stride", _i64), ("q_head_stride", _i64),
+                ("k_row_stride", _i64), ("k_head_stride", _i64),
+                ("v_row_stride", _i64), ("v_head_stride", _i64),
+                ("o_row_stride", _i64), ("o_head_stride", _i64),
+                ("opts", SoftmaxOpts)]
+
+
+class KvcacheArgs(ctypes.Structure):
+    _fields_ = [("dtype", _i32), ("batch", _i32), ("seqlen_q", _i32), ("seqlen_k", _i32),
+                ("heads_q", _i32), ("heads_kv", _i32), ("head_dim", _i32), ("num_splits", _i32),
+                ("q", _vp), ("k_cache", _vp), ("v_cache", _vp), ("cache_seqlens", _vp),
+                ("o", _vp), ("lse", _vp),
+                ("q_batch_stride", _i64), ("q_row_stride", _i64), ("q_head_stride", _i64),
+                ("k_batch_stride", _i64), ("k_row_stride", _i64), ("k_head_stride", _i64),
+                ("v_batch_stride", _i64), ("v_row_stride", _i64), ("v_head_stride", _i64),
+                ("o_batch_stride", _i64), ("o_row_stride", _i64), ("o_head_stride", _i64),
+                ("opts", SoftmaxOpts)]
+
+
+_LIB = None
+
+
+def lib():
+    """The loaded shared library (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m exact_tiled_attention_fa2_amd.build_lib`")
+        h = ctypes.CDLL(LIB_PATH)
+        h.attn_fwd.argtypes = [ctypes.POINTER(FwdArgs), _vp]
+        h.attn_fwd.restype = ctypes.c_int
+        h.attn_fwd_varlen.argtypes = [ctypes.POINTER(VarlenArgs), _vp, ctypes.c_size_t, _vp]
+        h.attn_fwd_varlen.restype = ctypes.c_int
+        h.attn_fwd_kvcache.argtypes = [ctypes.POINTER(KvcacheArgs), _vp, ctypes.c_size_t, _vp]
+        h.attn_fwd_kvcache.restype = ctypes.c_int
+        h.attn_varlen_workspace_bytes.argtypes = [_i32] * 5
+        h.attn_varlen_workspace_bytes.restype = ctypes.c_size_t
+        h.attn_kvcache_workspace_bytes.argtypes = [_i32] * 5
+        h.attn_kvcache_workspace_bytes.restype = ctypes.c_size_t
+        h.attn_kvcache_num_splits.argtypes = [_i32] * 6
+        h.attn_kvcache_num_splits.restype = _i32
+        h.attn_status_string.argtypes = [ctypes.c_int]
+        h.attn_status_string.restype = ctypes.c_char_p
+        h.attn_version.argtypes = []
+        h.attn_version.restype = ctypes.c_int
+        _LIB = h
+    return _LIB
+
+
+def status_string(code):
+    return lib().attn_status_string(int(code)).decode()
+
+
+def _check(code, what):
+    if code != ATTN_OK:
+        raise RuntimeError(f"{what} failed: {status_string(code)} (status {code})")
+
+
+def _opts(causal, window, softcap, softmax_scale, rescale_threshold):
+    return SoftmaxOpts(float(softmax_scale) if softmax_scale is not None else 0.0, int(bool(causal)),
+                       int(window[0]), int(window[1]), float(softcap), float(rescale_threshold))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype not in _DTYPE_CODES:
+        raise TypeError(f"unsupported dtype {t.dtype}; use float16 or bfloat16")
+    return _DTYPE_CODES[t.dtype]
+
+
+def _need_gpu(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+
+
+def attn_fwd(q, k, v, causal=False, window=(-1, -1), softcap=0.0, softmax_scale=None,
+             rescale_threshold=-1.0, out=None, lse=None, return_lse=True, stream=None):
+    """Dense attention forward: q [B, Sq, Hq, D], k/v [B, Sk, Hkv, D] -> (o, lse [B, Hq, Sq])."""
+    _need_gpu(q, k, v)
+    b, sq, hq, d = q.shape
+    sk, hkv = k.shape[1], k.shape[2]
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if lse is None and return_lse:
+        lse = torch.empty((b, hq, sq), dtype=torch.float32, device=q.device)
+    a = FwdArgs(_dtype_code(q), b, sq, sk, hq, hkv, d, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                *q.stride()[:3], *k.stride()[:3], *v.stride()[:3], *out.stride()[:3],
+                _opts(causal, window, softcap, softmax_scale, rescale_threshold))
+    if q.stride(3) != 1 or k.stride(3) != 1 or v.stride(3) != 1 or out.stride(3) != 1:
+        raise ValueError("the head dimension must be contiguous")
+    if k.dtype != q.dtype or v.dtype != q.dtype or out.dtype != q.dtype:
+        raise TypeError("q, k, v and out must share one dtype")
+    _check(lib().attn_fwd(ctypes.byref(a), _stream(stream, q.device)), "attn_fwd")
+    return out, lse
+
+
+def attn_varlen_workspace_bytes(batch, max_seqlen_q, heads_q, heads_kv, head_dim):
+    return int(lib().attn_varlen_workspace_bytes(batch, max_seqlen_q, heads_q, heads_kv, head_dim))
+
+
+def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, causal=False,
+                    window=(-1, -1), softcap=0.0, softmax_scale=None, rescale_threshold=-1.0,
+                    out=None, lse=None, return_lse=True, workspace=None, stream=None):
+    """Packed varlen forward: q [Tq, Hq, D], k/v [Tk, Hkv, D] -> (o, lse [Hq, Tq])."""
+    _need_gpu(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    tq, hq, d = q.shape
+    tk, hkv = k.shape[0], k.shape[1]
+    batch = cu_seqlens_q.shape[0] - 1
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if lse is None and return_lse:
+        lse = torch.empty((hq, tq), dtype=torch.float32, device=q.device)
+    need = attn_varlen_workspace_bytes(batch, max_seqlen_q, hq, hkv, d)
+    if need > 0 and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    a = VarlenArgs(_dtype_code(q), batch, tq, tk, int(max_seqlen_q), int(max_seqlen_k), hq, hkv, d,
+                   _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q),
+                   _ptr(cu_seqlens_k), *q.stride()[:2], *k.stride()[:2], *v.stride()[:2],
+                   *out.stride()[:2], _opts(causal, window, softcap, softmax_scale, rescale_threshold))
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().attn_fwd_varlen(ctypes.byref(a), _ptr(workspace), ws_bytes, _stream(stream, q.device)),
+           "attn_fwd_varlen")
+    return out, lse
+
+
+def attn_kvcache_num_splits(batch, seqlen_q, heads_q, heads_kv, seqlen_k, head_dim):
+    return int(lib().attn_kvcache_num_splits(batch, seqlen_q, heads_q, heads_kv, seqlen_k, head_dim))
+
+
+def attn_kvcache_workspace_bytes(batch, seqlen_q, heads_q, head_dim, num_splits):
+    return int(lib().attn_kvcache_workspace_bytes(batch, seqlen_q, heads_q, head_dim, num_splits))
+
+
+def attn_fwd_kvcache(q, k_cache, v_cache, cache_seqlens=None, num_splits=0, causal=False,
+                     window=(-1, -1), softcap=0.0, softmax_scale=None, rescale_threshold=-1.0,
+                     out=None, lse=None, return_lse=True, workspace=None, stream=None):
+    """Split-KV attention against a cache: q [B, Sq, Hq, D], caches [B, Sk, Hkv, D]."""
+    _need_gpu(q, k_cache, v_cache, cache_seqlens)
+    b, sq, hq, d = q.shape
+    sk, hkv = k_cache.shape[1], k_cache.shape[2]
+    if cache_seqlens is not None and cache_seqlens.dtype != torch.int32:
+        raise TypeError("cache_seqlens must be int32")
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if lse is None and return_lse:
+        lse = torch.empty((b, hq, sq), dtype=torch.float32, device=q.device)
+    splits = int(num_splits) if num_splits else attn_kvcache_num_splits(b, sq, hq, hkv, sk, d)
+    need = attn_kvcache_workspace_bytes(b, sq, hq, d, splits)
+    if need > 0 and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    a = KvcacheArgs(_dtype_code(q), b, sq, sk, hq, hkv, d, splits, _ptr(q), _ptr(k_cache),
+                    _ptr(v_cache), _ptr(cache_seqlens), _ptr(out), _ptr(lse),
+                    *q.stride()[:3], *k_cache.stride()[:3], *v_cache.stride()[:3], *out.stride()[:3],
+                    _opts(causal, window, softcap, softmax_scale, rescale_threshold))
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().attn_fwd_kvcache(ctypes.byref(a), _ptr(workspace), ws_bytes, _stream(stream, q.device)),
+           "attn_fwd_kvcache")
+    return out, lse
+
+
+def default_scale(head_dim):
+    return 1.0 / math.sqrt(head_dim)

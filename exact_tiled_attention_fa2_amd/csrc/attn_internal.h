@@ -1,0 +1,56 @@
+// Internal interface between the host C-ABI layer (attn_api.cpp) and the
+// HIP kernels (attn_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+// Everything one launch of the tile kernel needs, resolved on the host.
+// Strides are in elements.  Sequence offsets come from cu_seqlens (varlen) or
+// are zero (dense / kv-cache).
+struct FwdKernelParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;          // may be null
+  float* o_part;       // split-KV partial outputs [splits][B][Hq][Sq][D] (null: write o)
+  float* lse_part;     // split-KV partial LSEs    [splits][B][Hq][Sq]
+  const int32_t* cu_seqlens_q;  // varlen prefix sums [B+1] (null: dense)
+  const int32_t* cu_seqlens_k;
+  const int32_t* seqused_k;     // kv-cache valid lengths [B] (null: seqlen_k)
+  int64_t q_batch, q_row, q_head;
+  int64_t k_batch, k_row, k_head;
+  int64_t v_batch, v_row, v_head;
+  int64_t o_batch, o_row, o_head;
+  int64_t lse_batch, lse_head;  // LSE index = b*lse_batch + h*lse_head + (q_start + row)
+  int32_t batch, seqlen_q, seqlen_k, heads_q, heads_kv, group;
+  int32_t pack_gqa;     // 1: a query tile holds (row, head-in-group) pairs of one KV head
+  int32_t num_splits;
+  int32_t num_m_tiles;  // query tiles per (batch, head) in the grid's x dimension
+  int32_t window_left, window_right;  // -1 unbounded; causal already folded into window_right
+  float scale_log2;     // factor of the raw score inside exp2: scale*log2(e), or log2(e) with softcap
+  float scale_ln;       // running max -> natural-log units: scale, or 1 with softcap
+  float softcap_pre;    // scale / softcap
+  float softcap;        // 0: off
+  float tau;            // rescale threshold, log2 units
+};
+
+struct CombineParams {
+  const float* o_part;
+  const float* lse_part;
+  void* o;
+  float* lse;
+  int64_t o_batch, o_row, o_head;
+  int32_t batch, seqlen_q, heads_q, num_splits;
+};
+
+constexpr int kBlockM = 128;  // query rows (or packed row/head pairs) per workgroup
+
+// Host-side launchers (return a hipError_t).
+hipError_t launch_fwd(const FwdKernelParams& p, int dtype, int head_dim, hipStream_t stream);
+hipError_t launch_combine(const CombineParams& p, int dtype, int head_dim, hipStream_t stream);
+
+}  // namespace attn

@@ -1,0 +1,502 @@
+// Exact tiled attention forward for gfx950 (CDNA4): MFMA tile kernel with the
+// RescaleThreshold + max-lagging online softmax, and the split-KV combine.
+//
+// Method: release page "v1.7 / flash_attn 2.9.2.post1", section 1.2 (skip the
+// O/row_sum rescale while the row max rises by at most tau = 8 in log2 units,
+// and keep the previous max on a skip so O, row_sum and P share one base);
+// release page "FA2 2.9.0 Kernel Changes in v1.2", sections 1-3 (the rescale
+// step, the exp2-domain probabilities with the -inf guard, the first KV step
+// that never skips, and the split-KV variant of the row-block kernel).
+//
+// Layout of one workgroup (256 threads = 4 wave64s, 128 query rows):
+//  * Each wave owns 32 query rows.  Scores are computed transposed,
+//    S^T = K Q^T, with v_mfma_f32_32x32x16: A = a 32-key slice of K read
+//    from LDS, B = the wave's Q fragment held in VGPRs for the whole loop.
+//    In the 32x32 accumulator a lane holds one query (lane % 32) and 16 keys
+//    (8*(r/4) + 4*(lane/32) + r%4), so a row max is a register-local max
+//    plus one exchange with lane ^ 32, and each lane keeps its own m and l.
+//  * O^T = V^T P^T with the same MFMA.  The B operand (P^T, keys x queries)
+//    is the converted score registers themselves: registers 0-7 of a 32-key
+//    accumulator hold, per lane half, keys {0-3, 8-11} or {4-7, 12-15} of
+//    a 16-key slice, so the contraction runs over the keys in that order.
+//    The A operand (V^T) must use the same key order; it is read from the
+//    row-major V tile in LDS with ds_read_b64_tr_b16, whose 16-lane
+//    transpose hands lane l the element l % 4 of the rows addressed by
+//    lanes 4j + l / 4 -- two such reads give the 8 keys of one lane.
+//  * K and V tiles (BK keys x D) stream HBM -> VGPR -> LDS with 16-byte
+//    coalesced loads, double-buffered in LDS (one barrier per KV step); the
+//    global loads of step j+1 are in flight while step j computes.  16-byte
+//    chunks of a row are XOR-swizzled so that both the K reads (8/16 rows,
+//    same chunk) and the transposing V reads (4 rows x 2 chunks) hit
+//    distinct banks.
+//  * Masks run only on KV steps that cross a mask edge for the wave; steps
+//    that are fully masked for a wave are skipped by that wave.
+//  * Keys at or beyond the valid length are never loaded (zero-filled), so
+//    NaN in unused cache rows cannot reach the output.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "attn_internal.h"
+
+namespace attn {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct TypeBF16 {
+  static __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  // Two fp32 -> one packed pair, round to nearest even.
+  static __device__ __forceinline__ uint32_t pack(float x, float y) {
+    f32x2 v = {x, y};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+  }
+};
+
+struct TypeF16 {
+  static __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack(float x, float y) {
+    f32x2 v = {x, y};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+  }
+};
+
+// XOR pattern for the 16-byte chunk index of LDS row r (r taken mod 16): rows
+// 0..15 map to 16 distinct values, and any 4 consecutive rows starting at a
+// multiple of 4 differ in bits 1-2, so 4 rows x 2 adjacent chunks are distinct.
+__device__ __forceinline__ int chunk_swizzle(int r) {
+  return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <bool SOFTCAP>
+__device__ __forceinline__ float transform_score(float s, float pre, float cap) {
+  if constexpr (SOFTCAP) {
+    // cap * tanh(s * pre) with tanh(x) = 1 - 2 / (exp(2x) + 1); saturates to +-cap.
+    float e = fast_exp2(s * pre * (2.0f * kLog2e));
+    return cap * (1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f));
+  } else {
+    return s;
+  }
+}
+
+template <class Ty, int D, int BK, bool SOFTCAP, int MIN_WG>
+__global__ void __launch_bounds__(256, MIN_WG) fwd_tile_kernel(const FwdKernelParams p) {
+  constexpr int CH = D / 8;             // 16-byte chunks per row
+  constexpr int ROWB = D * 2;           // bytes per LDS row
+  constexpr int TILEB = BK * ROWB;      // bytes per K (or V) tile
+  constexpr int KT = BK / 32;           // 32-key MFMA tiles per KV step
+  constexpr int DS = D / 16;            // MFMA k-steps over the head dim (QK^T)
+  constexpr int DT = D / 32;            // 32-wide head-dim tiles of O^T
+  constexpr int KS = BK / 16;           // MFMA k-steps over keys (PV)
+  constexpr int LOADS = BK * CH / 256;  // 16-byte loads per thread per tile
+  constexpr int SWZ_MASK = CH < 16 ? CH - 1 : 15;
+  static_assert(LOADS >= 1 && (BK * CH) % 256 == 0, "tile must split evenly over 256 threads");
+
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hl = lane >> 5;  // which half of the wave: selects keys 4..7 of every 8
+
+  // ---------------------------------------------------------------- work item
+  const int mt = p.num_m_tiles - 1 - (int)blockIdx.x;  // heaviest causal tiles first
+  const int head = blockIdx.y;                         // q head, or kv head when packing
+  const int b = (int)blockIdx.z / p.num_splits;
+  const int split = (int)blockIdx.z - b * p.num_splits;
+
+  int q_start = 0, k_start = 0, sq = p.seqlen_q, sk = p.seqlen_k;
+  if (p.cu_seqlens_q != nullptr) {
+    q_start = p.cu_seqlens_q[b];
+    sq = p.cu_seqlens_q[b + 1] - q_start;
+    k_start = p.cu_seqlens_k[b];
+    sk = p.cu_seqlens_k[b + 1] - k_start;
+  }
+  if (p.seqused_k != nullptr) sk = min(max(p.seqused_k[b], 0), p.seqlen_k);
+  const int G = p.pack_gqa ? p.group : 1;
+  const int packed = sq * G;
+  const int m0 = mt * kBlockM;
+  if (m0 >= packed) return;
+  const int kvh = p.pack_gqa ? head : head / p.group;
+  const int off = sk - sq;
+  const int wl = p.window_left, wr = p.window_right;
+
+  // KV range of the whole tile, then this split's share of whole KV steps.
+  const int row_lo = m0 / G;
+  const int row_hi = min(packed - 1, m0 + kBlockM - 1) / G;
+  int n_lo = 0, n_hi = sk;
+  if (wl >= 0) n_lo = max(0, row_lo + off - wl);
+  if (wr >= 0) n_hi = min(sk, row_hi + off + wr + 1);
+  int blk_lo = 0, blk_hi = 0;
+  if (n_hi > n_lo) {
+    blk_lo = n_lo / BK;
+    blk_hi = (n_hi + BK - 1) / BK;
+  }
+  {
+    const int nblk = blk_hi - blk_lo;
+    const int per = (nblk + p.num_splits - 1) / p.num_splits;
+    const int s0 = blk_lo + split * per;
+    blk_hi = min(blk_hi, s0 + per);
+    blk_lo = s0;
+  }
+
+  // ---------------------------------------------------------------- this lane's query
+  const int pq = m0 + wave * 32 + l32;
+  const bool q_valid = pq < packed;
+  const int row = q_valid ? pq / G : 0;
+  const int hq = p.pack_gqa ? head * G + (q_valid ? pq - row * G : 0) : head;
+
+  // Rows covered by this wave (for per-wave skip / mask decisions).
+  const int wpq_lo = m0 + wave * 32;
+  const bool wave_live = wpq_lo < packed;
+  const int wrow_lo = wpq_lo / G;
+  const int wrow_hi = min(packed - 1, wpq_lo + 31) / G;
+  // Key bounds visible to this lane's row (inclusive), including the valid length.
+  const int kmin = (wl >= 0) ? row + off - wl : -0x40000000;
+  const int kmax = min(sk - 1, (wr >= 0) ? row + off + wr : 0x3fffffff);
+
+  // Q fragment (B operand of S^T = K Q^T): 8 consecutive dims per k-step.
+  u32x4 qf[DS];
+  {
+    const uint16_t* qbase = reinterpret_cast<const uint16_t*>(p.q) + (int64_t)b * p.q_batch +
+                            (int64_t)(q_start + row) * p.q_row + (int64_t)hq * p.q_head;
+#pragma unroll
+    for (int t = 0; t < DS; ++t) {
+      if (q_valid) {
+        qf[t] = *reinterpret_cast<const u32x4*>(qbase + 16 * t + 8 * hl);
+      } else {
+        qf[t] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+
+  // Per-lane LDS byte offsets of the MFMA operands (constant over the loop).
+  int k_off[DS];
+  {
+    const int sw = chunk_swizzle(lane & 15) & SWZ_MASK;
+#pragma unroll
+    for (int t = 0; t < DS; ++t) k_off[t] = l32 * ROWB + (((2 * t + hl) ^ sw) << 4);
+  }
+  int v_off[2][DT];
+  {
+    const int cl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+    for (int r2 = 0; r2 < 2; ++r2) {
+      const int vrow = 4 * hl + 8 * r2 + ((lane & 15) >> 2);
+      const int x = cl ^ (chunk_swizzle(vrow) & SWZ_MASK);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) v_off[r2][dt] = vrow * ROWB + (((4 * dt) ^ x) << 4) + ((lane & 1) << 3);
+    }
+  }
+
+  // Global -> register prefetch of one KV step.
+  const uint16_t* kbase = reinterpret_cast<const uint16_t*>(p.k) + (int64_t)b * p.k_batch +
+                          (int64_t)k_start * p.k_row + (int64_t)kvh * p.k_head;
+  const uint16_t* vbase = reinterpret_cast<const uint16_t*>(p.v) + (int64_t)b * p.v_batch +
+                          (int64_t)k_start * p.v_row + (int64_t)kvh * p.v_head;
+  u32x4 kr[LOADS], vr[LOADS];
+  auto load_tile = [&](int blk) {
+    const int j0 = blk * BK;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int u = tid + 256 * i;
+      const int r = u / CH, c = u % CH;
+      const int key = j0 + r;
+      if (key < sk) {
+        kr[i] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)key * p.k_row + c * 8);
+        vr[i] = *reinterpret_cast<const u32x4*>(vbase + (int64_t)key * p.v_row + c * 8);
+      } else {
+        kr[i] = u32x4{0u, 0u, 0u, 0u};
+        vr[i] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+    char* kl = smem + buf * (2 * TILEB);
+    char* vl = kl + TILEB;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int u = tid + 256 * i;
+      const int r = u / CH, c = u % CH;
+      const int o = r * ROWB + ((c ^ (chunk_swizzle(r & 15) & SWZ_MASK)) << 4);
+      *reinterpret_cast<u32x4*>(kl + o) = kr[i];
+      *reinterpret_cast<u32x4*>(vl + o) = vr[i];
+    }
+  };
+
+  // Running state: one query per lane (both halves hold the same m).
+  float m_run = -INFINITY;
+  float l_run = 0.0f;  // this half's partial row sum
+  f32x16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
+
+  const float c2 = p.scale_log2;
+  const float tau = p.tau;
+
+  if (blk_lo < blk_hi) {
+    load_tile(blk_lo);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int blk = blk_lo; blk < blk_hi; ++blk) {
+    const int buf = (blk - blk_lo) & 1;
+    const bool has_next = blk + 1 < blk_hi;
+    if (has_next) load_tile(blk + 1);
+
+    const int j0 = blk * BK;
+    // Wave-uniform: skip steps fully masked for every row of the wave.
+    const int w_kmin = (wl >= 0) ? wrow_lo + off - wl : -0x40000000;
+    const int w_kmax = min(sk - 1, (wr >= 0) ? wrow_hi + off + wr : 0x3fffffff);
+    const bool wave_skip = !wave_live || j0 > w_kmax || j0 + BK - 1 < w_kmin;
+    if (!wave_skip) {
+      const char* kl = smem + buf * (2 * TILEB);
+      const char* vl = kl + TILEB;
+      // ---- S^T = K Q^T
+      f32x16 s[KT];
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        s[kt] = f32x16{};
+#pragma unroll
+        for (int t = 0; t < DS; ++t) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(kl + kt * 32 * ROWB + k_off[t]);
+          s[kt] = Ty::mfma(a, qf[t], s[kt]);
+        }
+      }
+      // ---- score transform and masks (masks only where the step crosses an edge)
+      const int full_lo = (wl >= 0) ? wrow_hi + off - wl : -0x40000000;
+      const int full_hi = min(sk - 1, (wr >= 0) ? wrow_lo + off + wr : 0x3fffffff);
+      const bool need_mask = !(j0 >= full_lo && j0 + BK - 1 <= full_hi);
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kt][r] = transform_score<SOFTCAP>(s[kt][r], p.softcap_pre, p.softcap);
+      }
+      if (need_mask) {
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = j0 + 32 * kt + 8 * (r >> 2) + 4 * hl + (r & 3);
+            if (key < kmin || key > kmax) s[kt][r] = -INFINITY;
+          }
+        }
+      }
+      // ---- row max (registers, then the other half of the wave)
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      // ---- RescaleThreshold with max lagging
+      const float m_new = fmaxf(m_run, mx);
+      const float m_new_g = (m_new == -INFINITY) ? 0.0f : m_new;
+      const float diff = (m_run - m_new_g) * c2;  // <= 0; -inf on the first live step
+      const bool rescale = !(diff >= -tau);
+      if (__any(rescale)) {
+        const float alpha = rescale ? fast_exp2(diff) : 1.0f;
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+      }
+      if (rescale) m_run = m_new;
+      // ---- P = exp2(s*c2 - m*c2) <= exp2(tau), row sum, 16-bit pack
+      const float mg = (m_run == -INFINITY) ? 0.0f : m_run;
+      const float nb = -mg * c2;
+      uint32_t pk[KT][8];
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = fast_exp2(fmaf(s[kt][r], c2, nb));
+          const float p1 = fast_exp2(fmaf(s[kt][r + 1], c2, nb));
+          l_run += p0 + p1;
+          pk[kt][r >> 1] = Ty::pack(p0, p1);
+        }
+      }
+      // ---- O^T += V^T P^T
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 bop = {pk[ks >> 1][4 * (ks & 1) + 0], pk[ks >> 1][4 * (ks & 1) + 1],
+                           pk[ks >> 1][4 * (ks & 1) + 2], pk[ks >> 1][4 * (ks & 1) + 3]};
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4*)(vl + ks * 16 * ROWB + v_off[0][dt]));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4*)(vl + ks * 16 * ROWB + v_off[1][dt]));
+          const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
+          const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
+          const u32x4 aop = {lo2[0], lo2[1], hi2[0], hi2[1]};
+          acc[dt] = Ty::mfma(aop, bop, acc[dt]);
+        }
+      }
+    }
+    if (has_next) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---------------------------------------------------------------- epilogue
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  const float mg = (m_run == -INFINITY) ? 0.0f : m_run;
+  const float lse_val = l_tot > 0.0f ? mg * p.scale_ln + logf(l_tot) : -INFINITY;
+  if (!q_valid) return;
+  if (p.o_part == nullptr) {
+    uint16_t* op = reinterpret_cast<uint16_t*>(p.o) + (int64_t)b * p.o_batch +
+                   (int64_t)(q_start + row) * p.o_row + (int64_t)hq * p.o_head;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * dt + 8 * g4 + 4 * hl;
+        u32x2 w;
+        w[0] = Ty::pack(acc[dt][4 * g4 + 0] * inv, acc[dt][4 * g4 + 1] * inv);
+        w[1] = Ty::pack(acc[dt][4 * g4 + 2] * inv, acc[dt][4 * g4 + 3] * inv);
+        *reinterpret_cast<u32x2*>(op + d0) = w;
+      }
+    }
+    if (hl == 0 && p.lse != nullptr)
+      p.lse[(int64_t)b * p.lse_batch + (int64_t)hq * p.lse_head + q_start + row] = lse_val;
+  } else {
+    const int64_t pr = (((int64_t)split * p.batch + b) * p.heads_q + hq) * p.seqlen_q + row;
+    float* op = p.o_part + pr * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * dt + 8 * g4 + 4 * hl;
+        const f32x4 w = {acc[dt][4 * g4 + 0] * inv, acc[dt][4 * g4 + 1] * inv,
+                         acc[dt][4 * g4 + 2] * inv, acc[dt][4 * g4 + 3] * inv};
+        *reinterpret_cast<f32x4*>(op + d0) = w;
+      }
+    }
+    if (hl == 0) p.lse_part[pr] = lse_val;
+  }
+}
+
+// Log-sum-exp merge of the split partials: LSE = M + ln sum_s exp(LSE_s - M),
+// O = sum_s exp(LSE_s - LSE) O_s, in a fixed split order (deterministic).
+// Empty splits carry LSE_s = -inf and weight 0.  One thread per 4 dims.
+template <class Ty, int D>
+__global__ void __launch_bounds__(256) combine_kernel(const CombineParams p) {
+  constexpr int TPR = D / 4;  // threads per (b, h, row)
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t rows = (int64_t)p.batch * p.heads_q * p.seqlen_q;
+  const int64_t r = idx / TPR;
+  if (r >= rows) return;
+  const int dq = (int)(idx - r * TPR) * 4;
+  const int row = (int)(r % p.seqlen_q);
+  const int64_t bh = r / p.seqlen_q;
+  const int hq = (int)(bh % p.heads_q);
+  const int b = (int)(bh / p.heads_q);
+  const int64_t sstride = rows;  // partial entries per split
+  float mx = -INFINITY;
+  for (int s = 0; s < p.num_splits; ++s) mx = fmaxf(mx, p.lse_part[s * sstride + r]);
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  float lse = -INFINITY;
+  if (mx != -INFINITY) {
+    float sum = 0.0f;
+    for (int s = 0; s < p.num_splits; ++s) sum += expf(p.lse_part[s * sstride + r] - mx);
+    lse = mx + logf(sum);
+    for (int s = 0; s < p.num_splits; ++s) {
+      const float ls = p.lse_part[s * sstride + r];
+      if (ls == -INFINITY) continue;
+      const float w = expf(ls - lse);
+      const f32x4 v = *reinterpret_cast<const f32x4*>(p.o_part + (s * sstride + r) * D + dq);
+      o += w * v;
+    }
+  }
+  uint16_t* op = reinterpret_cast<uint16_t*>(p.o) + (int64_t)b * p.o_batch + (int64_t)row * p.o_row +
+                 (int64_t)hq * p.o_head + dq;
+  u32x2 w;
+  w[0] = Ty::pack(o[0], o[1]);
+  w[1] = Ty::pack(o[2], o[3]);
+  *reinterpret_cast<u32x2*>(op) = w;
+  if (dq == 0 && p.lse != nullptr) p.lse[r] = lse;
+}
+
+template <class Ty, int D, int BK, bool SOFTCAP, int MIN_WG>
+hipError_t launch_fwd_t(const FwdKernelParams& p, hipStream_t stream) {
+  constexpr size_t lds = 2 * 2 * (size_t)BK * D * 2;
+  auto kern = fwd_tile_kernel<Ty, D, BK, SOFTCAP, MIN_WG>;
+  static const hipError_t attr_err =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (attr_err != hipSuccess) return attr_err;
+  const int heads_grid = p.pack_gqa ? p.heads_kv : p.heads_q;
+  dim3 grid(p.num_m_tiles, heads_grid, p.batch * p.num_splits);
+  hipLaunchKernelGGL(kern, grid, dim3(256), lds, stream, p);
+  return hipGetLastError();
+}
+
+template <class Ty>
+hipError_t launch_fwd_dtype(const FwdKernelParams& p, int head_dim, hipStream_t stream) {
+  const bool cap = p.softcap > 0.0f;
+  switch (head_dim) {
+    case 64:
+      return cap ? launch_fwd_t<Ty, 64, 64, true, 2>(p, stream) : launch_fwd_t<Ty, 64, 64, false, 2>(p, stream);
+    case 128:
+      return cap ? launch_fwd_t<Ty, 128, 64, true, 2>(p, stream) : launch_fwd_t<Ty, 128, 64, false, 2>(p, stream);
+    case 256:
+      return cap ? launch_fwd_t<Ty, 256, 32, true, 1>(p, stream) : launch_fwd_t<Ty, 256, 32, false, 1>(p, stream);
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+template <class Ty, int D>
+hipError_t launch_combine_t(const CombineParams& p, hipStream_t stream) {
+  const int64_t threads = (int64_t)p.batch * p.heads_q * p.seqlen_q * (D / 4);
+  const int64_t blocks = (threads + 255) / 256;
+  hipLaunchKernelGGL((combine_kernel<Ty, D>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <class Ty>
+hipError_t launch_combine_dtype(const CombineParams& p, int head_dim, hipStream_t stream) {
+  switch (head_dim) {
+    case 64: return launch_combine_t<Ty, 64>(p, stream);
+    case 128: return launch_combine_t<Ty, 128>(p, stream);
+    case 256: return launch_combine_t<Ty, 256>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const FwdKernelParams& p, int dtype, int head_dim, hipStream_t stream) {
+  return dtype == 1 ? launch_fwd_dtype<TypeBF16>(p, head_dim, stream)
+                    : launch_fwd_dtype<TypeF16>(p, head_dim, stream);
+}
+
+hipError_t launch_combine(const CombineParams& p, int dtype, int head_dim, hipStream_t stream) {
+  return dtype == 1 ? launch_combine_dtype<TypeBF16>(p, head_dim, stream)
+                    : launch_combine_dtype<TypeF16>(p, head_dim, stream);
+}
+
+}  // namespace attn

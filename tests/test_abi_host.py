@@ -1,0 +1,186 @@
+"""CPU-only checks of the C ABI: the library loads, exports every declared entry
+point, its structs match the binding's layout, and host validation rejects bad
+arguments before any GPU work (no compute call is made here)."""
+
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_mi355x.h")
+
+binding = pytest.importorskip("exact_tiled_attention_fa2_amd.binding")
+
+
+def _lib():
+    try:
+        return binding.lib()
+    except RuntimeError as e:  # not built
+        pytest.fail(str(e))
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(attn_[a-z0-9_]+)\s*\(", text,
+                       flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_function():
+    h = _lib()
+    names = _declared_functions()
+    assert {"attn_fwd", "attn_fwd_varlen", "attn_fwd_kvcache"} <= set(names)
+    for n in names:
+        assert hasattr(h, n), f"{n} declared in the header but not exported"
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (attn_[a-z0-9_]+)", out))
+    assert set(names) <= exported
+
+
+def test_version_and_status_strings():
+    h = _lib()
+    assert h.attn_version() == 100
+    for code in range(-9, 1):
+        assert binding.status_string(code)
+    assert binding.status_string(-1234) == "unknown status"
+
+
+_LAYOUT_C = r"""
+#include <stddef.h>
+#include <stdio.h>
+#include "attn_mi355x.h"
+#define F(T, f) printf(#T " " #f " %zu\n", offsetof(T, f));
+int main(void) {
+  printf("attn_softmax_opts size %zu\n", sizeof(attn_softmax_opts));
+  printf("attn_fwd_args size %zu\n", sizeof(attn_fwd_args));
+  printf("attn_varlen_args size %zu\n", sizeof(attn_varlen_args));
+  printf("attn_kvcache_args size %zu\n", sizeof(attn_kvcache_args));
+  %FIELDS%
+  return 0;
+}
+"""
+
+
+def test_struct_layouts_match_binding():
+    structs = {"attn_softmax_opts": binding.SoftmaxOpts, "attn_fwd_args": binding.FwdArgs,
+               "attn_varlen_args": binding.VarlenArgs, "attn_kvcache_args": binding.KvcacheArgs}
+    fields = "\n".join(f"F({c}, {f})" for c, py in structs.items() for f, _ in py._fields_)
+    with tempfile.TemporaryDirectory() as d:
+        src = os.path.join(d, "layout.c")
+        exe = os.path.join(d, "layout")
+        open(src, "w").write(_LAYOUT_C.replace("%FIELDS%", fields))
+        subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), src, "-o", exe], check=True)
+        lines = subprocess.run([exe], capture_output=True, text=True, check=True).stdout.splitlines()
+    for line in lines:
+        name, field, value = line.split()
+        py = structs[name]
+        if field == "size":
+            assert ctypes.sizeof(py) == int(value), name
+        else:
+            assert getattr(py, field).offset == int(value), (name, field)
+
+
+def _fwd_args(**over):
+    base = dict(dtype=1, batch=2, seqlen_q=64, seqlen_k=64, heads_q=4, heads_kv=2, head_dim=128,
+                q=16, k=16, v=16, o=16, lse=None,
+                q_batch_stride=64 * 4 * 128, q_row_stride=4 * 128, q_head_stride=128,
+                k_batch_stride=64 * 2 * 128, k_row_stride=2 * 128, k_head_stride=128,
+                v_batch_stride=64 * 2 * 128, v_row_stride=2 * 128, v_head_stride=128,
+                o_batch_stride=64 * 4 * 128, o_row_stride=4 * 128, o_head_stride=128)
+    opts = dict(softmax_scale=0.0, causal=0, window_left=-1, window_right=-1, softcap=0.0,
+                rescale_threshold=-1.0)
+    for k, v in over.items():
+        if k in opts:
+            opts[k] = v
+        else:
+            base[k] = v
+    a = binding.FwdArgs()
+    for k, v in base.items():
+        setattr(a, k, v)
+    a.opts = binding.SoftmaxOpts(**opts)
+    return a
+
+
+# Each case is rejected by host validation before anything touches the GPU.
+_BAD_FWD = [
+    (dict(dtype=7), binding.ATTN_E_UNSUPPORTED),
+    (dict(head_dim=96), binding.ATTN_E_UNSUPPORTED),
+    (dict(heads_q=3), binding.ATTN_E_HEADS),
+    (dict(heads_kv=0), binding.ATTN_E_HEADS),
+    (dict(window_left=-2), binding.ATTN_E_WINDOW),
+    (dict(window_right=-5), binding.ATTN_E_WINDOW),
+    (dict(batch=-1), binding.ATTN_E_SHAPE),
+    (dict(seqlen_k=-3), binding.ATTN_E_SHAPE),
+    (dict(q=None), binding.ATTN_E_NULL),
+    (dict(o=None), binding.ATTN_E_NULL),
+    (dict(k=None), binding.ATTN_E_NULL),
+    (dict(q=24), binding.ATTN_E_ALIGN),
+    (dict(k_row_stride=2 * 128 + 4), binding.ATTN_E_ALIGN),
+    (dict(q_row_stride=1 << 24), binding.ATTN_E_ALIGN),
+    (dict(lse=18), binding.ATTN_E_ALIGN),
+    (dict(softcap=-1.0), binding.ATTN_E_ARG),
+    (dict(softmax_scale=float("nan")), binding.ATTN_E_ARG),
+    (dict(causal=2), binding.ATTN_E_ARG),
+]
+
+
+@pytest.mark.parametrize("over,code", _BAD_FWD, ids=[str(o) for o, _ in _BAD_FWD])
+def test_attn_fwd_rejects_bad_arguments(over, code):
+    h = _lib()
+    assert h.attn_fwd(ctypes.byref(_fwd_args(**over)), None) == code
+
+
+def test_null_args_and_empty_problems_launch_nothing():
+    h = _lib()
+    assert h.attn_fwd(None, None) == binding.ATTN_E_NULL
+    assert h.attn_fwd_varlen(None, None, 0, None) == binding.ATTN_E_NULL
+    assert h.attn_fwd_kvcache(None, None, 0, None) == binding.ATTN_E_NULL
+    # No query rows: OK without touching any pointer (they are NULL here).
+    assert h.attn_fwd(ctypes.byref(_fwd_args(batch=0, q=None, k=None, v=None, o=None)), None) == 0
+    assert h.attn_fwd(ctypes.byref(_fwd_args(seqlen_q=0, q=None, k=None, v=None, o=None)), None) == 0
+    va = binding.VarlenArgs(1, 3, 0, 0, 0, 0, 4, 4, 64)
+    va.opts = binding.SoftmaxOpts(0.0, 0, -1, -1, 0.0, -1.0)
+    assert h.attn_fwd_varlen(ctypes.byref(va), None, 0, None) == 0
+    ka = binding.KvcacheArgs(1, 0, 1, 128, 8, 2, 128, 0)
+    ka.opts = binding.SoftmaxOpts(0.0, 0, -1, -1, 0.0, -1.0)
+    assert h.attn_fwd_kvcache(ctypes.byref(ka), None, 0, None) == 0
+
+
+def test_varlen_validation():
+    h = _lib()
+    va = binding.VarlenArgs(1, 2, 100, 100, 64, 64, 4, 2, 128, 16, 16, 16, 16, None, None, 16,
+                            512, 128, 256, 128, 256, 128, 512, 128)
+    va.opts = binding.SoftmaxOpts(0.0, 1, -1, -1, 0.0, -1.0)
+    assert h.attn_fwd_varlen(ctypes.byref(va), None, 0, None) == binding.ATTN_E_NULL  # cu_seqlens_q
+    va.cu_seqlens_q = 16
+    va.heads_q = 5
+    assert h.attn_fwd_varlen(ctypes.byref(va), None, 0, None) == binding.ATTN_E_HEADS
+    va.heads_q = 4
+    va.total_q = -1
+    assert h.attn_fwd_varlen(ctypes.byref(va), None, 0, None) == binding.ATTN_E_SHAPE
+
+
+def test_kvcache_workspace_and_splits():
+    h = _lib()
+    # cfg: B=32, Sq=1, Hq=32, Hkv=8, Sk=32768, D=128, 16 splits
+    need = binding.attn_kvcache_workspace_bytes(32, 1, 32, 128, 16)
+    assert need == 16 * 32 * 32 * 1 * (128 + 1) * 4
+    assert binding.attn_kvcache_workspace_bytes(32, 1, 32, 128, 1) == 0
+    s = binding.attn_kvcache_num_splits(32, 1, 32, 8, 32768, 128)
+    assert 1 < s <= 128            # never forced to 1 when the grid would be small
+    assert binding.attn_kvcache_num_splits(1, 1, 8, 8, 64, 128) == 1
+    assert binding.attn_kvcache_num_splits(0, 1, 8, 8, 64, 128) == 1
+    ka = binding.KvcacheArgs(1, 32, 1, 32768, 32, 8, 128, 16, 16, 16, 16, None, 16, None,
+                             32 * 128, 32 * 128, 128, 32768 * 8 * 128, 8 * 128, 128,
+                             32768 * 8 * 128, 8 * 128, 128, 32 * 128, 32 * 128, 128)
+    ka.opts = binding.SoftmaxOpts(0.0, 0, -1, -1, 0.0, -1.0)
+    assert h.attn_fwd_kvcache(ctypes.byref(ka), None, 0, None) == binding.ATTN_E_WORKSPACE
+    assert h.attn_fwd_kvcache(ctypes.byref(ka), 16, need - 1, None) == binding.ATTN_E_WORKSPACE
+    ka.num_splits = 999
+    assert h.attn_fwd_kvcache(ctypes.byref(ka), 16, need, None) == binding.ATTN_E_ARG

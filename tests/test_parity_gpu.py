@@ -1,0 +1,277 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Small shapes are compared element by element over the whole output; the
+full-size workloads are compared on sampled query rows that the oracle
+computes one by one, in the same launch configuration the benchmark uses.
+Gates: bf16 rel_Linf <= 1e-2, fp16 rel_Linf <= 2e-2, cosine >= 0.9995 (page
+"v1.7 / flash_attn 2.9.2.post1", section 4) and LSE abs error <= 1e-3.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import attn_workloads as W
+import oracle
+from gpu_common import DT, gate_check, gpu_required, np64, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    gpu_required()
+
+
+def _eng():
+    import exact_tiled_attention_fa2_amd as eng
+    return eng
+
+
+def _dense_case(seed, b, sq, sk, hq, hkv, d, dtype, **kw):
+    q, k, v = W.make_dense(seed, b, sq, sk, hq, hkv, d, dtype, device="cuda",
+                           k_ramp=kw.pop("k_ramp", False), q_scale=kw.pop("q_scale", 1.0))
+    o, lse = _eng().attn_fwd(q, k, v, **kw)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_ref(np64(q), np64(k), np64(v), scale=kw.get("softmax_scale"),
+                                  causal=kw.get("causal", False), window=kw.get("window", (-1, -1)),
+                                  softcap=kw.get("softcap", 0.0))
+    return o, lse, ro, rl
+
+
+# ------------------------------------------------------------------ small full-output parity
+
+def test_cfg1_fp16_small_full():
+    c = W.WORKLOADS["cfg1_fp16_small"]
+    print("[case] cfg1 fp16 1x128x2x64", flush=True)
+    o, lse, ro, rl = _dense_case(c["seed"], 1, 128, 128, 2, 2, 64, "fp16", softmax_scale=c["scale"])
+    gate_check(np64(o), ro, np64(lse), rl, "fp16", "cfg1")
+
+
+DENSE_SMALL = [
+    # (seed, b, sq, sk, hq, hkv, d, dtype, kwargs)
+    (11, 2, 300, 300, 4, 4, 128, "bf16", dict(causal=True)),
+    (12, 2, 300, 300, 4, 4, 128, "bf16", dict(causal=False)),
+    (13, 1, 257, 513, 2, 2, 128, "fp16", dict(causal=True)),          # Sk > Sq, bottom-right
+    (14, 1, 513, 257, 2, 2, 128, "bf16", dict(causal=True)),          # Sq > Sk: early rows empty
+    (15, 2, 190, 190, 4, 1, 64, "fp16", dict(causal=True)),           # MQA, D=64
+    (16, 1, 333, 333, 8, 2, 128, "bf16", dict(causal=True, window=(100, 0), softcap=30.0)),
+    (17, 1, 333, 333, 8, 2, 128, "bf16", dict(causal=True, window=(100, 0), softcap=30.0, q_scale=8.0)),
+    (18, 1, 200, 200, 4, 2, 128, "bf16", dict(window=(17, 9))),
+    (19, 1, 300, 300, 4, 2, 256, "fp16", dict(causal=True)),
+    (20, 1, 300, 300, 4, 4, 256, "bf16", dict(causal=False, softcap=5.0)),
+    (21, 1, 160, 160, 2, 2, 64, "bf16", dict(window=(128, 128))),
+    (22, 3, 1, 1, 2, 2, 128, "fp16", dict()),                         # S = 1
+    (23, 1, 2, 2, 1, 1, 64, "fp16", dict(causal=True)),               # S = 2, H = 1
+]
+
+
+@pytest.mark.parametrize("case", DENSE_SMALL, ids=[f"s{c[0]}" for c in DENSE_SMALL])
+def test_dense_small_full(case):
+    seed, b, sq, sk, hq, hkv, d, dtype, kw = case
+    print(f"[case] dense seed={seed} b={b} sq={sq} sk={sk} hq={hq} hkv={hkv} d={d} {dtype} {kw}", flush=True)
+    o, lse, ro, rl = _dense_case(seed, b, sq, sk, hq, hkv, d, dtype, **dict(kw))
+    gate_check(np64(o), ro, np64(lse), rl, dtype, f"dense seed {seed}")
+
+
+def test_ramp_threshold8_vs_threshold0():
+    """Rising row max across KV steps: both thresholds match the oracle and each other."""
+    print("[case] ramp tau8 vs tau0 bf16 1x1024x2x128 causal", flush=True)
+    eng = _eng()
+    q, k, v = W.make_dense(1002, 1, 1024, 1024, 2, 2, 128, "bf16", k_ramp=True, device="cuda")
+    o8, l8 = eng.attn_fwd(q, k, v, causal=True, rescale_threshold=8.0)
+    o0, l0 = eng.attn_fwd(q, k, v, causal=True, rescale_threshold=0.0)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_ref(np64(q), np64(k), np64(v), causal=True)
+    gate_check(np64(o8), ro, np64(l8), rl, "bf16", "ramp tau=8")
+    gate_check(np64(o0), ro, np64(l0), rl, "bf16", "ramp tau=0")
+    assert oracle.rel_linf(np64(o8), np64(o0)) <= 1e-2
+    assert np.max(np.abs(np64(l8) - np64(l0))) <= 1e-3
+
+
+def test_window_00_is_v_bit_exact():
+    """Page "v1.7 / flash_attn 2.9.2.post1" section 4.6: window (0,0) gives O == V exactly."""
+    print("[case] window (0,0)", flush=True)
+    q, k, v = W.make_dense(31, 2, 200, 200, 4, 2, 128, "bf16", device="cuda")
+    o, _ = _eng().attn_fwd(q, k, v, window=(0, 0))
+    torch.cuda.synchronize()
+    vv = v.repeat_interleave(2, dim=2)
+    assert torch.equal(o, vv)
+
+
+def test_determinism_bit_identical():
+    """Page section 4.6: two identical calls are bit-identical."""
+    print("[case] determinism", flush=True)
+    eng = _eng()
+    q, k, v = W.make_dense(32, 2, 777, 777, 8, 2, 128, "bf16", device="cuda")
+    o1, l1 = eng.attn_fwd(q, k, v, causal=True)
+    o2, l2 = eng.attn_fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_empty_keys_give_zero_and_neg_inf():
+    print("[case] seqlen_k = 0", flush=True)
+    eng = _eng()
+    q = torch.randn(1, 5, 2, 128, device="cuda").to(torch.bfloat16)
+    k = torch.empty(1, 0, 2, 128, device="cuda", dtype=torch.bfloat16)
+    o, lse = eng.attn_fwd(q, k, k)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
+VARLEN_SMALL = [
+    (41, [1, 64, 129, 300, 77], 4, 4, 128, "bf16", dict(causal=True)),
+    (42, [200, 5, 131], 4, 2, 128, "fp16", dict(causal=False)),
+    (43, [70, 0, 260], 8, 2, 128, "bf16", dict(causal=True, window=(50, 0), softcap=30.0)),
+]
+
+
+@pytest.mark.parametrize("case", VARLEN_SMALL, ids=[f"s{c[0]}" for c in VARLEN_SMALL])
+def test_varlen_small_full(case):
+    seed, lens, hq, hkv, d, dtype, kw = case
+    print(f"[case] varlen seed={seed} lens={lens} hq={hq} hkv={hkv} d={d} {dtype} {kw}", flush=True)
+    q, k, v, cu, lens = W.make_varlen(seed, len(lens), 1, 1, hq, hkv, d, dtype, device="cuda",
+                                      lengths=lens)
+    o, lse = _eng().attn_fwd_varlen(q, k, v, cu, cu, max(lens), max(lens), **kw)
+    torch.cuda.synchronize()
+    cu_np = cu.cpu().numpy()
+    ro, rl = oracle.attention_varlen_ref(np64(q), np64(k), np64(v), cu_np, cu_np, **kw)
+    gate_check(np64(o), ro, np64(lse), rl, dtype, f"varlen {seed}")
+
+
+DECODE_SMALL = [
+    (51, 3, 1, 1000, 8, 2, 128, "bf16", 1),
+    (52, 3, 1, 1000, 8, 2, 128, "bf16", 2),
+    (53, 3, 1, 1000, 8, 2, 128, "bf16", 7),
+    (54, 3, 1, 1000, 8, 2, 128, "bf16", 16),
+    (55, 2, 3, 777, 8, 8, 64, "fp16", 5),
+    (56, 4, 1, 333, 16, 2, 256, "fp16", 0),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_SMALL, ids=[f"s{c[0]}" for c in DECODE_SMALL])
+def test_kvcache_small_nan_tail(case):
+    """Random valid lengths, NaN past them; every split count gives the oracle's answer."""
+    seed, b, sq, sk, hq, hkv, d, dtype, splits = case
+    print(f"[case] kvcache seed={seed} b={b} sq={sq} sk={sk} hq={hq} hkv={hkv} d={d} {dtype} splits={splits}",
+          flush=True)
+    q, kc, vc, lens = W.make_kvcache(seed, b, sq, sk, hq, hkv, d, dtype, device="cuda",
+                                     random_lengths=True, nan_tail=True)
+    o, lse = _eng().attn_fwd_kvcache(q, kc, vc, cache_seqlens=lens, num_splits=splits, causal=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_kvcache_ref(np64(q), np64(kc), np64(vc), lens.cpu().numpy(), causal=True)
+    gate_check(np64(o), ro, np64(lse), rl, dtype, f"kvcache {seed}")
+
+
+def test_kvcache_split_invariance_and_prefill_match():
+    """num_splits in {1, 2, 16, 37} agree; one split equals attn_fwd on the same cache."""
+    print("[case] split invariance", flush=True)
+    eng = _eng()
+    q, kc, vc, _ = W.make_kvcache(57, 2, 1, 3000, 8, 2, 128, "bf16", device="cuda")
+    outs = [eng.attn_fwd_kvcache(q, kc, vc, num_splits=s) for s in (1, 2, 16, 37)]
+    of, lf = eng.attn_fwd(q, kc, vc)
+    torch.cuda.synchronize()
+    base_o, base_l = np64(outs[0][0]), np64(outs[0][1])
+    for o, l in outs[1:]:
+        assert oracle.rel_linf(np64(o), base_o) <= 1e-2
+        assert np.max(np.abs(np64(l) - base_l)) <= 1e-4
+    assert torch.equal(outs[0][0], of) and torch.equal(outs[0][1], lf)
+
+
+# ------------------------------------------------------------------ full-size workloads (sampled rows)
+
+def _sampled_dense(name, n_heads_sampled=3, n_rows=24, **extra):
+    c = dict(W.WORKLOADS[name])
+    print(f"[case] full {name}", flush=True)
+    q, k, v = W.make_dense(c["seed"], c["batch"], c["seqlen_q"], c["seqlen_k"], c["heads_q"],
+                           c["heads_kv"], c["head_dim"], c["dtype"], k_ramp=c.get("k_ramp", False),
+                           device="cuda", **extra)
+    o, lse = _eng().attn_fwd(q, k, v, causal=c["causal"], window=c["window"], softcap=c["softcap"],
+                             softmax_scale=c.get("scale"))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(c["seed"])
+    g = c["heads_q"] // c["heads_kv"]
+    outs, refs, lses, lrefs = [], [], [], []
+    for _ in range(n_heads_sampled):
+        b = int(rng.integers(0, c["batch"]))
+        h = int(rng.integers(0, c["heads_q"]))
+        rows = sample_rows(c["seqlen_q"], n_rows, int(rng.integers(1 << 30)))
+        ro, rl = oracle.attention_ref(np64(q[b:b + 1, :, h:h + 1]), np64(k[b:b + 1, :, h // g:h // g + 1]),
+                                      np64(v[b:b + 1, :, h // g:h // g + 1]), scale=c.get("scale"),
+                                      causal=c["causal"], window=c["window"], softcap=c["softcap"],
+                                      rows=rows)
+        outs.append(np64(o[b, torch.as_tensor(rows, device=o.device), h]))
+        refs.append(ro[0, :, 0])
+        lses.append(np64(lse[b, h, torch.as_tensor(rows, device=o.device)]))
+        lrefs.append(rl[0, 0])
+    gate_check(np.concatenate(outs), np.concatenate(refs), np.concatenate(lses), np.concatenate(lrefs),
+               c["dtype"], name)
+
+
+def test_full_cfg2():
+    _sampled_dense("cfg2_bf16_causal_2k")
+
+
+def test_full_cfg2_kramp():
+    _sampled_dense("cfg2r_bf16_causal_2k_kramp")
+
+
+def test_full_cfg4():
+    _sampled_dense("cfg4_bf16_gqa_window_softcap")
+
+
+def test_full_cfg4_saturating_softcap():
+    _sampled_dense("cfg4_bf16_gqa_window_softcap", q_scale=8.0)
+
+
+def test_full_cfg5b():
+    _sampled_dense("cfg5b_fp16_d256_causal")
+
+
+def test_full_cfg3_varlen():
+    c = W.WORKLOADS["cfg3_bf16_varlen"]
+    print("[case] full cfg3 varlen", flush=True)
+    q, k, v, cu, lens = W.make_varlen(c["seed"], c["n_seqs"], c["len_lo"], c["len_hi"], c["heads_q"],
+                                      c["heads_kv"], c["head_dim"], c["dtype"], device="cuda")
+    o, lse = _eng().attn_fwd_varlen(q, k, v, cu, cu, max(lens), max(lens), causal=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    cu_np = cu.cpu().numpy()
+    outs, refs, lses, lrefs = [], [], [], []
+    for s in rng.choice(len(lens), size=4, replace=False):
+        a, z = int(cu_np[s]), int(cu_np[s + 1])
+        h = int(rng.integers(0, c["heads_q"]))
+        rows = sample_rows(z - a, 16, int(s))
+        ro, rl = oracle.attention_ref(np64(q[None, a:z, h:h + 1]), np64(k[None, a:z, h:h + 1]),
+                                      np64(v[None, a:z, h:h + 1]), causal=True, rows=rows)
+        idx = torch.as_tensor(a + rows, device=o.device)
+        outs.append(np64(o[idx, h]))
+        refs.append(ro[0, :, 0])
+        lses.append(np64(lse[h, idx]))
+        lrefs.append(rl[0, 0])
+    gate_check(np.concatenate(outs), np.concatenate(refs), np.concatenate(lses), np.concatenate(lrefs),
+               "bf16", "cfg3")
+
+
+def test_full_cfg5a_decode():
+    c = W.WORKLOADS["cfg5a_bf16_decode"]
+    print("[case] full cfg5a decode", flush=True)
+    q, kc, vc, lens = W.make_kvcache(c["seed"], c["batch"], 1, c["seqlen_k"], c["heads_q"], c["heads_kv"],
+                                     c["head_dim"], c["dtype"], device="cuda")
+    o, lse = _eng().attn_fwd_kvcache(q, kc, vc, cache_seqlens=lens, num_splits=c["num_splits"])
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    g = c["heads_q"] // c["heads_kv"]
+    outs, refs, lses, lrefs = [], [], [], []
+    for _ in range(6):
+        b = int(rng.integers(0, c["batch"]))
+        h = int(rng.integers(0, c["heads_q"]))
+        ro, rl = oracle.attention_ref(np64(q[b:b + 1, :, h:h + 1]), np64(kc[b:b + 1, :, h // g:h // g + 1]),
+                                      np64(vc[b:b + 1, :, h // g:h // g + 1]))
+        outs.append(np64(o[b, :, h]))
+        refs.append(ro[0, :, 0])
+        lses.append(np64(lse[b, h]))
+        lrefs.append(rl[0, 0])
+    gate_check(np.concatenate(outs), np.concatenate(refs), np.concatenate(lses), np.concatenate(lrefs),
+               "bf16", "cfg5a")
