@@ -31,11 +31,15 @@
 //    distinct banks.
 //  * Masks run only on KV steps that cross a mask edge for the wave; steps
 //    that are fully masked for a wave are skipped by that wave.
-//  * Keys at or beyond the valid length are never loaded (zero-filled), so
-//    NaN in unused cache rows cannot reach the output.
+//  * Keys at or beyond the valid length are never loaded (the last partial
+//    step re-reads the last valid row and masks it), so NaN in unused cache
+//    rows cannot reach the output.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
+
+#include <type_traits>
 
 #include "attn_internal.h"
 
@@ -79,12 +83,13 @@ struct TypeF16 {
   }
 };
 
-// XOR pattern for the 16-byte chunk index of LDS row r (r taken mod 16): rows
-// 0..15 map to 16 distinct values, and any 4 consecutive rows starting at a
-// multiple of 4 differ in bits 1-2, so 4 rows x 2 adjacent chunks are distinct.
-__device__ __forceinline__ int chunk_swizzle(int r) {
-  return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8);
-}
+// XOR pattern for the 16-byte chunk index of LDS row r (r taken mod 16).
+// Rows 0..15 map to 16 distinct values, so the K operand reads (16 rows, one
+// chunk each) cover all banks.  Within each group of 4 consecutive rows that
+// starts at a multiple of 4 the pattern differs in bits 2-3 only, so the
+// transposing V reads (4 rows x 4 adjacent chunks per 32 lanes) also land on
+// 16 distinct chunk positions.
+__device__ __forceinline__ int chunk_swizzle(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -99,6 +104,16 @@ __device__ __forceinline__ float transform_score(float s, float pre, float cap) 
   }
 }
 
+// One 16-byte HBM -> LDS copy per lane (global_load_lds_dwordx4): lane l of
+// the wave writes LDS bytes [lds + 16 l, lds + 16 l + 16); `lds` must be
+// wave-uniform.  No VGPR is used for the data.
+__device__ __forceinline__ void dma16(const void* g, const char* lds) {
+  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(g),
+                                   (__attribute__((address_space(3))) void*)(lds), 16, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
 template <class Ty, int D, int BK, bool SOFTCAP, int MIN_WG>
 __global__ void __launch_bounds__(256, MIN_WG) fwd_tile_kernel(const FwdKernelParams p) {
   constexpr int CH = D / 8;             // 16-byte chunks per row
@@ -108,23 +123,41 @@ __global__ void __launch_bounds__(256, MIN_WG) fwd_tile_kernel(const FwdKernelPa
   constexpr int DS = D / 16;            // MFMA k-steps over the head dim (QK^T)
   constexpr int DT = D / 32;            // 32-wide head-dim tiles of O^T
   constexpr int KS = BK / 16;           // MFMA k-steps over keys (PV)
-  constexpr int LOADS = BK * CH / 256;  // 16-byte loads per thread per tile
+  constexpr int LOADS = BK * CH / 256;  // 16-byte copies per lane per tile
+  constexpr int ROWS_PER_COPY = 64 / CH;  // tile rows one wave-wide copy covers
   constexpr int SWZ_MASK = CH < 16 ? CH - 1 : 15;
   static_assert(LOADS >= 1 && (BK * CH) % 256 == 0, "tile must split evenly over 256 threads");
 
-  extern __shared__ __attribute__((aligned(16))) char smem[];
+  // Two K and two V tiles, as separate arrays so that each copy's target is
+  // known at compile time (steps are unrolled by two).
+  __shared__ __attribute__((aligned(16))) char lds_k0[TILEB];
+  __shared__ __attribute__((aligned(16))) char lds_k1[TILEB];
+  __shared__ __attribute__((aligned(16))) char lds_v0[TILEB];
+  __shared__ __attribute__((aligned(16))) char lds_v1[TILEB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int hl = lane >> 5;  // which half of the wave: selects keys 4..7 of every 8
 
   // ---------------------------------------------------------------- work item
-  const int mt = p.num_m_tiles - 1 - (int)blockIdx.x;  // heaviest causal tiles first
-  const int head = blockIdx.y;                         // q head, or kv head when packing
-  const int b = (int)blockIdx.z / p.num_splits;
-  const int split = (int)blockIdx.z - b * p.num_splits;
+  // Workgroups are dealt round-robin to the 8 XCDs (each with its own L2).
+  // Renumber them so that every XCD receives a contiguous range of work items:
+  // all query tiles of one (batch, head) then run on one XCD and share its L2.
+  int wid;
+  {
+    const int nx = gridDim.x, ny = gridDim.y;
+    const int total = nx * ny * (int)gridDim.z;
+    const int lin = (int)blockIdx.x + nx * ((int)blockIdx.y + ny * (int)blockIdx.z);
+    const int per = total >> 3;
+    wid = (lin < (per << 3)) ? (lin & 7) * per + (lin >> 3) : lin;
+  }
+  const int mt = p.num_m_tiles - 1 - wid % p.num_m_tiles;  // heaviest causal tiles first
+  const int head = (wid / p.num_m_tiles) % (int)gridDim.y;   // q head, or kv head when packing
+  const int zz = wid / (p.num_m_tiles * (int)gridDim.y);
+  const int b = zz / p.num_splits;
+  const int split = zz - b * p.num_splits;
 
   int q_start = 0, k_start = 0, sq = p.seqlen_q, sk = p.seqlen_k;
   if (p.cu_seqlens_q != nullptr) {
@@ -167,9 +200,8 @@ __global__ void __launch_bounds__(256, MIN_WG) fwd_tile_kernel(const FwdKernelPa
   const int row = q_valid ? pq / G : 0;
   const int hq = p.pack_gqa ? head * G + (q_valid ? pq - row * G : 0) : head;
 
-  // Rows covered by this wave (for per-wave skip / mask decisions).
+  // Rows covered by this wave (for the per-step mask decision).
   const int wpq_lo = m0 + wave * 32;
-  const bool wave_live = wpq_lo < packed;
   const int wrow_lo = wpq_lo / G;
   const int wrow_hi = min(packed - 1, wpq_lo + 31) / G;
   // Key bounds visible to this lane's row (inclusive), including the valid length.
@@ -189,6 +221,9 @@ __global__ void __launch_bounds__(256, MIN_WG) fwd_tile_kernel(const FwdKernelPa
         qf[t] = u32x4{0u, 0u, 0u, 0u};
       }
     }
+    // Retire the Q loads here, so the loop's only outstanding vector memory
+    // operations are the tile copies.
+    wait_vmem();
   }
 
   // Per-lane LDS byte offsets of the MFMA operands (constant over the loop).
@@ -210,40 +245,43 @@ __global__ void __launch_bounds__(256, MIN_WG) fwd_tile_kernel(const FwdKernelPa
     }
   }
 
-  // Global -> register prefetch of one KV step.
-  const uint16_t* kbase = reinterpret_cast<const uint16_t*>(p.k) + (int64_t)b * p.k_batch +
-                          (int64_t)k_start * p.k_row + (int64_t)kvh * p.k_head;
-  const uint16_t* vbase = reinterpret_cast<const uint16_t*>(p.v) + (int64_t)b * p.v_batch +
-                          (int64_t)k_start * p.v_row + (int64_t)kvh * p.v_head;
-  u32x4 kr[LOADS], vr[LOADS];
-  auto load_tile = [&](int blk) {
-    const int j0 = blk * BK;
+  // HBM -> LDS tile copies.  Copy i of wave w fills LDS bytes
+  // [(4i + w) * 1024, +1024) of the tile; the lane that lands on row r,
+  // chunk position pos fetches the global chunk pos ^ swizzle(r), which
+  // produces the swizzled layout the operand reads expect.
+  const char* kbase = reinterpret_cast<const char*>(p.k) +
+                      2 * ((int64_t)b * p.k_batch + (int64_t)k_start * p.k_row + (int64_t)kvh * p.k_head);
+  const char* vbase = reinterpret_cast<const char*>(p.v) +
+                      2 * ((int64_t)b * p.v_batch + (int64_t)k_start * p.v_row + (int64_t)kvh * p.v_head);
+  const int64_t k_rowb = 2 * p.k_row, v_rowb = 2 * p.v_row;
+  int cp_row[LOADS], cp_col[LOADS];  // tile row and global byte column of each copy
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int u = tid + 256 * i;
-      const int r = u / CH, c = u % CH;
-      const int key = j0 + r;
-      if (key < sk) {
-        kr[i] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)key * p.k_row + c * 8);
-        vr[i] = *reinterpret_cast<const u32x4*>(vbase + (int64_t)key * p.v_row + c * 8);
-      } else {
-        kr[i] = u32x4{0u, 0u, 0u, 0u};
-        vr[i] = u32x4{0u, 0u, 0u, 0u};
+  for (int i = 0; i < LOADS; ++i) {
+    const int u = (4 * i + wave) * 64 + lane;
+    const int r = u / CH, pos = u % CH;
+    cp_row[i] = r;
+    cp_col[i] = (pos ^ (chunk_swizzle(r & 15) & SWZ_MASK)) << 4;
+  }
+  auto copy_tile = [&](const char* gbase, int64_t rowb, char* tile, int blk) {
+    const int j0 = blk * BK;
+    if (j0 + BK <= sk) {
+      const char* tb = gbase + (int64_t)j0 * rowb;
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i)
+        dma16(tb + (uint32_t)(cp_row[i] * (int)rowb + cp_col[i]), tile + (4 * i + wave) * 1024);
+    } else {
+      // Last, partial step: rows at or past the valid length re-read row
+      // sk-1 instead.  Their scores are masked to -inf, so P = 0 multiplies
+      // finite values, and memory past the valid length (which may hold NaN)
+      // is never touched.
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const int key = min(j0 + cp_row[i], sk - 1);
+        dma16(gbase + (int64_t)key * rowb + cp_col[i], tile + (4 * i + wave) * 1024);
       }
     }
   };
-  auto store_tile = [&](int buf) {
-    char* kl = smem + buf * (2 * TILEB);
-    char* vl = kl + TILEB;
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int u = tid + 256 * i;
-      const int r = u / CH, c = u % CH;
-      const int o = r * ROWB + ((c ^ (chunk_swizzle(r & 15) & SWZ_MASK)) << 4);
-      *reinterpret_cast<u32x4*>(kl + o) = kr[i];
-      *reinterpret_cast<u32x4*>(vl + o) = vr[i];
-    }
-  };
+  (void)ROWS_PER_COPY;
 
   // Running state: one query per lane (both halves hold the same m).
   float m_run = -INFINITY;
@@ -254,117 +292,148 @@ __global__ void __launch_bounds__(256, MIN_WG) fwd_tile_kernel(const FwdKernelPa
 
   const float c2 = p.scale_log2;
   const float tau = p.tau;
+  const int n = blk_hi - blk_lo;
 
-  if (blk_lo < blk_hi) {
-    load_tile(blk_lo);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int blk = blk_lo; blk < blk_hi; ++blk) {
-    const int buf = (blk - blk_lo) & 1;
-    const bool has_next = blk + 1 < blk_hi;
-    if (has_next) load_tile(blk + 1);
-
+  // ---- the pieces of one KV step
+  // S^T = K Q^T from an LDS K tile.
+  auto qk = [&](f32x16 (&sc)[KT], const char* kl) {
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) sc[kt] = f32x16{};
+#pragma unroll
+    for (int t = 0; t < DS; ++t) {
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(kl + kt * 32 * ROWB + k_off[t]);
+        sc[kt] = Ty::mfma(a, qf[t], sc[kt]);
+      }
+    }
+  };
+  // O^T += V^T P^T from an LDS V tile and the packed probabilities.
+  auto pv = [&](const uint32_t (&pkk)[KT][8], const char* vl) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4 bop = {pkk[ks >> 1][4 * (ks & 1) + 0], pkk[ks >> 1][4 * (ks & 1) + 1],
+                         pkk[ks >> 1][4 * (ks & 1) + 2], pkk[ks >> 1][4 * (ks & 1) + 3]};
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl + ks * 16 * ROWB + v_off[0][dt]));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl + ks * 16 * ROWB + v_off[1][dt]));
+        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
+        const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
+        const u32x4 aop = {lo2[0], lo2[1], hi2[0], hi2[1]};
+        acc[dt] = Ty::mfma(aop, bop, acc[dt]);
+      }
+    }
+  };
+  // Softcap and masks on the scores of step blk (masks only where an edge crosses it).
+  auto transform_and_mask = [&](f32x16 (&sc)[KT], int blk) {
+    if constexpr (SOFTCAP) {
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[kt][r] = transform_score<SOFTCAP>(sc[kt][r], p.softcap_pre, p.softcap);
+      }
+    }
     const int j0 = blk * BK;
-    // Wave-uniform: skip steps fully masked for every row of the wave.
-    const int w_kmin = (wl >= 0) ? wrow_lo + off - wl : -0x40000000;
-    const int w_kmax = min(sk - 1, (wr >= 0) ? wrow_hi + off + wr : 0x3fffffff);
-    const bool wave_skip = !wave_live || j0 > w_kmax || j0 + BK - 1 < w_kmin;
-    if (!wave_skip) {
-      const char* kl = smem + buf * (2 * TILEB);
-      const char* vl = kl + TILEB;
-      // ---- S^T = K Q^T
-      f32x16 s[KT];
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-        s[kt] = f32x16{};
-#pragma unroll
-        for (int t = 0; t < DS; ++t) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(kl + kt * 32 * ROWB + k_off[t]);
-          s[kt] = Ty::mfma(a, qf[t], s[kt]);
-        }
-      }
-      // ---- score transform and masks (masks only where the step crosses an edge)
-      const int full_lo = (wl >= 0) ? wrow_hi + off - wl : -0x40000000;
-      const int full_hi = min(sk - 1, (wr >= 0) ? wrow_lo + off + wr : 0x3fffffff);
-      const bool need_mask = !(j0 >= full_lo && j0 + BK - 1 <= full_hi);
+    const int full_lo = (wl >= 0) ? wrow_hi + off - wl : -0x40000000;
+    const int full_hi = min(sk - 1, (wr >= 0) ? wrow_lo + off + wr : 0x3fffffff);
+    if (!(j0 >= full_lo && j0 + BK - 1 <= full_hi)) {
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[kt][r] = transform_score<SOFTCAP>(s[kt][r], p.softcap_pre, p.softcap);
-      }
-      if (need_mask) {
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = j0 + 32 * kt + 8 * (r >> 2) + 4 * hl + (r & 3);
-            if (key < kmin || key > kmax) s[kt][r] = -INFINITY;
-          }
-        }
-      }
-      // ---- row max (registers, then the other half of the wave)
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      // ---- RescaleThreshold with max lagging
-      const float m_new = fmaxf(m_run, mx);
-      const float m_new_g = (m_new == -INFINITY) ? 0.0f : m_new;
-      const float diff = (m_run - m_new_g) * c2;  // <= 0; -inf on the first live step
-      const bool rescale = !(diff >= -tau);
-      if (__any(rescale)) {
-        const float alpha = rescale ? fast_exp2(diff) : 1.0f;
-        l_run *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
-      }
-      if (rescale) m_run = m_new;
-      // ---- P = exp2(s*c2 - m*c2) <= exp2(tau), row sum, 16-bit pack
-      const float mg = (m_run == -INFINITY) ? 0.0f : m_run;
-      const float nb = -mg * c2;
-      uint32_t pk[KT][8];
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = fast_exp2(fmaf(s[kt][r], c2, nb));
-          const float p1 = fast_exp2(fmaf(s[kt][r + 1], c2, nb));
-          l_run += p0 + p1;
-          pk[kt][r >> 1] = Ty::pack(p0, p1);
-        }
-      }
-      // ---- O^T += V^T P^T
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 bop = {pk[ks >> 1][4 * (ks & 1) + 0], pk[ks >> 1][4 * (ks & 1) + 1],
-                           pk[ks >> 1][4 * (ks & 1) + 2], pk[ks >> 1][4 * (ks & 1) + 3]};
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4*)(vl + ks * 16 * ROWB + v_off[0][dt]));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4*)(vl + ks * 16 * ROWB + v_off[1][dt]));
-          const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
-          const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
-          const u32x4 aop = {lo2[0], lo2[1], hi2[0], hi2[1]};
-          acc[dt] = Ty::mfma(aop, bop, acc[dt]);
+        for (int r = 0; r < 16; ++r) {
+          const int key = j0 + 32 * kt + 8 * (r >> 2) + 4 * hl + (r & 3);
+          if (key < kmin || key > kmax) sc[kt][r] = -INFINITY;
         }
       }
     }
-    if (has_next) store_tile(buf ^ 1);
+  };
+
+  // Rescale threshold in units of the raw score: the running max may lag the
+  // block max by up to tau / c2 before O and l are rescaled.
+  const float tau_raw = tau / c2;
+
+  // One KV step r (PAR = r & 1): the tiles of step r sit in buffers PAR; the
+  // copies for step r+1 stream into the other pair meanwhile.
+  auto step = [&](auto par, int r) {
+    constexpr int PAR = decltype(par)::value;
+    const char* const k_cur = PAR ? lds_k1 : lds_k0;
+    const char* const v_cur = PAR ? lds_v1 : lds_v0;
+    char* const k_nxt = PAR ? lds_k0 : lds_k1;
+    char* const v_nxt = PAR ? lds_v0 : lds_v1;
+    const int blk = blk_lo + r;
+    if (r + 1 < n) {
+      copy_tile(kbase, k_rowb, k_nxt, blk + 1);
+      copy_tile(vbase, v_rowb, v_nxt, blk + 1);
+    }
+    // ---- S^T = K Q^T
+    f32x16 sc[KT];
+    qk(sc, k_cur);
+    transform_and_mask(sc, blk);
+    // ---- block max of this lane's keys (one half of the row)
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+      for (int r2 = 0; r2 < 16; ++r2) mx = fmaxf(mx, sc[kt][r2]);
+    }
+    // ---- RescaleThreshold with max lagging.  While no row's block max rises
+    // more than tau above its running max, the running max is kept as is (no
+    // exchange between the two halves is needed for that).  Otherwise the two
+    // halves agree on the row max and rows that rose too far are rescaled.
+    if (__any(mx > m_run + tau_raw)) {
+      const float mx_row = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx_row);
+      const float m_new_g = (m_new == -INFINITY) ? 0.0f : m_new;
+      const float diff = (m_run - m_new_g) * c2;  // <= 0; -inf on the first live step
+      if (!(diff >= -tau)) {
+        const float alpha = fast_exp2(diff);
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+        m_run = m_new;
+      }
+    }
+    // ---- P = exp2((s - m) c2) <= exp2(tau), row sum, 16-bit pack
+    const float mg = (m_run == -INFINITY) ? 0.0f : m_run;
+    const float nb = -mg * c2;
+    uint32_t pk[KT][8];
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+      for (int r2 = 0; r2 < 16; r2 += 2) {
+        const float p0 = fast_exp2(fmaf(sc[kt][r2], c2, nb));
+        const float p1 = fast_exp2(fmaf(sc[kt][r2 + 1], c2, nb));
+        l_run += p0 + p1;
+        pk[kt][r2 >> 1] = Ty::pack(p0, p1);
+      }
+    }
+    // ---- O^T += V^T P^T
+    pv(pk, v_cur);
+    wait_vmem();  // the copies for step r+1 have landed in LDS
     __syncthreads();
+  };
+
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  if (n > 0) {
+    copy_tile(kbase, k_rowb, lds_k0, blk_lo);
+    copy_tile(vbase, v_rowb, lds_v0, blk_lo);
+    wait_vmem();
+    __syncthreads();
+    int r = 0;
+    for (; r + 1 < n; r += 2) {
+      step(P0{}, r);
+      step(P1{}, r + 1);
+    }
+    if (r < n) step(P0{}, r);
   }
 
   // ---------------------------------------------------------------- epilogue
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  const float mg = (m_run == -INFINITY) ? 0.0f : m_run;
-  const float lse_val = l_tot > 0.0f ? mg * p.scale_ln + logf(l_tot) : -INFINITY;
+  const float mgf = (m_run == -INFINITY) ? 0.0f : m_run;
+  const float lse_val = l_tot > 0.0f ? mgf * p.scale_ln + logf(l_tot) : -INFINITY;
   if (!q_valid) return;
   if (p.o_part == nullptr) {
     uint16_t* op = reinterpret_cast<uint16_t*>(p.o) + (int64_t)b * p.o_batch +
@@ -442,16 +511,20 @@ __global__ void __launch_bounds__(256) combine_kernel(const CombineParams p) {
 
 template <class Ty, int D, int BK, bool SOFTCAP, int MIN_WG>
 hipError_t launch_fwd_t(const FwdKernelParams& p, hipStream_t stream) {
-  constexpr size_t lds = 2 * 2 * (size_t)BK * D * 2;
   auto kern = fwd_tile_kernel<Ty, D, BK, SOFTCAP, MIN_WG>;
-  static const hipError_t attr_err =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (attr_err != hipSuccess) return attr_err;
   const int heads_grid = p.pack_gqa ? p.heads_kv : p.heads_q;
   dim3 grid(p.num_m_tiles, heads_grid, p.batch * p.num_splits);
-  hipLaunchKernelGGL(kern, grid, dim3(256), lds, stream, p);
+  hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, p);
   return hipGetLastError();
+}
+
+// Tile-shape variant for tuning sweeps (environment ATTN_MI355X_FWD_VARIANT); 0 = default.
+int fwd_variant() {
+  static const int v = [] {
+    const char* e = getenv("ATTN_MI355X_FWD_VARIANT");
+    return e ? atoi(e) : 0;
+  }();
+  return v;
 }
 
 template <class Ty>
@@ -461,6 +534,9 @@ hipError_t launch_fwd_dtype(const FwdKernelParams& p, int head_dim, hipStream_t 
     case 64:
       return cap ? launch_fwd_t<Ty, 64, 64, true, 2>(p, stream) : launch_fwd_t<Ty, 64, 64, false, 2>(p, stream);
     case 128:
+      if (!cap && fwd_variant() == 1) return launch_fwd_t<Ty, 128, 32, false, 3>(p, stream);
+      if (!cap && fwd_variant() == 2) return launch_fwd_t<Ty, 128, 32, false, 2>(p, stream);
+      if (!cap && fwd_variant() == 3) return launch_fwd_t<Ty, 128, 64, false, 3>(p, stream);
       return cap ? launch_fwd_t<Ty, 128, 64, true, 2>(p, stream) : launch_fwd_t<Ty, 128, 64, false, 2>(p, stream);
     case 256:
       return cap ? launch_fwd_t<Ty, 256, 32, true, 1>(p, stream) : launch_fwd_t<Ty, 256, 32, false, 1>(p, stream);
