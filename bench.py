@@ -88,9 +88,9 @@ def time_region(fn, steps, warmup, torch):
     return e0.elapsed_time(e1) / steps
 
 
-def cpu_baseline(cfg, budget_s=12.0):
-    """The fp64 NumPy oracle, as is, on a bounded sample of the same workload."""
-    import numpy as np
+def cpu_baseline(cfg, budget_s=20.0):
+    """The fp64 NumPy oracle, as is, on a bounded sample of the same workload: whole
+    (batch, head) pairs in order until the budget is spent or the workload is done."""
     import torch
 
     import attn_workloads as W
@@ -100,18 +100,19 @@ def cpu_baseline(cfg, budget_s=12.0):
         from threadpoolctl import threadpool_info
     except ImportError:  # pragma: no cover
         threadpool_info = None
-    q, k, v = W.make_dense(cfg["seed"], 1, cfg["seqlen_q"], cfg["seqlen_k"], cfg["heads_q"],
+    q, k, v = W.make_dense(cfg["seed"], cfg["batch"], cfg["seqlen_q"], cfg["seqlen_k"], cfg["heads_q"],
                            cfg["heads_kv"], cfg["head_dim"], cfg["dtype"], device="cpu",
                            k_ramp=cfg.get("k_ramp", False))
     g = cfg["heads_q"] // cfg["heads_kv"]
     pairs = visible_pairs(cfg["seqlen_q"], cfg["seqlen_k"], cfg["causal"], cfg["window"])
     flops_head = 4.0 * cfg["head_dim"] * pairs
+    total = cfg["batch"] * cfg["heads_q"]
     done, t0 = 0, time.perf_counter()
-    while done < cfg["heads_q"]:
-        h = done
-        oracle.attention_ref(q[:, :, h:h + 1].to(torch.float64).numpy(),
-                             k[:, :, h // g:h // g + 1].to(torch.float64).numpy(),
-                             v[:, :, h // g:h // g + 1].to(torch.float64).numpy(),
+    while done < total:
+        b, h = divmod(done, cfg["heads_q"])
+        oracle.attention_ref(q[b:b + 1, :, h:h + 1].to(torch.float64).numpy(),
+                             k[b:b + 1, :, h // g:h // g + 1].to(torch.float64).numpy(),
+                             v[b:b + 1, :, h // g:h // g + 1].to(torch.float64).numpy(),
                              scale=cfg.get("scale"), causal=cfg["causal"], window=cfg["window"],
                              softcap=cfg["softcap"])
         done += 1
@@ -125,8 +126,9 @@ def cpu_baseline(cfg, budget_s=12.0):
             threads = max(x.get("num_threads", 1) for x in info)
     return {"value": round(done * flops_head / dt / 1e12, 6), "unit": "TFLOP/s",
             "cores": threads if threads else os.cpu_count(), "kind": "oracle",
-            "sample": f"{done} of {cfg['batch'] * cfg['heads_q']} (batch, head) pairs of the workload, "
-                      f"each a full {cfg['seqlen_q']}x{cfg['seqlen_k']} head, fp64 NumPy, {dt:.1f} s",
+            "sample": f"{done} of {total} (batch, head) pairs of the workload"
+                      f"{' (the whole workload)' if done == total else ''}, each a full "
+                      f"{cfg['seqlen_q']}x{cfg['seqlen_k']} head, fp64 NumPy oracle, {dt:.1f} s",
             "host_cpus": os.cpu_count()}
 
 
@@ -150,6 +152,30 @@ def bench_dense(name, steps, warmup, torch, eng, W):
               "heads_q": c["heads_q"], "heads_kv": c["heads_kv"], "head_dim": c["head_dim"],
               "causal": c["causal"], "window": list(c["window"]), "softcap": c["softcap"],
               "flop_count": "4*D per visible (query, key) pair",
+              "flops_per_step": flops, "literal_formula_flops_per_step": literal,
+              "literal_formula_tflops": round(literal / (ms * 1e-3) / 1e12, 3)}
+    return ms, flops, config, c
+
+
+def bench_varlen(name, steps, warmup, torch, eng, W):
+    c = W.WORKLOADS[name]
+    q, k, v, cu, lens = W.make_varlen(c["seed"], c["n_seqs"], c["len_lo"], c["len_hi"], c["heads_q"],
+                                      c["heads_kv"], c["head_dim"], c["dtype"], device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((c["heads_q"], q.shape[0]), dtype=torch.float32, device="cuda")
+    mx = max(lens)
+
+    def step():
+        eng.attn_fwd_varlen(q, k, v, cu, cu, mx, mx, causal=c["causal"], window=c["window"],
+                            softcap=c["softcap"], out=o, lse=lse)
+
+    ms = time_region(step, steps, warmup, torch)
+    pairs = sum(visible_pairs(n, n, c["causal"], c["window"]) for n in lens)
+    flops = 4.0 * c["head_dim"] * pairs * c["heads_q"]
+    literal = sum(4.0 * c["heads_q"] * n * n * c["head_dim"] for n in lens)
+    config = {"workload": name, "n_seqs": c["n_seqs"], "lengths": lens, "total_tokens": int(q.shape[0]),
+              "heads_q": c["heads_q"], "heads_kv": c["heads_kv"], "head_dim": c["head_dim"],
+              "causal": c["causal"], "flop_count": "4*D per visible (query, key) pair",
               "flops_per_step": flops, "literal_formula_flops_per_step": literal,
               "literal_formula_tflops": round(literal / (ms * 1e-3) / 1e12, 3)}
     return ms, flops, config, c
@@ -234,7 +260,10 @@ def main():
         print(json.dumps(line), flush=True)
         return
 
-    ms, flops, config, cfg = bench_dense(args.workload, args.steps, args.warmup, torch, eng, W)
+    if c["kind"] == "varlen":
+        ms, flops, config, cfg = bench_varlen(args.workload, args.steps, args.warmup, torch, eng, W)
+    else:
+        ms, flops, config, cfg = bench_dense(args.workload, args.steps, args.warmup, torch, eng, W)
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_MFMA_TFLOPS[cfg["dtype"]]
     log(f"{args.workload}: {ms:.4f} ms/step, {tflops:.1f} TFLOP/s")
@@ -252,7 +281,7 @@ def main():
         line["secondary"] = [bench_kvcache("cfg5a_bf16_decode", max(5, args.steps // 5),
                                            max(2, args.warmup // 10), torch, eng, W)]
         torch.cuda.empty_cache()
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and c["kind"] == "dense":
         log("cpu baseline (oracle on a bounded sample)")
         line["cpu_baseline"] = cpu_baseline(cfg)
     print(json.dumps(line), flush=True)

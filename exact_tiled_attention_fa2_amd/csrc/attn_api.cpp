@@ -112,7 +112,6 @@ int attn_fwd(const attn_fwd_args* a, void* stream) {
   p.heads_q = a->heads_q; p.heads_kv = a->heads_kv; p.group = a->heads_q / a->heads_kv;
   p.pack_gqa = p.group > 1 ? 1 : 0;
   p.num_splits = 1;
-  p.num_m_tiles = ceil_div((int64_t)a->seqlen_q * (p.pack_gqa ? p.group : 1), attn::kBlockM);
   resolve_opts(a->opts, a->head_dim, p);
   return launch_status(attn::launch_fwd(p, a->dtype, a->head_dim, (hipStream_t)stream));
 }
@@ -153,7 +152,6 @@ int attn_fwd_varlen(const attn_varlen_args* a, void* workspace, size_t workspace
   p.heads_q = a->heads_q; p.heads_kv = a->heads_kv; p.group = a->heads_q / a->heads_kv;
   p.pack_gqa = p.group > 1 ? 1 : 0;
   p.num_splits = 1;
-  p.num_m_tiles = ceil_div((int64_t)a->max_seqlen_q * (p.pack_gqa ? p.group : 1), attn::kBlockM);
   resolve_opts(a->opts, a->head_dim, p);
   return launch_status(attn::launch_fwd(p, a->dtype, a->head_dim, (hipStream_t)stream));
 }
@@ -218,7 +216,6 @@ int attn_fwd_kvcache(const attn_kvcache_args* a, void* workspace, size_t workspa
   p.heads_q = a->heads_q; p.heads_kv = a->heads_kv; p.group = a->heads_q / a->heads_kv;
   p.pack_gqa = p.group > 1 ? 1 : 0;
   p.num_splits = splits;
-  p.num_m_tiles = ceil_div((int64_t)a->seqlen_q * (p.pack_gqa ? p.group : 1), attn::kBlockM);
   resolve_opts(a->opts, a->head_dim, p);
   if (splits > 1) {
     const size_t rows = (size_t)splits * a->batch * a->heads_q * a->seqlen_q;

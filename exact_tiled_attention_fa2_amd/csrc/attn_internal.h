@@ -29,7 +29,8 @@ struct FwdKernelParams {
   int32_t batch, seqlen_q, seqlen_k, heads_q, heads_kv, group;
   int32_t pack_gqa;     // 1: a query tile holds (row, head-in-group) pairs of one KV head
   int32_t num_splits;
-  int32_t num_m_tiles;  // query tiles per (batch, head) in the grid's x dimension
+  int32_t num_m_tiles;  // query tiles per (batch, head) in the grid's x dimension (set by the launcher)
+  int32_t col_group;    // (head, batch) columns per longest-first group (set by the launcher)
   int32_t window_left, window_right;  // -1 unbounded; causal already folded into window_right
   float scale_log2;     // factor of the raw score inside exp2: scale*log2(e), or log2(e) with softcap
   float scale_ln;       // running max -> natural-log units: scale, or 1 with softcap
@@ -47,7 +48,7 @@ struct CombineParams {
   int32_t batch, seqlen_q, heads_q, num_splits;
 };
 
-constexpr int kBlockM = 128;  // query rows (or packed row/head pairs) per workgroup
+constexpr int kBlockM = 128;  // nominal query rows per workgroup (split-count heuristic)
 
 // Host-side launchers (return a hipError_t).
 hipError_t launch_fwd(const FwdKernelParams& p, int dtype, int head_dim, hipStream_t stream);

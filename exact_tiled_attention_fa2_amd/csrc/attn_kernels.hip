@@ -39,6 +39,7 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "attn_internal.h"
@@ -114,8 +115,14 @@ __device__ __forceinline__ void dma16(const void* g, const char* lds) {
 
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
-template <class Ty, int D, int BK, bool SOFTCAP, int MIN_WG>
-__global__ void __launch_bounds__(256, MIN_WG) fwd_tile_kernel(const FwdKernelParams p) {
+// Forward tile kernel.  NW waves per workgroup, each owning QG groups of 32
+// query rows (BQ = 32 NW QG rows per workgroup); BK keys per KV step; LEAD
+// LDS operand reads kept in flight ahead of the MFMAs; WPE waves per SIMD.
+template <class Ty, int D, int BK, int NW, int QG, bool SOFTCAP, int LEAD, int WPE>
+__global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(WPE, WPE)))
+fwd_tile_kernel(const FwdKernelParams p) {
+  constexpr int NT = NW * 64;           // threads per workgroup
+  constexpr int BQ = 32 * NW * QG;      // query rows (packed row/head pairs) per workgroup
   constexpr int CH = D / 8;             // 16-byte chunks per row
   constexpr int ROWB = D * 2;           // bytes per LDS row
   constexpr int TILEB = BK * ROWB;      // bytes per K (or V) tile
@@ -123,10 +130,9 @@ __global__ void __launch_bounds__(256, MIN_WG) fwd_tile_kernel(const FwdKernelPa
   constexpr int DS = D / 16;            // MFMA k-steps over the head dim (QK^T)
   constexpr int DT = D / 32;            // 32-wide head-dim tiles of O^T
   constexpr int KS = BK / 16;           // MFMA k-steps over keys (PV)
-  constexpr int LOADS = BK * CH / 256;  // 16-byte copies per lane per tile
-  constexpr int ROWS_PER_COPY = 64 / CH;  // tile rows one wave-wide copy covers
+  constexpr int LOADS = BK * CH / NT;   // 16-byte copies per lane per tile
   constexpr int SWZ_MASK = CH < 16 ? CH - 1 : 15;
-  static_assert(LOADS >= 1 && (BK * CH) % 256 == 0, "tile must split evenly over 256 threads");
+  static_assert(LOADS >= 1 && (BK * CH) % NT == 0, "tile must split evenly over the workgroup");
 
   // Two K and two V tiles, as separate arrays so that each copy's target is
   // known at compile time (steps are unrolled by two).
@@ -142,20 +148,38 @@ __global__ void __launch_bounds__(256, MIN_WG) fwd_tile_kernel(const FwdKernelPa
   const int hl = lane >> 5;  // which half of the wave: selects keys 4..7 of every 8
 
   // ---------------------------------------------------------------- work item
-  // Workgroups are dealt round-robin to the 8 XCDs (each with its own L2).
-  // Renumber them so that every XCD receives a contiguous range of work items:
-  // all query tiles of one (batch, head) then run on one XCD and share its L2.
-  int wid;
+  // Work items are (query tile, head, batch x split).  Workgroups are dealt
+  // round-robin to the 8 XCDs (each with its own L2), so workgroup `lin`
+  // runs on XCD lin % 8 as that XCD's (lin / 8)-th workgroup.  Each XCD is
+  // given a contiguous set of (head, batch x split) columns, and walks them
+  // in groups of p.col_group columns whose K/V fit in its L2; inside a group
+  // it runs the heaviest query tile of every column first, so long causal
+  // tiles start early and short ones fill the tail (longest-first order).
+  int mt, head, zz;
   {
-    const int nx = gridDim.x, ny = gridDim.y;
-    const int total = nx * ny * (int)gridDim.z;
-    const int lin = (int)blockIdx.x + nx * ((int)blockIdx.y + ny * (int)blockIdx.z);
-    const int per = total >> 3;
-    wid = (lin < (per << 3)) ? (lin & 7) * per + (lin >> 3) : lin;
+    const int ny = gridDim.y;
+    const int nmt = p.num_m_tiles;
+    const int hz_total = ny * (int)gridDim.z;  // (head, batch x split) columns
+    const int lin = (int)blockIdx.x + (int)gridDim.x * ((int)blockIdx.y + ny * (int)blockIdx.z);
+    int col, rank;
+    if ((hz_total & 7) == 0) {
+      const int per_xcd = hz_total >> 3;
+      const int k = lin >> 3;                       // position in this XCD's sequence
+      const int cg = p.col_group;                   // columns per group
+      const int grp = k / (cg * nmt);
+      const int c0 = grp * cg;                      // first column of the group
+      const int gcols = min(cg, per_xcd - c0);      // the last group may be narrower
+      const int k2 = k - grp * cg * nmt;
+      rank = k2 / gcols;
+      col = (lin & 7) * per_xcd + c0 + (k2 - rank * gcols);
+    } else {
+      rank = lin / hz_total;
+      col = lin - rank * hz_total;
+    }
+    mt = nmt - 1 - rank;
+    head = col % ny;  // q head, or kv head when packing
+    zz = col / ny;
   }
-  const int mt = p.num_m_tiles - 1 - wid % p.num_m_tiles;  // heaviest causal tiles first
-  const int head = (wid / p.num_m_tiles) % (int)gridDim.y;   // q head, or kv head when packing
-  const int zz = wid / (p.num_m_tiles * (int)gridDim.y);
   const int b = zz / p.num_splits;
   const int split = zz - b * p.num_splits;
 
@@ -169,7 +193,7 @@ __global__ void __launch_bounds__(256, MIN_WG) fwd_tile_kernel(const FwdKernelPa
   if (p.seqused_k != nullptr) sk = min(max(p.seqused_k[b], 0), p.seqlen_k);
   const int G = p.pack_gqa ? p.group : 1;
   const int packed = sq * G;
-  const int m0 = mt * kBlockM;
+  const int m0 = mt * BQ;
   if (m0 >= packed) return;
   const int kvh = p.pack_gqa ? head : head / p.group;
   const int off = sk - sq;
@@ -177,7 +201,7 @@ __global__ void __launch_bounds__(256, MIN_WG) fwd_tile_kernel(const FwdKernelPa
 
   // KV range of the whole tile, then this split's share of whole KV steps.
   const int row_lo = m0 / G;
-  const int row_hi = min(packed - 1, m0 + kBlockM - 1) / G;
+  const int row_hi = min(packed - 1, m0 + BQ - 1) / G;
   int n_lo = 0, n_hi = sk;
   if (wl >= 0) n_lo = max(0, row_lo + off - wl);
   if (wr >= 0) n_hi = min(sk, row_hi + off + wr + 1);
@@ -194,37 +218,42 @@ __global__ void __launch_bounds__(256, MIN_WG) fwd_tile_kernel(const FwdKernelPa
     blk_lo = s0;
   }
 
-  // ---------------------------------------------------------------- this lane's query
-  const int pq = m0 + wave * 32 + l32;
-  const bool q_valid = pq < packed;
-  const int row = q_valid ? pq / G : 0;
-  const int hq = p.pack_gqa ? head * G + (q_valid ? pq - row * G : 0) : head;
+  // ---------------------------------------------------------------- this lane's queries
+  // Group g of this wave covers packed rows [m0 + 32 (QG wave + g), +32).
+  int row[QG], hq[QG], kmin[QG], kmax[QG], grow_lo[QG], grow_hi[QG];
+  bool q_valid[QG];
+#pragma unroll
+  for (int g = 0; g < QG; ++g) {
+    const int gpq_lo = m0 + 32 * (QG * wave + g);
+    const int pq = gpq_lo + l32;
+    q_valid[g] = pq < packed;
+    row[g] = q_valid[g] ? pq / G : 0;
+    hq[g] = p.pack_gqa ? head * G + (q_valid[g] ? pq - row[g] * G : 0) : head;
+    grow_lo[g] = gpq_lo / G;
+    grow_hi[g] = min(packed - 1, gpq_lo + 31) / G;
+    // Key bounds visible to this lane's row (inclusive), including the valid length.
+    kmin[g] = (wl >= 0) ? row[g] + off - wl : -0x40000000;
+    kmax[g] = min(sk - 1, (wr >= 0) ? row[g] + off + wr : 0x3fffffff);
+  }
 
-  // Rows covered by this wave (for the per-step mask decision).
-  const int wpq_lo = m0 + wave * 32;
-  const int wrow_lo = wpq_lo / G;
-  const int wrow_hi = min(packed - 1, wpq_lo + 31) / G;
-  // Key bounds visible to this lane's row (inclusive), including the valid length.
-  const int kmin = (wl >= 0) ? row + off - wl : -0x40000000;
-  const int kmax = min(sk - 1, (wr >= 0) ? row + off + wr : 0x3fffffff);
-
-  // Q fragment (B operand of S^T = K Q^T): 8 consecutive dims per k-step.
-  u32x4 qf[DS];
-  {
+  // Q fragments (B operand of S^T = K Q^T): 8 consecutive dims per k-step.
+  u32x4 qf[QG][DS];
+#pragma unroll
+  for (int g = 0; g < QG; ++g) {
     const uint16_t* qbase = reinterpret_cast<const uint16_t*>(p.q) + (int64_t)b * p.q_batch +
-                            (int64_t)(q_start + row) * p.q_row + (int64_t)hq * p.q_head;
+                            (int64_t)(q_start + row[g]) * p.q_row + (int64_t)hq[g] * p.q_head;
 #pragma unroll
     for (int t = 0; t < DS; ++t) {
-      if (q_valid) {
-        qf[t] = *reinterpret_cast<const u32x4*>(qbase + 16 * t + 8 * hl);
+      if (q_valid[g]) {
+        qf[g][t] = *reinterpret_cast<const u32x4*>(qbase + 16 * t + 8 * hl);
       } else {
-        qf[t] = u32x4{0u, 0u, 0u, 0u};
+        qf[g][t] = u32x4{0u, 0u, 0u, 0u};
       }
     }
-    // Retire the Q loads here, so the loop's only outstanding vector memory
-    // operations are the tile copies.
-    wait_vmem();
   }
+  // Retire the Q loads here, so the loop's only outstanding vector memory
+  // operations are the tile copies.
+  wait_vmem();
 
   // Per-lane LDS byte offsets of the MFMA operands (constant over the loop).
   int k_off[DS];
@@ -246,7 +275,7 @@ __global__ void __launch_bounds__(256, MIN_WG) fwd_tile_kernel(const FwdKernelPa
   }
 
   // HBM -> LDS tile copies.  Copy i of wave w fills LDS bytes
-  // [(4i + w) * 1024, +1024) of the tile; the lane that lands on row r,
+  // [(NW i + w) * 1024, +1024) of the tile; the lane that lands on row r,
   // chunk position pos fetches the global chunk pos ^ swizzle(r), which
   // produces the swizzled layout the operand reads expect.
   const char* kbase = reinterpret_cast<const char*>(p.k) +
@@ -257,7 +286,7 @@ __global__ void __launch_bounds__(256, MIN_WG) fwd_tile_kernel(const FwdKernelPa
   int cp_row[LOADS], cp_col[LOADS];  // tile row and global byte column of each copy
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
-    const int u = (4 * i + wave) * 64 + lane;
+    const int u = (NW * i + wave) * 64 + lane;
     const int r = u / CH, pos = u % CH;
     cp_row[i] = r;
     cp_col[i] = (pos ^ (chunk_swizzle(r & 15) & SWZ_MASK)) << 4;
@@ -268,7 +297,7 @@ __global__ void __launch_bounds__(256, MIN_WG) fwd_tile_kernel(const FwdKernelPa
       const char* tb = gbase + (int64_t)j0 * rowb;
 #pragma unroll
       for (int i = 0; i < LOADS; ++i)
-        dma16(tb + (uint32_t)(cp_row[i] * (int)rowb + cp_col[i]), tile + (4 * i + wave) * 1024);
+        dma16(tb + (uint32_t)(cp_row[i] * (int)rowb + cp_col[i]), tile + (NW * i + wave) * 1024);
     } else {
       // Last, partial step: rows at or past the valid length re-read row
       // sk-1 instead.  Their scores are masked to -inf, so P = 0 multiplies
@@ -277,81 +306,28 @@ __global__ void __launch_bounds__(256, MIN_WG) fwd_tile_kernel(const FwdKernelPa
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
         const int key = min(j0 + cp_row[i], sk - 1);
-        dma16(gbase + (int64_t)key * rowb + cp_col[i], tile + (4 * i + wave) * 1024);
+        dma16(gbase + (int64_t)key * rowb + cp_col[i], tile + (NW * i + wave) * 1024);
       }
     }
   };
-  (void)ROWS_PER_COPY;
 
-  // Running state: one query per lane (both halves hold the same m).
-  float m_run = -INFINITY;
-  float l_run = 0.0f;  // this half's partial row sum
-  f32x16 acc[DT];
+  // Running state: one query per lane and group (both halves hold the same m).
+  float m_run[QG], l_run[QG];  // l_run: this half's partial row sum
+  f32x16 acc[QG][DT];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
+  for (int g = 0; g < QG; ++g) {
+    m_run[g] = -INFINITY;
+    l_run[g] = 0.0f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[g][dt] = f32x16{};
+  }
 
   const float c2 = p.scale_log2;
   const float tau = p.tau;
-  const int n = blk_hi - blk_lo;
-
-  // ---- the pieces of one KV step
-  // S^T = K Q^T from an LDS K tile.
-  auto qk = [&](f32x16 (&sc)[KT], const char* kl) {
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) sc[kt] = f32x16{};
-#pragma unroll
-    for (int t = 0; t < DS; ++t) {
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(kl + kt * 32 * ROWB + k_off[t]);
-        sc[kt] = Ty::mfma(a, qf[t], sc[kt]);
-      }
-    }
-  };
-  // O^T += V^T P^T from an LDS V tile and the packed probabilities.
-  auto pv = [&](const uint32_t (&pkk)[KT][8], const char* vl) {
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const u32x4 bop = {pkk[ks >> 1][4 * (ks & 1) + 0], pkk[ks >> 1][4 * (ks & 1) + 1],
-                         pkk[ks >> 1][4 * (ks & 1) + 2], pkk[ks >> 1][4 * (ks & 1) + 3]};
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl + ks * 16 * ROWB + v_off[0][dt]));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl + ks * 16 * ROWB + v_off[1][dt]));
-        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
-        const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
-        const u32x4 aop = {lo2[0], lo2[1], hi2[0], hi2[1]};
-        acc[dt] = Ty::mfma(aop, bop, acc[dt]);
-      }
-    }
-  };
-  // Softcap and masks on the scores of step blk (masks only where an edge crosses it).
-  auto transform_and_mask = [&](f32x16 (&sc)[KT], int blk) {
-    if constexpr (SOFTCAP) {
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sc[kt][r] = transform_score<SOFTCAP>(sc[kt][r], p.softcap_pre, p.softcap);
-      }
-    }
-    const int j0 = blk * BK;
-    const int full_lo = (wl >= 0) ? wrow_hi + off - wl : -0x40000000;
-    const int full_hi = min(sk - 1, (wr >= 0) ? wrow_lo + off + wr : 0x3fffffff);
-    if (!(j0 >= full_lo && j0 + BK - 1 <= full_hi)) {
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = j0 + 32 * kt + 8 * (r >> 2) + 4 * hl + (r & 3);
-          if (key < kmin || key > kmax) sc[kt][r] = -INFINITY;
-        }
-      }
-    }
-  };
-
   // Rescale threshold in units of the raw score: the running max may lag the
   // block max by up to tau / c2 before O and l are rescaled.
   const float tau_raw = tau / c2;
+  const int n = blk_hi - blk_lo;
 
   // One KV step r (PAR = r & 1): the tiles of step r sit in buffers PAR; the
   // copies for step r+1 stream into the other pair meanwhile.
@@ -362,54 +338,119 @@ __global__ void __launch_bounds__(256, MIN_WG) fwd_tile_kernel(const FwdKernelPa
     char* const k_nxt = PAR ? lds_k0 : lds_k1;
     char* const v_nxt = PAR ? lds_v0 : lds_v1;
     const int blk = blk_lo + r;
+    const int j0 = blk * BK;
     if (r + 1 < n) {
       copy_tile(kbase, k_rowb, k_nxt, blk + 1);
       copy_tile(vbase, v_rowb, v_nxt, blk + 1);
     }
-    // ---- S^T = K Q^T
-    f32x16 sc[KT];
-    qk(sc, k_cur);
-    transform_and_mask(sc, blk);
-    // ---- block max of this lane's keys (one half of the row)
-    float mx = -INFINITY;
+    // ---- S^T = K Q^T: each K operand read feeds all QG groups
+    f32x16 sc[QG][KT];
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
+    for (int g = 0; g < QG; ++g)
 #pragma unroll
-      for (int r2 = 0; r2 < 16; ++r2) mx = fmaxf(mx, sc[kt][r2]);
-    }
-    // ---- RescaleThreshold with max lagging.  While no row's block max rises
-    // more than tau above its running max, the running max is kept as is (no
-    // exchange between the two halves is needed for that).  Otherwise the two
-    // halves agree on the row max and rows that rose too far are rescaled.
-    if (__any(mx > m_run + tau_raw)) {
-      const float mx_row = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx_row);
-      const float m_new_g = (m_new == -INFINITY) ? 0.0f : m_new;
-      const float diff = (m_run - m_new_g) * c2;  // <= 0; -inf on the first live step
-      if (!(diff >= -tau)) {
-        const float alpha = fast_exp2(diff);
-        l_run *= alpha;
+      for (int kt = 0; kt < KT; ++kt) sc[g][kt] = f32x16{};
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
-        m_run = m_new;
+    for (int t = 0; t < DS; ++t) {
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(k_cur + kt * 32 * ROWB + k_off[t]);
+#pragma unroll
+        for (int g = 0; g < QG; ++g) sc[g][kt] = Ty::mfma(a, qf[g][t], sc[g][kt]);
       }
     }
-    // ---- P = exp2((s - m) c2) <= exp2(tau), row sum, 16-bit pack
-    const float mg = (m_run == -INFINITY) ? 0.0f : m_run;
-    const float nb = -mg * c2;
-    uint32_t pk[KT][8];
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-#pragma unroll
-      for (int r2 = 0; r2 < 16; r2 += 2) {
-        const float p0 = fast_exp2(fmaf(sc[kt][r2], c2, nb));
-        const float p1 = fast_exp2(fmaf(sc[kt][r2 + 1], c2, nb));
-        l_run += p0 + p1;
-        pk[kt][r2 >> 1] = Ty::pack(p0, p1);
+    if constexpr (LEAD > 0) {
+      // Keep LEAD operand reads in flight ahead of the MFMAs.
+      __builtin_amdgcn_sched_group_barrier(0x100, LEAD, 0);
+      for (int i = 0; i < DS * KT; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, QG, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
     }
-    // ---- O^T += V^T P^T
-    pv(pk, v_cur);
+    uint32_t pk[QG][KT][8];
+#pragma unroll
+    for (int g = 0; g < QG; ++g) {
+      // ---- softcap, and masks where an edge crosses this step for the group
+      if constexpr (SOFTCAP) {
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+          for (int r2 = 0; r2 < 16; ++r2)
+            sc[g][kt][r2] = transform_score<SOFTCAP>(sc[g][kt][r2], p.softcap_pre, p.softcap);
+      }
+      const int full_lo = (wl >= 0) ? grow_hi[g] + off - wl : -0x40000000;
+      const int full_hi = min(sk - 1, (wr >= 0) ? grow_lo[g] + off + wr : 0x3fffffff);
+      if (!(j0 >= full_lo && j0 + BK - 1 <= full_hi)) {
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+          for (int r2 = 0; r2 < 16; ++r2) {
+            const int key = j0 + 32 * kt + 8 * (r2 >> 2) + 4 * hl + (r2 & 3);
+            if (key < kmin[g] || key > kmax[g]) sc[g][kt][r2] = -INFINITY;
+          }
+        }
+      }
+      // ---- block max of this lane's keys (one half of the row)
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int r2 = 0; r2 < 16; ++r2) mx = fmaxf(mx, sc[g][kt][r2]);
+      // ---- RescaleThreshold with max lagging.  While no row's block max
+      // rises more than tau above its running max, the running max is kept
+      // (no exchange between the two halves is needed for that).  Otherwise
+      // the halves agree on the row max and rows that rose too far rescale.
+      if (__any(mx > m_run[g] + tau_raw)) {
+        const float mx_row = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run[g], mx_row);
+        const float m_new_g = (m_new == -INFINITY) ? 0.0f : m_new;
+        const float diff = (m_run[g] - m_new_g) * c2;  // <= 0; -inf on the first live step
+        if (!(diff >= -tau)) {
+          const float alpha = fast_exp2(diff);
+          l_run[g] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) acc[g][dt] *= alpha;
+          m_run[g] = m_new;
+        }
+      }
+      // ---- P = exp2((s - m) c2) <= exp2(tau), row sum, 16-bit pack
+      const float mg = (m_run[g] == -INFINITY) ? 0.0f : m_run[g];
+      const float nb = -mg * c2;
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+        for (int r2 = 0; r2 < 16; r2 += 2) {
+          const float p0 = fast_exp2(fmaf(sc[g][kt][r2], c2, nb));
+          const float p1 = fast_exp2(fmaf(sc[g][kt][r2 + 1], c2, nb));
+          l_run[g] += p0 + p1;
+          pk[g][kt][r2 >> 1] = Ty::pack(p0, p1);
+        }
+      }
+    }
+    // ---- O^T += V^T P^T: each V^T operand read feeds all QG groups
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(v_cur + ks * 16 * ROWB + v_off[0][dt]));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(v_cur + ks * 16 * ROWB + v_off[1][dt]));
+        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
+        const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
+        const u32x4 aop = {lo2[0], lo2[1], hi2[0], hi2[1]};
+#pragma unroll
+        for (int g = 0; g < QG; ++g) {
+          const u32x4 bop = {pk[g][ks >> 1][4 * (ks & 1) + 0], pk[g][ks >> 1][4 * (ks & 1) + 1],
+                             pk[g][ks >> 1][4 * (ks & 1) + 2], pk[g][ks >> 1][4 * (ks & 1) + 3]};
+          acc[g][dt] = Ty::mfma(aop, bop, acc[g][dt]);
+        }
+      }
+    }
+    if constexpr (LEAD > 0) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * LEAD, 0);
+      for (int i = 0; i < KS * DT; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, QG, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+    }
     wait_vmem();  // the copies for step r+1 have landed in LDS
     __syncthreads();
   };
@@ -430,41 +471,44 @@ __global__ void __launch_bounds__(256, MIN_WG) fwd_tile_kernel(const FwdKernelPa
   }
 
   // ---------------------------------------------------------------- epilogue
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  const float mgf = (m_run == -INFINITY) ? 0.0f : m_run;
-  const float lse_val = l_tot > 0.0f ? mgf * p.scale_ln + logf(l_tot) : -INFINITY;
-  if (!q_valid) return;
-  if (p.o_part == nullptr) {
-    uint16_t* op = reinterpret_cast<uint16_t*>(p.o) + (int64_t)b * p.o_batch +
-                   (int64_t)(q_start + row) * p.o_row + (int64_t)hq * p.o_head;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
+  for (int g = 0; g < QG; ++g) {
+    const float l_tot = l_run[g] + __shfl_xor(l_run[g], 32);
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    const float mgf = (m_run[g] == -INFINITY) ? 0.0f : m_run[g];
+    const float lse_val = l_tot > 0.0f ? mgf * p.scale_ln + logf(l_tot) : -INFINITY;
+    if (!q_valid[g]) continue;
+    if (p.o_part == nullptr) {
+      uint16_t* op = reinterpret_cast<uint16_t*>(p.o) + (int64_t)b * p.o_batch +
+                     (int64_t)(q_start + row[g]) * p.o_row + (int64_t)hq[g] * p.o_head;
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = 32 * dt + 8 * g4 + 4 * hl;
-        u32x2 w;
-        w[0] = Ty::pack(acc[dt][4 * g4 + 0] * inv, acc[dt][4 * g4 + 1] * inv);
-        w[1] = Ty::pack(acc[dt][4 * g4 + 2] * inv, acc[dt][4 * g4 + 3] * inv);
-        *reinterpret_cast<u32x2*>(op + d0) = w;
+      for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d0 = 32 * dt + 8 * g4 + 4 * hl;
+          u32x2 w;
+          w[0] = Ty::pack(acc[g][dt][4 * g4 + 0] * inv, acc[g][dt][4 * g4 + 1] * inv);
+          w[1] = Ty::pack(acc[g][dt][4 * g4 + 2] * inv, acc[g][dt][4 * g4 + 3] * inv);
+          *reinterpret_cast<u32x2*>(op + d0) = w;
+        }
       }
-    }
-    if (hl == 0 && p.lse != nullptr)
-      p.lse[(int64_t)b * p.lse_batch + (int64_t)hq * p.lse_head + q_start + row] = lse_val;
-  } else {
-    const int64_t pr = (((int64_t)split * p.batch + b) * p.heads_q + hq) * p.seqlen_q + row;
-    float* op = p.o_part + pr * D;
+      if (hl == 0 && p.lse != nullptr)
+        p.lse[(int64_t)b * p.lse_batch + (int64_t)hq[g] * p.lse_head + q_start + row[g]] = lse_val;
+    } else {
+      const int64_t pr = (((int64_t)split * p.batch + b) * p.heads_q + hq[g]) * p.seqlen_q + row[g];
+      float* op = p.o_part + pr * D;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
+      for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = 32 * dt + 8 * g4 + 4 * hl;
-        const f32x4 w = {acc[dt][4 * g4 + 0] * inv, acc[dt][4 * g4 + 1] * inv,
-                         acc[dt][4 * g4 + 2] * inv, acc[dt][4 * g4 + 3] * inv};
-        *reinterpret_cast<f32x4*>(op + d0) = w;
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d0 = 32 * dt + 8 * g4 + 4 * hl;
+          const f32x4 w = {acc[g][dt][4 * g4 + 0] * inv, acc[g][dt][4 * g4 + 1] * inv,
+                           acc[g][dt][4 * g4 + 2] * inv, acc[g][dt][4 * g4 + 3] * inv};
+          *reinterpret_cast<f32x4*>(op + d0) = w;
+        }
       }
+      if (hl == 0) p.lse_part[pr] = lse_val;
     }
-    if (hl == 0) p.lse_part[pr] = lse_val;
   }
 }
 
@@ -509,12 +553,20 @@ __global__ void __launch_bounds__(256) combine_kernel(const CombineParams p) {
   if (dq == 0 && p.lse != nullptr) p.lse[r] = lse;
 }
 
-template <class Ty, int D, int BK, bool SOFTCAP, int MIN_WG>
-hipError_t launch_fwd_t(const FwdKernelParams& p, hipStream_t stream) {
-  auto kern = fwd_tile_kernel<Ty, D, BK, SOFTCAP, MIN_WG>;
+template <class Ty, int D, int BK, int NW, int QG, bool SOFTCAP, int LEAD, int WPE>
+hipError_t launch_fwd_t(FwdKernelParams p, hipStream_t stream) {
+  constexpr int BQ = 32 * NW * QG;
+  const int64_t rows = (int64_t)p.seqlen_q * (p.pack_gqa ? p.group : 1);
+  p.num_m_tiles = (int)((rows + BQ - 1) / BQ);
   const int heads_grid = p.pack_gqa ? p.heads_kv : p.heads_q;
+  {
+    // Columns per longest-first group: as many as keep ~8 MB of K/V live per XCD.
+    const int64_t kv_bytes = 2 * (int64_t)max(p.seqlen_k, 1) * D * 2 / p.num_splits;
+    const int per_xcd = max(1, heads_grid * p.batch * p.num_splits / 8);
+    p.col_group = (int)std::min<int64_t>(per_xcd, std::max<int64_t>(1, (int64_t(8) << 20) / kv_bytes));
+  }
   dim3 grid(p.num_m_tiles, heads_grid, p.batch * p.num_splits);
-  hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((fwd_tile_kernel<Ty, D, BK, NW, QG, SOFTCAP, LEAD, WPE>), grid, dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -527,22 +579,30 @@ int fwd_variant() {
   return v;
 }
 
-template <class Ty>
-hipError_t launch_fwd_dtype(const FwdKernelParams& p, int head_dim, hipStream_t stream) {
-  const bool cap = p.softcap > 0.0f;
+template <class Ty, bool CAP>
+hipError_t launch_fwd_cap(const FwdKernelParams& p, int head_dim, hipStream_t stream) {
   switch (head_dim) {
     case 64:
-      return cap ? launch_fwd_t<Ty, 64, 64, true, 2>(p, stream) : launch_fwd_t<Ty, 64, 64, false, 2>(p, stream);
+      return launch_fwd_t<Ty, 64, 64, 4, 1, CAP, 4, 2>(p, stream);
     case 128:
-      if (!cap && fwd_variant() == 1) return launch_fwd_t<Ty, 128, 32, false, 3>(p, stream);
-      if (!cap && fwd_variant() == 2) return launch_fwd_t<Ty, 128, 32, false, 2>(p, stream);
-      if (!cap && fwd_variant() == 3) return launch_fwd_t<Ty, 128, 64, false, 3>(p, stream);
-      return cap ? launch_fwd_t<Ty, 128, 64, true, 2>(p, stream) : launch_fwd_t<Ty, 128, 64, false, 2>(p, stream);
+      switch (fwd_variant()) {
+        case 1: return launch_fwd_t<Ty, 128, 64, 2, 2, CAP, 4, 1>(p, stream);
+        case 2: return launch_fwd_t<Ty, 128, 32, 2, 2, CAP, 4, 1>(p, stream);
+        case 3: return launch_fwd_t<Ty, 128, 64, 4, 2, CAP, 4, 1>(p, stream);
+        case 4: return launch_fwd_t<Ty, 128, 64, 2, 2, CAP, 8, 1>(p, stream);
+        default: return launch_fwd_t<Ty, 128, 64, 4, 1, CAP, 4, 2>(p, stream);
+      }
     case 256:
-      return cap ? launch_fwd_t<Ty, 256, 32, true, 1>(p, stream) : launch_fwd_t<Ty, 256, 32, false, 1>(p, stream);
+      return launch_fwd_t<Ty, 256, 32, 4, 1, CAP, 4, 1>(p, stream);
     default:
       return hipErrorInvalidValue;
   }
+}
+
+template <class Ty>
+hipError_t launch_fwd_dtype(const FwdKernelParams& p, int head_dim, hipStream_t stream) {
+  return p.softcap > 0.0f ? launch_fwd_cap<Ty, true>(p, head_dim, stream)
+                          : launch_fwd_cap<Ty, false>(p, head_dim, stream);
 }
 
 template <class Ty, int D>
