@@ -115,10 +115,19 @@ __device__ __forceinline__ void dma16(const void* g, const char* lds) {
 
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
+// s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt in bits 3:0 and 15:14), other counters untouched.
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // Forward tile kernel.  NW waves per workgroup, each owning QG groups of 32
 // query rows (BQ = 32 NW QG rows per workgroup); BK keys per KV step; LEAD
-// LDS operand reads kept in flight ahead of the MFMAs; WPE waves per SIMD.
-template <class Ty, int D, int BK, int NW, int QG, bool SOFTCAP, int LEAD, int WPE>
+// LDS operand reads kept in flight ahead of the MFMAs; WPE waves per SIMD;
+// NSTAGE K/V tile buffers (copies run NSTAGE - 1 steps ahead of compute).
+template <class Ty, int D, int BK, int NW, int QG, bool SOFTCAP, int LEAD, int WPE, int NSTAGE = 2,
+          bool PINGPONG = false>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(WPE, WPE)))
 fwd_tile_kernel(const FwdKernelParams p) {
   constexpr int NT = NW * 64;           // threads per workgroup
@@ -134,12 +143,31 @@ fwd_tile_kernel(const FwdKernelParams p) {
   constexpr int SWZ_MASK = CH < 16 ? CH - 1 : 15;
   static_assert(LOADS >= 1 && (BK * CH) % NT == 0, "tile must split evenly over the workgroup");
 
-  // Two K and two V tiles, as separate arrays so that each copy's target is
-  // known at compile time (steps are unrolled by two).
+  // NSTAGE K and V tile buffers, as separate arrays so that each copy's
+  // target is known at compile time (steps are unrolled by NSTAGE).
+  static_assert(NSTAGE >= 2 && NSTAGE <= 4, "2 to 4 stages");
   __shared__ __attribute__((aligned(16))) char lds_k0[TILEB];
   __shared__ __attribute__((aligned(16))) char lds_k1[TILEB];
+  __shared__ __attribute__((aligned(16))) char lds_k2[NSTAGE > 2 ? TILEB : 16];
+  __shared__ __attribute__((aligned(16))) char lds_k3[NSTAGE > 3 ? TILEB : 16];
   __shared__ __attribute__((aligned(16))) char lds_v0[TILEB];
   __shared__ __attribute__((aligned(16))) char lds_v1[TILEB];
+  __shared__ __attribute__((aligned(16))) char lds_v2[NSTAGE > 2 ? TILEB : 16];
+  __shared__ __attribute__((aligned(16))) char lds_v3[NSTAGE > 3 ? TILEB : 16];
+  auto kbuf = [&](auto st) __attribute__((always_inline)) -> char* {
+    constexpr int S = decltype(st)::value;
+    if constexpr (S == 0) return lds_k0;
+    else if constexpr (S == 1) return lds_k1;
+    else if constexpr (S == 2) return lds_k2;
+    else return lds_k3;
+  };
+  auto vbuf = [&](auto st) __attribute__((always_inline)) -> char* {
+    constexpr int S = decltype(st)::value;
+    if constexpr (S == 0) return lds_v0;
+    else if constexpr (S == 1) return lds_v1;
+    else if constexpr (S == 2) return lds_v2;
+    else return lds_v3;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -291,7 +319,7 @@ fwd_tile_kernel(const FwdKernelParams p) {
     cp_row[i] = r;
     cp_col[i] = (pos ^ (chunk_swizzle(r & 15) & SWZ_MASK)) << 4;
   }
-  auto copy_tile = [&](const char* gbase, int64_t rowb, char* tile, int blk) {
+  auto copy_tile = [&](const char* gbase, int64_t rowb, char* tile, int blk) __attribute__((always_inline)) {
     const int j0 = blk * BK;
     if (j0 + BK <= sk) {
       const char* tb = gbase + (int64_t)j0 * rowb;
@@ -329,22 +357,12 @@ fwd_tile_kernel(const FwdKernelParams p) {
   const float tau_raw = tau / c2;
   const int n = blk_hi - blk_lo;
 
-  // One KV step r (PAR = r & 1): the tiles of step r sit in buffers PAR; the
-  // copies for step r+1 stream into the other pair meanwhile.
-  auto step = [&](auto par, int r) {
-    constexpr int PAR = decltype(par)::value;
-    const char* const k_cur = PAR ? lds_k1 : lds_k0;
-    const char* const v_cur = PAR ? lds_v1 : lds_v0;
-    char* const k_nxt = PAR ? lds_k0 : lds_k1;
-    char* const v_nxt = PAR ? lds_v0 : lds_v1;
-    const int blk = blk_lo + r;
-    const int j0 = blk * BK;
-    if (r + 1 < n) {
-      copy_tile(kbase, k_rowb, k_nxt, blk + 1);
-      copy_tile(vbase, v_rowb, v_nxt, blk + 1);
-    }
-    // ---- S^T = K Q^T: each K operand read feeds all QG groups
-    f32x16 sc[QG][KT];
+  // ---- the three pieces of a KV step, on persistent per-wave registers
+  f32x16 sc[QG][KT];      // scores of the step being processed
+  uint32_t pk[QG][KT][8];  // its probabilities, packed to 16 bits
+
+  // S^T = K Q^T: each K operand read feeds all QG groups.
+  auto qk_part = [&](const char* k_cur) __attribute__((always_inline)) {
 #pragma unroll
     for (int g = 0; g < QG; ++g)
 #pragma unroll
@@ -358,15 +376,10 @@ fwd_tile_kernel(const FwdKernelParams p) {
         for (int g = 0; g < QG; ++g) sc[g][kt] = Ty::mfma(a, qf[g][t], sc[g][kt]);
       }
     }
-    if constexpr (LEAD > 0) {
-      // Keep LEAD operand reads in flight ahead of the MFMAs.
-      __builtin_amdgcn_sched_group_barrier(0x100, LEAD, 0);
-      for (int i = 0; i < DS * KT; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, QG, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-    }
-    uint32_t pk[QG][KT][8];
+  };
+  // Softcap, masks, RescaleThreshold with lagging, P = exp2(...), row sums, pack.
+  auto softmax_part = [&](int blk) __attribute__((always_inline)) {
+    const int j0 = blk * BK;
 #pragma unroll
     for (int g = 0; g < QG; ++g) {
       // ---- softcap, and masks where an edge crosses this step for the group
@@ -426,7 +439,9 @@ fwd_tile_kernel(const FwdKernelParams p) {
         }
       }
     }
-    // ---- O^T += V^T P^T: each V^T operand read feeds all QG groups
+  };
+  // O^T += V^T P^T: each V^T operand read feeds all QG groups.
+  auto pv_part = [&](const char* v_cur) __attribute__((always_inline)) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
@@ -444,6 +459,17 @@ fwd_tile_kernel(const FwdKernelParams p) {
         }
       }
     }
+  };
+  auto lead_qk = [&]() __attribute__((always_inline)) {
+    if constexpr (LEAD > 0) {  // keep LEAD operand reads in flight ahead of the MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, LEAD, 0);
+      for (int i = 0; i < DS * KT; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, QG, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
+  };
+  auto lead_pv = [&]() __attribute__((always_inline)) {
     if constexpr (LEAD > 0) {
       __builtin_amdgcn_sched_group_barrier(0x100, 2 * LEAD, 0);
       for (int i = 0; i < KS * DT; ++i) {
@@ -451,23 +477,150 @@ fwd_tile_kernel(const FwdKernelParams p) {
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
     }
-    wait_vmem();  // the copies for step r+1 have landed in LDS
-    __syncthreads();
   };
 
-  using P0 = std::integral_constant<int, 0>;
-  using P1 = std::integral_constant<int, 1>;
-  if (n > 0) {
-    copy_tile(kbase, k_rowb, lds_k0, blk_lo);
-    copy_tile(vbase, v_rowb, lds_v0, blk_lo);
-    wait_vmem();
-    __syncthreads();
-    int r = 0;
-    for (; r + 1 < n; r += 2) {
-      step(P0{}, r);
-      step(P1{}, r + 1);
+  if constexpr (!PINGPONG) {
+    // One KV step r with its tiles in stage ST = r % NSTAGE.  The copies for
+    // step r + NSTAGE - 1 stream into the stage step r - 1 released.
+    auto step = [&](auto st, int r) __attribute__((always_inline)) {
+      constexpr int ST = decltype(st)::value;
+      constexpr int FILL = (ST + NSTAGE - 1) % NSTAGE;
+      const int blk = blk_lo + r;
+      if (r + NSTAGE - 1 < n) {
+        copy_tile(kbase, k_rowb, kbuf(std::integral_constant<int, FILL>{}), blk + NSTAGE - 1);
+        copy_tile(vbase, v_rowb, vbuf(std::integral_constant<int, FILL>{}), blk + NSTAGE - 1);
+      }
+      qk_part(kbuf(std::integral_constant<int, ST>{}));
+      lead_qk();
+      softmax_part(blk);
+      pv_part(vbuf(std::integral_constant<int, ST>{}));
+      lead_pv();
+      // The copies for step r+1 must have landed; later steps' may still fly.
+      // Copies are issued in step order, 2 LOADS per step per lane.
+      const int later = min(NSTAGE - 2, n - 2 - r);  // steps r+2.. with copies in flight
+      if constexpr (NSTAGE >= 4) {
+        if (later >= 2) wait_vmem_le<4 * LOADS>();
+        else if (later == 1) wait_vmem_le<2 * LOADS>();
+        else wait_vmem();
+      } else if constexpr (NSTAGE == 3) {
+        if (later >= 1) wait_vmem_le<2 * LOADS>();
+        else wait_vmem();
+      } else {
+        wait_vmem();
+      }
+      __syncthreads();
+    };
+
+    if (n > 0) {
+      // Prologue: tiles of the first NSTAGE - 1 steps.
+      copy_tile(kbase, k_rowb, lds_k0, blk_lo);
+      copy_tile(vbase, v_rowb, lds_v0, blk_lo);
+      if constexpr (NSTAGE > 2) {
+        if (n > 1) {
+          copy_tile(kbase, k_rowb, lds_k1, blk_lo + 1);
+          copy_tile(vbase, v_rowb, lds_v1, blk_lo + 1);
+        }
+      }
+      if constexpr (NSTAGE > 3) {
+        if (n > 2) {
+          copy_tile(kbase, k_rowb, lds_k2, blk_lo + 2);
+          copy_tile(vbase, v_rowb, lds_v2, blk_lo + 2);
+        }
+      }
+      if constexpr (NSTAGE > 2) {
+        // step 0's tiles must have landed; later prologue copies may still fly
+        const int later = min(NSTAGE - 2, n - 1);
+        if (NSTAGE >= 4 && later >= 2) wait_vmem_le<4 * LOADS>();
+        else if (later >= 1) wait_vmem_le<2 * LOADS>();
+        else wait_vmem();
+      } else {
+        wait_vmem();
+      }
+      __syncthreads();
+      int r = 0;
+      for (; r + NSTAGE <= n; r += NSTAGE) {
+        step(std::integral_constant<int, 0>{}, r);
+        step(std::integral_constant<int, 1>{}, r + 1);
+        if constexpr (NSTAGE > 2) step(std::integral_constant<int, 2>{}, r + 2);
+        if constexpr (NSTAGE > 3) step(std::integral_constant<int, 3>{}, r + 3);
+      }
+      if (r < n) step(std::integral_constant<int, 0>{}, r);
+      if (r + 1 < n) step(std::integral_constant<int, 1>{}, r + 1);
+      if constexpr (NSTAGE > 2) {
+        if (r + 2 < n) step(std::integral_constant<int, 2>{}, r + 2);
+      }
     }
-    if (r < n) step(P0{}, r);
+  } else {
+    // Ping-pong: waves w and w + NW/2 share a SIMD (waves are dealt to the 4
+    // SIMDs round-robin).  The leading half runs its MFMA phase [PV(j-1),
+    // QK(j)] while the trailing half runs the softmax of the previous step,
+    // then they swap; a barrier separates phases, so on every SIMD one wave
+    // feeds the matrix core while the other works on the VALU.  Phase p:
+    // leading group works on q = p, trailing on q = p - 1; q = 2j is the MFMA
+    // phase of step j, q = 2j + 1 its softmax.  Copies of K(j+1) and V(j) are
+    // issued in phase 2j and must land by the end of phase 2j + 1; every
+    // buffer is refilled only after the last phase that reads it.
+    static_assert(NSTAGE == 2 && NW % 2 == 0, "ping-pong uses double buffers and paired waves");
+    const int trail = wave >= NW / 2 ? 1 : 0;
+    auto pp_barrier = [&]() __attribute__((always_inline)) { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+    // One phase; SLOT = p % 4 fixes every buffer choice at compile time.
+    auto phase = [&](auto slot, int p) __attribute__((always_inline)) {
+      constexpr int SLOT = decltype(slot)::value;
+      if constexpr ((SLOT & 1) == 0) {  // copies: K(j+1), V(j) for j = p / 2
+        const int j = p >> 1;
+        char* const kdst = (SLOT == 0) ? lds_k1 : lds_k0;  // K(j+1): j even -> buffer 1
+        char* const vdst = (SLOT == 0) ? lds_v0 : lds_v1;  // V(j):   j even -> buffer 0
+        if (j + 1 < n) copy_tile(kbase, k_rowb, kdst, blk_lo + j + 1);
+        if (j < n) copy_tile(vbase, v_rowb, vdst, blk_lo + j);
+      }
+      // Work of this wave: q = p - trail.  q even -> MFMA phase of step q/2
+      // (uses V of step q/2 - 1 and K of step q/2); q odd -> softmax of (q-1)/2.
+      // The parity of j = q/2 (or (q-1)/2) is fixed by SLOT and trail.
+      auto mfma_phase = [&](auto jpar, int j) __attribute__((always_inline)) {
+        constexpr int JP = decltype(jpar)::value;  // j & 1
+        __builtin_amdgcn_s_setprio(1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (j >= 1 && j <= n) {
+          pv_part(JP ? lds_v0 : lds_v1);  // V(j-1)
+          lead_pv();
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep QK's operand reads after PV
+        if (j < n) {
+          qk_part(JP ? lds_k1 : lds_k0);  // K(j)
+          lead_qk();
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
+      };
+      if (trail == 0) {
+        // q = p: SLOT 0 -> MFMA j even, 1 -> softmax j even, 2 -> MFMA j odd, 3 -> softmax j odd
+        if constexpr (SLOT == 0) mfma_phase(std::integral_constant<int, 0>{}, p >> 1);
+        else if constexpr (SLOT == 2) mfma_phase(std::integral_constant<int, 1>{}, p >> 1);
+        else { if ((p >> 1) < n) softmax_part(blk_lo + (p >> 1)); }
+      } else {
+        const int q = p - 1;
+        // SLOT 1 -> MFMA j even, 3 -> MFMA j odd, 0 and 2 -> softmax
+        if constexpr (SLOT == 1) mfma_phase(std::integral_constant<int, 0>{}, q >> 1);
+        else if constexpr (SLOT == 3) mfma_phase(std::integral_constant<int, 1>{}, q >> 1);
+        else { if (q >= 0 && (q >> 1) < n) softmax_part(blk_lo + (q >> 1)); }
+      }
+      if constexpr ((SLOT & 1) == 1) wait_vmem();  // copies of the previous phase have landed
+      pp_barrier();
+    };
+    if (n > 0) {
+      copy_tile(kbase, k_rowb, lds_k0, blk_lo);  // K(0)
+      wait_vmem();
+      pp_barrier();
+      const int phases = 2 * n + 2;
+      for (int p = 0; p < phases; p += 4) {
+        phase(std::integral_constant<int, 0>{}, p);
+        phase(std::integral_constant<int, 1>{}, p + 1);
+        if (p + 2 < phases) {
+          phase(std::integral_constant<int, 2>{}, p + 2);
+          phase(std::integral_constant<int, 3>{}, p + 3);
+        }
+      }
+    }
   }
 
   // ---------------------------------------------------------------- epilogue
@@ -553,7 +706,8 @@ __global__ void __launch_bounds__(256) combine_kernel(const CombineParams p) {
   if (dq == 0 && p.lse != nullptr) p.lse[r] = lse;
 }
 
-template <class Ty, int D, int BK, int NW, int QG, bool SOFTCAP, int LEAD, int WPE>
+template <class Ty, int D, int BK, int NW, int QG, bool SOFTCAP, int LEAD, int WPE, int NSTAGE = 2,
+          bool PINGPONG = false>
 hipError_t launch_fwd_t(FwdKernelParams p, hipStream_t stream) {
   constexpr int BQ = 32 * NW * QG;
   const int64_t rows = (int64_t)p.seqlen_q * (p.pack_gqa ? p.group : 1);
@@ -566,7 +720,7 @@ hipError_t launch_fwd_t(FwdKernelParams p, hipStream_t stream) {
     p.col_group = (int)std::min<int64_t>(per_xcd, std::max<int64_t>(1, (int64_t(8) << 20) / kv_bytes));
   }
   dim3 grid(p.num_m_tiles, heads_grid, p.batch * p.num_splits);
-  hipLaunchKernelGGL((fwd_tile_kernel<Ty, D, BK, NW, QG, SOFTCAP, LEAD, WPE>), grid, dim3(NW * 64), 0, stream, p);
+  hipLaunchKernelGGL((fwd_tile_kernel<Ty, D, BK, NW, QG, SOFTCAP, LEAD, WPE, NSTAGE, PINGPONG>), grid, dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -586,10 +740,10 @@ hipError_t launch_fwd_cap(const FwdKernelParams& p, int head_dim, hipStream_t st
       return launch_fwd_t<Ty, 64, 64, 4, 1, CAP, 4, 2>(p, stream);
     case 128:
       switch (fwd_variant()) {
-        case 1: return launch_fwd_t<Ty, 128, 64, 2, 2, CAP, 4, 1>(p, stream);
-        case 2: return launch_fwd_t<Ty, 128, 32, 2, 2, CAP, 4, 1>(p, stream);
-        case 3: return launch_fwd_t<Ty, 128, 64, 4, 2, CAP, 4, 1>(p, stream);
-        case 4: return launch_fwd_t<Ty, 128, 64, 2, 2, CAP, 8, 1>(p, stream);
+        case 1: return launch_fwd_t<Ty, 128, 64, 8, 1, CAP, 4, 2, 2, true>(p, stream);
+        case 2: return launch_fwd_t<Ty, 128, 64, 8, 1, CAP, 0, 2, 2, true>(p, stream);
+        case 3: return launch_fwd_t<Ty, 128, 32, 8, 1, CAP, 4, 2, 2, true>(p, stream);
+        case 4: return launch_fwd_t<Ty, 128, 64, 8, 1, CAP, 8, 2, 2, true>(p, stream);
         default: return launch_fwd_t<Ty, 128, 64, 4, 1, CAP, 4, 2>(p, stream);
       }
     case 256:
