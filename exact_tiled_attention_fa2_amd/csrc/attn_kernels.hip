@@ -264,6 +264,10 @@ fwd_tile_kernel(const FwdKernelParams p) {
     kmax[g] = min(sk - 1, (wr >= 0) ? row[g] + off + wr : 0x3fffffff);
   }
 
+  // A wave whose rows all lie past the end (decode packs only G x Sq rows)
+  // skips the compute and only takes part in the tile copies.
+  const bool wave_live = m0 + 32 * QG * wave < packed;
+
   // Q fragments (B operand of S^T = K Q^T): 8 consecutive dims per k-step.
   u32x4 qf[QG][DS];
 #pragma unroll
@@ -490,11 +494,13 @@ fwd_tile_kernel(const FwdKernelParams p) {
         copy_tile(kbase, k_rowb, kbuf(std::integral_constant<int, FILL>{}), blk + NSTAGE - 1);
         copy_tile(vbase, v_rowb, vbuf(std::integral_constant<int, FILL>{}), blk + NSTAGE - 1);
       }
-      qk_part(kbuf(std::integral_constant<int, ST>{}));
-      lead_qk();
-      softmax_part(blk);
-      pv_part(vbuf(std::integral_constant<int, ST>{}));
-      lead_pv();
+      if (wave_live) {  // waves whose rows are all padding only help with the copies
+        qk_part(kbuf(std::integral_constant<int, ST>{}));
+        lead_qk();
+        softmax_part(blk);
+        pv_part(vbuf(std::integral_constant<int, ST>{}));
+        lead_pv();
+      }
       // The copies for step r+1 must have landed; later steps' may still fly.
       // Copies are issued in step order, 2 LOADS per step per lane.
       const int later = min(NSTAGE - 2, n - 2 - r);  // steps r+2.. with copies in flight
@@ -666,44 +672,65 @@ fwd_tile_kernel(const FwdKernelParams p) {
 }
 
 // Log-sum-exp merge of the split partials: LSE = M + ln sum_s exp(LSE_s - M),
-// O = sum_s exp(LSE_s - LSE) O_s, in a fixed split order (deterministic).
-// Empty splits carry LSE_s = -inf and weight 0.  One thread per 4 dims.
+// O = sum_s exp(LSE_s - LSE) O_s.  One wave per output row: lanes stride over
+// the splits for the two reductions (fixed shuffle pattern), then every lane
+// sums its D/64 dims over the splits in split order -- deterministic.  Empty
+// splits carry LSE_s = -inf and weight 0.
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
 template <class Ty, int D>
 __global__ void __launch_bounds__(256) combine_kernel(const CombineParams p) {
-  constexpr int TPR = D / 4;  // threads per (b, h, row)
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  constexpr int DPL = D / 64;  // dims per lane
   const int64_t rows = (int64_t)p.batch * p.heads_q * p.seqlen_q;
-  const int64_t r = idx / TPR;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= rows) return;
-  const int dq = (int)(idx - r * TPR) * 4;
+  const int lane = threadIdx.x & 63;
+  const int ns = p.num_splits;
+  float mx = -INFINITY;
+  for (int s = lane; s < ns; s += 64) mx = fmaxf(mx, p.lse_part[s * rows + r]);
+  mx = wave_max(mx);
+  float lse = -INFINITY;
+  float o[DPL];
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) o[i] = 0.0f;
+  if (mx != -INFINITY) {
+    float sum = 0.0f;
+    for (int s = lane; s < ns; s += 64) sum += expf(p.lse_part[s * rows + r] - mx);
+    sum = wave_sum(sum);
+    lse = mx + logf(sum);
+    const float* op = p.o_part + r * D + lane * DPL;
+#pragma unroll 4
+    for (int s = 0; s < ns; ++s) {
+      const float ls = p.lse_part[s * rows + r];
+      const float w = (ls == -INFINITY) ? 0.0f : expf(ls - lse);
+      const float* src = op + s * rows * D;
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) o[i] += w * src[i];
+    }
+  }
   const int row = (int)(r % p.seqlen_q);
   const int64_t bh = r / p.seqlen_q;
   const int hq = (int)(bh % p.heads_q);
   const int b = (int)(bh / p.heads_q);
-  const int64_t sstride = rows;  // partial entries per split
-  float mx = -INFINITY;
-  for (int s = 0; s < p.num_splits; ++s) mx = fmaxf(mx, p.lse_part[s * sstride + r]);
-  f32x4 o = {0.f, 0.f, 0.f, 0.f};
-  float lse = -INFINITY;
-  if (mx != -INFINITY) {
-    float sum = 0.0f;
-    for (int s = 0; s < p.num_splits; ++s) sum += expf(p.lse_part[s * sstride + r] - mx);
-    lse = mx + logf(sum);
-    for (int s = 0; s < p.num_splits; ++s) {
-      const float ls = p.lse_part[s * sstride + r];
-      if (ls == -INFINITY) continue;
-      const float w = expf(ls - lse);
-      const f32x4 v = *reinterpret_cast<const f32x4*>(p.o_part + (s * sstride + r) * D + dq);
-      o += w * v;
-    }
+  uint16_t* dst = reinterpret_cast<uint16_t*>(p.o) + (int64_t)b * p.o_batch + (int64_t)row * p.o_row +
+                  (int64_t)hq * p.o_head + lane * DPL;
+  if constexpr (DPL == 1) {
+    f32x2 v2 = {o[0], 0.0f};
+    *dst = (uint16_t)(Ty::pack(v2[0], v2[1]) & 0xffffu);
+  } else {
+#pragma unroll
+    for (int i = 0; i < DPL; i += 2) *reinterpret_cast<uint32_t*>(dst + i) = Ty::pack(o[i], o[i + 1]);
   }
-  uint16_t* op = reinterpret_cast<uint16_t*>(p.o) + (int64_t)b * p.o_batch + (int64_t)row * p.o_row +
-                 (int64_t)hq * p.o_head + dq;
-  u32x2 w;
-  w[0] = Ty::pack(o[0], o[1]);
-  w[1] = Ty::pack(o[2], o[3]);
-  *reinterpret_cast<u32x2*>(op) = w;
-  if (dq == 0 && p.lse != nullptr) p.lse[r] = lse;
+  if (lane == 0 && p.lse != nullptr) p.lse[r] = lse;
 }
 
 template <class Ty, int D, int BK, int NW, int QG, bool SOFTCAP, int LEAD, int WPE, int NSTAGE = 2,
@@ -733,12 +760,31 @@ int fwd_variant() {
   return v;
 }
 
+// Decode tile variant for tuning sweeps (environment ATTN_MI355X_DEC_VARIANT); 0 = default.
+int dec_variant() {
+  static const int v = [] {
+    const char* e = getenv("ATTN_MI355X_DEC_VARIANT");
+    return e ? atoi(e) : 0;
+  }();
+  return v;
+}
+
 template <class Ty, bool CAP>
 hipError_t launch_fwd_cap(const FwdKernelParams& p, int head_dim, hipStream_t stream) {
   switch (head_dim) {
     case 64:
       return launch_fwd_t<Ty, 64, 64, 4, 1, CAP, 4, 2>(p, stream);
     case 128:
+      if ((int64_t)p.seqlen_q * (p.pack_gqa ? p.group : 1) <= 64) {
+        // Decode-shaped launches (few live rows; the KV stream dominates).
+        // Deeper buffering measured within noise of the prefill tile, which
+        // stays the default; the others remain selectable for sweeps.
+        switch (dec_variant()) {
+          case 1: return launch_fwd_t<Ty, 128, 32, 4, 1, CAP, 4, 2, 4>(p, stream);
+          case 2: return launch_fwd_t<Ty, 128, 32, 2, 1, CAP, 4, 2, 4>(p, stream);
+          default: break;
+        }
+      }
       switch (fwd_variant()) {
         case 1: return launch_fwd_t<Ty, 128, 64, 8, 1, CAP, 4, 2, 2, true>(p, stream);
         case 2: return launch_fwd_t<Ty, 128, 64, 8, 1, CAP, 0, 2, 2, true>(p, stream);
@@ -761,8 +807,8 @@ hipError_t launch_fwd_dtype(const FwdKernelParams& p, int head_dim, hipStream_t 
 
 template <class Ty, int D>
 hipError_t launch_combine_t(const CombineParams& p, hipStream_t stream) {
-  const int64_t threads = (int64_t)p.batch * p.heads_q * p.seqlen_q * (D / 4);
-  const int64_t blocks = (threads + 255) / 256;
+  const int64_t rows = (int64_t)p.batch * p.heads_q * p.seqlen_q;
+  const int64_t blocks = (rows + 3) / 4;
   hipLaunchKernelGGL((combine_kernel<Ty, D>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
