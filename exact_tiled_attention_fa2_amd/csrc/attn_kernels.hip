@@ -207,8 +207,7 @@ __device__ __forceinline__ bool tile_work(const FwdKernelParams& p, TileWork& w)
 // query rows (BQ = 32 NW QG rows per workgroup); BK keys per KV step; LEAD
 // LDS operand reads kept in flight ahead of the MFMAs; WPE waves per SIMD;
 // NSTAGE K/V tile buffers (copies run NSTAGE - 1 steps ahead of compute).
-template <class Ty, int D, int BK, int NW, int QG, bool SOFTCAP, int LEAD, int WPE, int NSTAGE = 2,
-          bool PINGPONG = false>
+template <class Ty, int D, int BK, int NW, int QG, bool SOFTCAP, int LEAD, int WPE, int NSTAGE = 2>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(WPE, WPE)))
 fwd_tile_kernel(const FwdKernelParams p) {
   constexpr int NT = NW * 64;           // threads per workgroup
@@ -502,149 +501,76 @@ fwd_tile_kernel(const FwdKernelParams p) {
     }
   };
 
-  if constexpr (!PINGPONG) {
-    // One KV step r with its tiles in stage ST = r % NSTAGE.  The copies for
-    // step r + NSTAGE - 1 stream into the stage step r - 1 released.
-    auto step = [&](auto st, int r) __attribute__((always_inline)) {
-      constexpr int ST = decltype(st)::value;
-      constexpr int FILL = (ST + NSTAGE - 1) % NSTAGE;
-      const int blk = blk_lo + r;
-      if (r + NSTAGE - 1 < n) {
-        copy_tile(kbase, k_rowb, kbuf(std::integral_constant<int, FILL>{}), blk + NSTAGE - 1);
-        copy_tile(vbase, v_rowb, vbuf(std::integral_constant<int, FILL>{}), blk + NSTAGE - 1);
-      }
-      if (wave_live) {  // waves whose rows are all padding only help with the copies
-        qk_part(kbuf(std::integral_constant<int, ST>{}));
-        lead_qk();
-        softmax_part(blk);
-        pv_part(vbuf(std::integral_constant<int, ST>{}));
-        lead_pv();
-      }
-      // The copies for step r+1 must have landed; later steps' may still fly.
-      // Copies are issued in step order, 2 LOADS per step per lane.
-      const int later = min(NSTAGE - 2, n - 2 - r);  // steps r+2.. with copies in flight
-      if constexpr (NSTAGE >= 4) {
-        if (later >= 2) wait_vmem_le<4 * LOADS>();
-        else if (later == 1) wait_vmem_le<2 * LOADS>();
-        else wait_vmem();
-      } else if constexpr (NSTAGE == 3) {
-        if (later >= 1) wait_vmem_le<2 * LOADS>();
-        else wait_vmem();
-      } else {
-        wait_vmem();
-      }
-      __syncthreads();
-    };
+  // One KV step r with its tiles in stage ST = r % NSTAGE.  The copies for
+  // step r + NSTAGE - 1 stream into the stage step r - 1 released.
+  auto step = [&](auto st, int r) __attribute__((always_inline)) {
+    constexpr int ST = decltype(st)::value;
+    constexpr int FILL = (ST + NSTAGE - 1) % NSTAGE;
+    const int blk = blk_lo + r;
+    if (r + NSTAGE - 1 < n) {
+      copy_tile(kbase, k_rowb, kbuf(std::integral_constant<int, FILL>{}), blk + NSTAGE - 1);
+      copy_tile(vbase, v_rowb, vbuf(std::integral_constant<int, FILL>{}), blk + NSTAGE - 1);
+    }
+    if (wave_live) {  // waves whose rows are all padding only help with the copies
+      qk_part(kbuf(std::integral_constant<int, ST>{}));
+      lead_qk();
+      softmax_part(blk);
+      pv_part(vbuf(std::integral_constant<int, ST>{}));
+      lead_pv();
+    }
+    // The copies for step r+1 must have landed; later steps' may still fly.
+    // Copies are issued in step order, 2 LOADS per step per lane.
+    const int later = min(NSTAGE - 2, n - 2 - r);  // steps r+2.. with copies in flight
+    if constexpr (NSTAGE >= 4) {
+      if (later >= 2) wait_vmem_le<4 * LOADS>();
+      else if (later == 1) wait_vmem_le<2 * LOADS>();
+      else wait_vmem();
+    } else if constexpr (NSTAGE == 3) {
+      if (later >= 1) wait_vmem_le<2 * LOADS>();
+      else wait_vmem();
+    } else {
+      wait_vmem();
+    }
+    __syncthreads();
+  };
 
-    if (n > 0) {
-      // Prologue: tiles of the first NSTAGE - 1 steps.
-      copy_tile(kbase, k_rowb, lds_k0, blk_lo);
-      copy_tile(vbase, v_rowb, lds_v0, blk_lo);
-      if constexpr (NSTAGE > 2) {
-        if (n > 1) {
-          copy_tile(kbase, k_rowb, lds_k1, blk_lo + 1);
-          copy_tile(vbase, v_rowb, lds_v1, blk_lo + 1);
-        }
-      }
-      if constexpr (NSTAGE > 3) {
-        if (n > 2) {
-          copy_tile(kbase, k_rowb, lds_k2, blk_lo + 2);
-          copy_tile(vbase, v_rowb, lds_v2, blk_lo + 2);
-        }
-      }
-      if constexpr (NSTAGE > 2) {
-        // step 0's tiles must have landed; later prologue copies may still fly
-        const int later = min(NSTAGE - 2, n - 1);
-        if (NSTAGE >= 4 && later >= 2) wait_vmem_le<4 * LOADS>();
-        else if (later >= 1) wait_vmem_le<2 * LOADS>();
-        else wait_vmem();
-      } else {
-        wait_vmem();
-      }
-      __syncthreads();
-      int r = 0;
-      for (; r + NSTAGE <= n; r += NSTAGE) {
-        step(std::integral_constant<int, 0>{}, r);
-        step(std::integral_constant<int, 1>{}, r + 1);
-        if constexpr (NSTAGE > 2) step(std::integral_constant<int, 2>{}, r + 2);
-        if constexpr (NSTAGE > 3) step(std::integral_constant<int, 3>{}, r + 3);
-      }
-      if (r < n) step(std::integral_constant<int, 0>{}, r);
-      if (r + 1 < n) step(std::integral_constant<int, 1>{}, r + 1);
-      if constexpr (NSTAGE > 2) {
-        if (r + 2 < n) step(std::integral_constant<int, 2>{}, r + 2);
+  if (n > 0) {
+    // Prologue: tiles of the first NSTAGE - 1 steps.
+    copy_tile(kbase, k_rowb, lds_k0, blk_lo);
+    copy_tile(vbase, v_rowb, lds_v0, blk_lo);
+    if constexpr (NSTAGE > 2) {
+      if (n > 1) {
+        copy_tile(kbase, k_rowb, lds_k1, blk_lo + 1);
+        copy_tile(vbase, v_rowb, lds_v1, blk_lo + 1);
       }
     }
-  } else {
-    // Ping-pong: waves w and w + NW/2 share a SIMD (waves are dealt to the 4
-    // SIMDs round-robin).  The leading half runs its MFMA phase [PV(j-1),
-    // QK(j)] while the trailing half runs the softmax of the previous step,
-    // then they swap; a barrier separates phases, so on every SIMD one wave
-    // feeds the matrix core while the other works on the VALU.  Phase p:
-    // leading group works on q = p, trailing on q = p - 1; q = 2j is the MFMA
-    // phase of step j, q = 2j + 1 its softmax.  Copies of K(j+1) and V(j) are
-    // issued in phase 2j and must land by the end of phase 2j + 1; every
-    // buffer is refilled only after the last phase that reads it.
-    static_assert(NSTAGE == 2 && NW % 2 == 0, "ping-pong uses double buffers and paired waves");
-    const int trail = wave >= NW / 2 ? 1 : 0;
-    auto pp_barrier = [&]() __attribute__((always_inline)) { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
-    // One phase; SLOT = p % 4 fixes every buffer choice at compile time.
-    auto phase = [&](auto slot, int p) __attribute__((always_inline)) {
-      constexpr int SLOT = decltype(slot)::value;
-      if constexpr ((SLOT & 1) == 0) {  // copies: K(j+1), V(j) for j = p / 2
-        const int j = p >> 1;
-        char* const kdst = (SLOT == 0) ? lds_k1 : lds_k0;  // K(j+1): j even -> buffer 1
-        char* const vdst = (SLOT == 0) ? lds_v0 : lds_v1;  // V(j):   j even -> buffer 0
-        if (j + 1 < n) copy_tile(kbase, k_rowb, kdst, blk_lo + j + 1);
-        if (j < n) copy_tile(vbase, v_rowb, vdst, blk_lo + j);
+    if constexpr (NSTAGE > 3) {
+      if (n > 2) {
+        copy_tile(kbase, k_rowb, lds_k2, blk_lo + 2);
+        copy_tile(vbase, v_rowb, lds_v2, blk_lo + 2);
       }
-      // Work of this wave: q = p - trail.  q even -> MFMA phase of step q/2
-      // (uses V of step q/2 - 1 and K of step q/2); q odd -> softmax of (q-1)/2.
-      // The parity of j = q/2 (or (q-1)/2) is fixed by SLOT and trail.
-      auto mfma_phase = [&](auto jpar, int j) __attribute__((always_inline)) {
-        constexpr int JP = decltype(jpar)::value;  // j & 1
-        __builtin_amdgcn_s_setprio(1);
-        __builtin_amdgcn_sched_barrier(0);
-        if (j >= 1 && j <= n) {
-          pv_part(JP ? lds_v0 : lds_v1);  // V(j-1)
-          lead_pv();
-        }
-        __builtin_amdgcn_sched_barrier(0);  // keep QK's operand reads after PV
-        if (j < n) {
-          qk_part(JP ? lds_k1 : lds_k0);  // K(j)
-          lead_qk();
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_setprio(0);
-      };
-      if (trail == 0) {
-        // q = p: SLOT 0 -> MFMA j even, 1 -> softmax j even, 2 -> MFMA j odd, 3 -> softmax j odd
-        if constexpr (SLOT == 0) mfma_phase(std::integral_constant<int, 0>{}, p >> 1);
-        else if constexpr (SLOT == 2) mfma_phase(std::integral_constant<int, 1>{}, p >> 1);
-        else { if ((p >> 1) < n) softmax_part(blk_lo + (p >> 1)); }
-      } else {
-        const int q = p - 1;
-        // SLOT 1 -> MFMA j even, 3 -> MFMA j odd, 0 and 2 -> softmax
-        if constexpr (SLOT == 1) mfma_phase(std::integral_constant<int, 0>{}, q >> 1);
-        else if constexpr (SLOT == 3) mfma_phase(std::integral_constant<int, 1>{}, q >> 1);
-        else { if (q >= 0 && (q >> 1) < n) softmax_part(blk_lo + (q >> 1)); }
-      }
-      if constexpr ((SLOT & 1) == 1) wait_vmem();  // copies of the previous phase have landed
-      pp_barrier();
-    };
-    if (n > 0) {
-      copy_tile(kbase, k_rowb, lds_k0, blk_lo);  // K(0)
+    }
+    if constexpr (NSTAGE > 2) {
+      // step 0's tiles must have landed; later prologue copies may still fly
+      const int later = min(NSTAGE - 2, n - 1);
+      if (NSTAGE >= 4 && later >= 2) wait_vmem_le<4 * LOADS>();
+      else if (later >= 1) wait_vmem_le<2 * LOADS>();
+      else wait_vmem();
+    } else {
       wait_vmem();
-      pp_barrier();
-      const int phases = 2 * n + 2;
-      for (int p = 0; p < phases; p += 4) {
-        phase(std::integral_constant<int, 0>{}, p);
-        phase(std::integral_constant<int, 1>{}, p + 1);
-        if (p + 2 < phases) {
-          phase(std::integral_constant<int, 2>{}, p + 2);
-          phase(std::integral_constant<int, 3>{}, p + 3);
-        }
-      }
+    }
+    __syncthreads();
+    int r = 0;
+    for (; r + NSTAGE <= n; r += NSTAGE) {
+      step(std::integral_constant<int, 0>{}, r);
+      step(std::integral_constant<int, 1>{}, r + 1);
+      if constexpr (NSTAGE > 2) step(std::integral_constant<int, 2>{}, r + 2);
+      if constexpr (NSTAGE > 3) step(std::integral_constant<int, 3>{}, r + 3);
+    }
+    if (r < n) step(std::integral_constant<int, 0>{}, r);
+    if (r + 1 < n) step(std::integral_constant<int, 1>{}, r + 1);
+    if constexpr (NSTAGE > 2) {
+      if (r + 2 < n) step(std::integral_constant<int, 2>{}, r + 2);
     }
   }
 
@@ -683,420 +609,6 @@ fwd_tile_kernel(const FwdKernelParams p) {
           const f32x4 w = {acc[g][dt][4 * g4 + 0] * inv, acc[g][dt][4 * g4 + 1] * inv,
                            acc[g][dt][4 * g4 + 2] * inv, acc[g][dt][4 * g4 + 3] * inv};
           *reinterpret_cast<f32x4*>(op + d0) = w;
-        }
-      }
-      if (hl == 0) p.lse_part[pr] = lse_val;
-    }
-  }
-}
-
-// Software-pipelined forward kernel.  Every wave owns QG groups of 32 query
-// rows, and each K or V^T operand read from LDS feeds the MFMAs of all its
-// groups (QG = 2 halves the LDS traffic per flop).  The score MFMAs
-// run one KV step ahead of the softmax, so the VALU work of step j overlaps
-// the matrix-core work of the same wave:
-//   segment 1 of step j:  MFMA  S(j+1) = K(j+1) Q^T     VALU  P(j) = exp2(...), row sums
-//   segment 2 of step j:  MFMA  O += V(j)^T P(j)^T      VALU  masks and block max of S(j+1)
-// followed by the (rare) rescale of O for step j+1 and one workgroup barrier,
-// after which the buffers of K(j+1) and V(j) take the copies of K(j+1+NSTAGE)
-// and V(j+NSTAGE).  The MFMAs write S(j+1) into `sc` while the softmax works
-// on a register copy `sv` of S(j).  One wave per SIMD; NW waves share the K/V
-// tiles; WPE waves per SIMD.
-template <class Ty, int D, int BK, int NW, int QG, bool SOFTCAP, int NSTAGE, int LEAD, int WPE>
-__global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(WPE, WPE)))
-fwd_pipe_kernel(const FwdKernelParams p) {
-  constexpr int NT = NW * 64;
-  constexpr int BQ = 32 * QG * NW;
-  constexpr int CH = D / 8;
-  constexpr int ROWB = D * 2;
-  constexpr int TILEB = BK * ROWB;
-  constexpr int KT = BK / 32;
-  constexpr int DS = D / 16;
-  constexpr int DT = D / 32;
-  constexpr int KS = BK / 16;
-  constexpr int LOADS = BK * CH / NT;
-  constexpr int SWZ_MASK = CH < 16 ? CH - 1 : 15;
-  constexpr int NIQ = DS * KT;  // K operand reads per step (QG MFMAs each)
-  constexpr int NIP = KS * DT;  // V^T operand reads per step (QG MFMAs each)
-  static_assert(LOADS >= 1 && (BK * CH) % NT == 0, "tile must split evenly over the workgroup");
-  static_assert(NSTAGE >= 2 && NSTAGE <= 4, "2 to 4 stages");
-
-  __shared__ __attribute__((aligned(16))) char lds_k[NSTAGE * TILEB];
-  __shared__ __attribute__((aligned(16))) char lds_v[NSTAGE * TILEB];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31;
-  const int hl = lane >> 5;
-
-  TileWork w;
-  if (!tile_work<BQ, BK>(p, w)) return;
-  const int b = w.b, split = w.split, head = w.head, kvh = w.kvh;
-  const int q_start = w.q_start, k_start = w.k_start, sk = w.sk;
-  const int G = w.G, packed = w.packed, m0 = w.m0, off = w.off;
-  const int blk_lo = w.blk_lo;
-  const int n = w.blk_hi - w.blk_lo;
-  const int wl = p.window_left, wr = p.window_right;
-
-  // ---------------------------------------------------------------- this lane's queries
-  int row[QG], hq[QG], kmin[QG], kmax[QG], full_lo[QG], full_hi[QG];
-  bool q_valid[QG];
-#pragma unroll
-  for (int g = 0; g < QG; ++g) {
-    const int gpq_lo = m0 + 32 * (QG * wave + g);
-    const int pq = gpq_lo + l32;
-    q_valid[g] = pq < packed;
-    row[g] = q_valid[g] ? pq / G : 0;
-    hq[g] = p.pack_gqa ? head * G + (q_valid[g] ? pq - row[g] * G : 0) : head;
-    const int grow_lo = gpq_lo / G;
-    const int grow_hi = min(packed - 1, gpq_lo + 31) / G;
-    kmin[g] = (wl >= 0) ? row[g] + off - wl : -0x40000000;
-    kmax[g] = min(sk - 1, (wr >= 0) ? row[g] + off + wr : 0x3fffffff);
-    // keys visible to every row of the group
-    full_lo[g] = (wl >= 0) ? grow_hi + off - wl : -0x40000000;
-    full_hi[g] = min(sk - 1, (wr >= 0) ? grow_lo + off + wr : 0x3fffffff);
-  }
-  u32x4 qf[QG][DS];
-#pragma unroll
-  for (int g = 0; g < QG; ++g) {
-    const uint16_t* qbase = reinterpret_cast<const uint16_t*>(p.q) + (int64_t)b * p.q_batch +
-                            (int64_t)(q_start + row[g]) * p.q_row + (int64_t)hq[g] * p.q_head;
-#pragma unroll
-    for (int t = 0; t < DS; ++t)
-      qf[g][t] = q_valid[g] ? *reinterpret_cast<const u32x4*>(qbase + 16 * t + 8 * hl) : u32x4{0u, 0u, 0u, 0u};
-  }
-  wait_vmem();
-
-  // Per-lane LDS byte offsets of the MFMA operands within a tile.
-  int k_off[DS];
-  {
-    const int sw = chunk_swizzle(lane & 15) & SWZ_MASK;
-#pragma unroll
-    for (int t = 0; t < DS; ++t) k_off[t] = l32 * ROWB + (((2 * t + hl) ^ sw) << 4);
-  }
-  int v_off[2][DT];
-  {
-    const int cl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-#pragma unroll
-    for (int r2 = 0; r2 < 2; ++r2) {
-      const int vrow = 4 * hl + 8 * r2 + ((lane & 15) >> 2);
-      const int x = cl ^ (chunk_swizzle(vrow) & SWZ_MASK);
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) v_off[r2][dt] = vrow * ROWB + (((4 * dt) ^ x) << 4) + ((lane & 1) << 3);
-    }
-  }
-
-  // HBM -> LDS tile copies (same layout and tail handling as fwd_tile_kernel).
-  const char* kbase = reinterpret_cast<const char*>(p.k) +
-                      2 * ((int64_t)b * p.k_batch + (int64_t)k_start * p.k_row + (int64_t)kvh * p.k_head);
-  const char* vbase = reinterpret_cast<const char*>(p.v) +
-                      2 * ((int64_t)b * p.v_batch + (int64_t)k_start * p.v_row + (int64_t)kvh * p.v_head);
-  const int64_t k_rowb = 2 * p.k_row, v_rowb = 2 * p.v_row;
-  int cp_row[LOADS], cp_col[LOADS], cp_k[LOADS], cp_v[LOADS];
-#pragma unroll
-  for (int i = 0; i < LOADS; ++i) {
-    const int u = (NW * i + wave) * 64 + lane;
-    const int r = u / CH, pos = u % CH;
-    cp_row[i] = r;
-    cp_col[i] = (pos ^ (chunk_swizzle(r & 15) & SWZ_MASK)) << 4;
-    cp_k[i] = cp_row[i] * (int)k_rowb + cp_col[i];  // byte offset inside a full K tile
-    cp_v[i] = cp_row[i] * (int)v_rowb + cp_col[i];
-  }
-  auto copy_tile = [&](const char* gbase, int64_t rowb, const int (&cp_off)[LOADS], char* tile, int blk)
-      __attribute__((always_inline)) {
-    const int j0 = blk * BK;
-    if (j0 + BK <= sk) {
-      const char* tb = gbase + (int64_t)j0 * rowb;
-#pragma unroll
-      for (int i = 0; i < LOADS; ++i) dma16(tb + (uint32_t)cp_off[i], tile + (NW * i + wave) * 1024);
-    } else {
-#pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        const int key = min(j0 + cp_row[i], sk - 1);
-        dma16(gbase + (int64_t)key * rowb + cp_col[i], tile + (NW * i + wave) * 1024);
-      }
-    }
-  };
-  auto kstage = [&](int j) __attribute__((always_inline)) -> const char* { return lds_k + (j % NSTAGE) * TILEB; };
-  auto vstage = [&](int j) __attribute__((always_inline)) -> const char* { return lds_v + (j % NSTAGE) * TILEB; };
-
-  // Running state.
-  float m_run[QG], l_run[QG], mx[QG];
-  f32x16 acc[QG][DT];
-#pragma unroll
-  for (int g = 0; g < QG; ++g) {
-    m_run[g] = -INFINITY;
-    l_run[g] = 0.0f;
-    mx[g] = -INFINITY;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) acc[g][dt] = f32x16{};
-  }
-  const float c2 = p.scale_log2;
-  const float tau = p.tau;
-  const float tau_raw = tau / c2;
-  f32x16 sc[QG][KT];       // scores being produced by the MFMAs
-  f32x16 sv[QG][KT];       // scores of the step in the softmax
-  uint32_t pk[QG][KT][8];  // probabilities of the step being accumulated, 16-bit pairs
-
-  // ---- MFMA work (each operand read feeds both groups)
-  auto qk_items = [&](const char* k_cur) __attribute__((always_inline)) {
-    u32x4 op[LEAD + 1];
-#pragma unroll
-    for (int i = 0; i < LEAD && i < NIQ; ++i) {
-      const int t = i / KT, kt = i % KT;
-      op[i] = *reinterpret_cast<const u32x4*>(k_cur + kt * 32 * ROWB + k_off[t]);
-    }
-#pragma unroll
-    for (int i = 0; i < NIQ; ++i) {
-      if (i + LEAD < NIQ) {
-        const int t = (i + LEAD) / KT, kt = (i + LEAD) % KT;
-        op[(i + LEAD) % (LEAD + 1)] = *reinterpret_cast<const u32x4*>(k_cur + kt * 32 * ROWB + k_off[t]);
-      }
-      const int t = i / KT, kt = i % KT;
-#pragma unroll
-      for (int g = 0; g < QG; ++g)
-        sc[g][kt] = Ty::mfma(op[i % (LEAD + 1)], qf[g][t], t == 0 ? f32x16{} : sc[g][kt]);
-    }
-  };
-  auto pv_items = [&](const char* v_cur) __attribute__((always_inline)) {
-    auto load = [&](int i) __attribute__((always_inline)) -> u32x4 {
-      const int ks = i / DT, dt = i % DT;
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(v_cur + ks * 16 * ROWB + v_off[0][dt]));
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(v_cur + ks * 16 * ROWB + v_off[1][dt]));
-      const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
-      const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
-      return u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
-    };
-    u32x4 op[LEAD + 1];
-#pragma unroll
-    for (int i = 0; i < LEAD && i < NIP; ++i) op[i] = load(i);
-#pragma unroll
-    for (int i = 0; i < NIP; ++i) {
-      if (i + LEAD < NIP) op[(i + LEAD) % (LEAD + 1)] = load(i + LEAD);
-      const int ks = i / DT, dt = i % DT;
-#pragma unroll
-      for (int g = 0; g < QG; ++g) {
-        const u32x4 bop = {pk[g][ks >> 1][4 * (ks & 1) + 0], pk[g][ks >> 1][4 * (ks & 1) + 1],
-                           pk[g][ks >> 1][4 * (ks & 1) + 2], pk[g][ks >> 1][4 * (ks & 1) + 3]};
-        acc[g][dt] = Ty::mfma(op[i % (LEAD + 1)], bop, acc[g][dt]);
-      }
-    }
-  };
-
-  // ---- softmax pieces, on the register copy sv
-  auto take_scores = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int g = 0; g < QG; ++g)
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) sv[g][kt] = sc[g][kt];
-  };
-  auto soft_cap = [&]() __attribute__((always_inline)) {
-    if constexpr (SOFTCAP) {
-#pragma unroll
-      for (int g = 0; g < QG; ++g)
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-          for (int r2 = 0; r2 < 16; ++r2)
-            sv[g][kt][r2] = transform_score<SOFTCAP>(sv[g][kt][r2], p.softcap_pre, p.softcap);
-    }
-  };
-  // Masks of KV step blk (only steps that cross a causal / window / length edge).
-  auto soft_mask = [&](int blk) __attribute__((always_inline)) {
-    const int j0 = blk * BK;
-#pragma unroll
-    for (int g = 0; g < QG; ++g)
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-        for (int r2 = 0; r2 < 16; ++r2) {
-          const int key = j0 + 32 * kt + 8 * (r2 >> 2) + 4 * hl + (r2 & 3);
-          if (key < kmin[g] || key > kmax[g]) sv[g][kt][r2] = -INFINITY;
-        }
-  };
-  // This half-row's block max.
-  auto soft_max = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int g = 0; g < QG; ++g) {
-      float m = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-        for (int r2 = 0; r2 < 16; ++r2) m = fmaxf(m, sv[g][kt][r2]);
-      mx[g] = m;
-    }
-  };
-  // RescaleThreshold with max lagging: when some row's block max rose more
-  // than tau above its running max, the halves agree on the row max and those
-  // rows rescale O and l (alpha = 1 for the others, so the branch is uniform).
-  auto soft_rescale = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int g = 0; g < QG; ++g) {
-      if (__any(mx[g] > m_run[g] + tau_raw)) {
-        const float mx_row = fmaxf(mx[g], __shfl_xor(mx[g], 32));
-        const float m_new = fmaxf(m_run[g], mx_row);
-        const float m_new_g = (m_new == -INFINITY) ? 0.0f : m_new;
-        const float diff = (m_run[g] - m_new_g) * c2;
-        const bool resc = !(diff >= -tau);
-        const float alpha = resc ? fast_exp2(diff) : 1.0f;
-        m_run[g] = resc ? m_new : m_run[g];
-        l_run[g] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) acc[g][dt] *= alpha;
-      }
-    }
-  };
-  // P = exp2((s - m) c2) <= exp2(tau), row sums, 16-bit pack.
-  auto soft_tail = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int g = 0; g < QG; ++g) {
-      const float mg = (m_run[g] == -INFINITY) ? 0.0f : m_run[g];
-      const float nb = -mg * c2;
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-#pragma unroll
-        for (int r2 = 0; r2 < 16; r2 += 2) {
-          const float p0 = fast_exp2(fmaf(sv[g][kt][r2], c2, nb));
-          const float p1 = fast_exp2(fmaf(sv[g][kt][r2 + 1], c2, nb));
-          l_run[g] += p0 + p1;
-          pk[g][kt][r2 >> 1] = Ty::pack(p0, p1);
-        }
-      }
-    }
-  };
-  // Does KV step blk need masks for either group?
-  auto needs_mask = [&](int blk) __attribute__((always_inline)) -> bool {
-    const int j0 = blk * BK;
-    bool m = false;
-#pragma unroll
-    for (int g = 0; g < QG; ++g) m = m || !(j0 >= full_lo[g] && j0 + BK - 1 <= full_hi[g]);
-    return m;
-  };
-
-  // ---- interleave hints: the score MFMAs spaced out by the softmax tail's
-  // VALU work, operand reads kept LEAD ahead of their MFMAs.
-  auto hint_qk_tail = [&]() __attribute__((always_inline)) {
-    constexpr int VPM = (KT * 60 + NIQ - 1) / NIQ;  // VALU per MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, LEAD, 0);
-#pragma unroll
-    for (int i = 0; i < NIQ; ++i) {
-#pragma unroll
-      for (int g = 0; g < QG; ++g) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-  };
-  auto hint_pv = [&]() __attribute__((always_inline)) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * LEAD, 0);
-#pragma unroll
-    for (int i = 0; i < NIP; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, QG, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-  };
-
-  // Copies issued at the barrier of step x (x = -1: after S(0)).
-  auto issue_copies = [&](int x) __attribute__((always_inline)) {
-    if (x + 1 + NSTAGE < n) copy_tile(kbase, k_rowb, cp_k, lds_k + ((x + 1 + NSTAGE) % NSTAGE) * TILEB, blk_lo + x + 1 + NSTAGE);
-    if (x + NSTAGE < n) copy_tile(vbase, v_rowb, cp_v, lds_v + ((x + NSTAGE) % NSTAGE) * TILEB, blk_lo + x + NSTAGE);
-  };
-  // Barrier of step j: K(j+2) and V(j+1) have landed (those of later steps
-  // may still fly), every wave is done with K(j+1) and V(j); refill those.
-  auto step_barrier = [&](int j) __attribute__((always_inline)) {
-    if constexpr (NSTAGE == 2) {
-      wait_vmem();
-    } else {
-      // copies of steps j-1 .. j+2-NSTAGE (issued after ours) may remain
-      int later = 0;
-#pragma unroll
-      for (int x = j + 3 - NSTAGE; x < j; ++x) later += (x + 1 + NSTAGE < n ? 1 : 0) + (x + NSTAGE < n ? 1 : 0);
-      if (later >= 4) wait_vmem_le<4 * LOADS>();
-      else if (later == 3) wait_vmem_le<3 * LOADS>();
-      else if (later == 2) wait_vmem_le<2 * LOADS>();
-      else if (later == 1) wait_vmem_le<LOADS>();
-      else wait_vmem();
-    }
-    __syncthreads();
-    issue_copies(j);
-  };
-
-  // One pipelined step j (S(j) in sv, j + 1 < n).
-  auto body = [&](int j) __attribute__((always_inline)) {
-    qk_items(kstage(j + 1));
-    soft_tail();
-    hint_qk_tail();
-    pv_items(vstage(j));
-    take_scores();
-    soft_cap();
-    hint_pv();
-    if (needs_mask(blk_lo + j + 1)) soft_mask(blk_lo + j + 1);
-    soft_max();
-    soft_rescale();
-    step_barrier(j);
-  };
-
-  if (n > 0) {
-    // Prologue: K(0..NSTAGE-1) and V(0..NSTAGE-2), then S(0) and its block max.
-#pragma unroll
-    for (int x = 0; x < NSTAGE; ++x)
-      if (x < n) copy_tile(kbase, k_rowb, cp_k, lds_k + x * TILEB, blk_lo + x);
-#pragma unroll
-    for (int x = 0; x + 1 < NSTAGE; ++x)
-      if (x < n) copy_tile(vbase, v_rowb, cp_v, lds_v + x * TILEB, blk_lo + x);
-    wait_vmem();
-    __syncthreads();
-    qk_items(lds_k);
-    take_scores();
-    soft_cap();
-    if (needs_mask(blk_lo)) soft_mask(blk_lo);
-    soft_max();
-    soft_rescale();
-    __syncthreads();  // every wave is done with K(0)
-    issue_copies(-1);
-    for (int j = 0; j + 1 < n; ++j) body(j);
-    // The last step: softmax tail, then O += V P.
-    soft_tail();
-    pv_items(vstage(n - 1));
-  }
-
-  // ---------------------------------------------------------------- epilogue
-#pragma unroll
-  for (int g = 0; g < QG; ++g) {
-    const float l_tot = l_run[g] + __shfl_xor(l_run[g], 32);
-    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    const float mgf = (m_run[g] == -INFINITY) ? 0.0f : m_run[g];
-    const float lse_val = l_tot > 0.0f ? mgf * p.scale_ln + logf(l_tot) : -INFINITY;
-    if (!q_valid[g]) continue;
-    if (p.o_part == nullptr) {
-      uint16_t* op = reinterpret_cast<uint16_t*>(p.o) + (int64_t)b * p.o_batch +
-                     (int64_t)(q_start + row[g]) * p.o_row + (int64_t)hq[g] * p.o_head;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int d0 = 32 * dt + 8 * g4 + 4 * hl;
-          u32x2 wv;
-          wv[0] = Ty::pack(acc[g][dt][4 * g4 + 0] * inv, acc[g][dt][4 * g4 + 1] * inv);
-          wv[1] = Ty::pack(acc[g][dt][4 * g4 + 2] * inv, acc[g][dt][4 * g4 + 3] * inv);
-          *reinterpret_cast<u32x2*>(op + d0) = wv;
-        }
-      }
-      if (hl == 0 && p.lse != nullptr)
-        p.lse[(int64_t)b * p.lse_batch + (int64_t)hq[g] * p.lse_head + q_start + row[g]] = lse_val;
-    } else {
-      const int64_t pr = (((int64_t)split * p.batch + b) * p.heads_q + hq[g]) * p.seqlen_q + row[g];
-      float* op = p.o_part + pr * D;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int d0 = 32 * dt + 8 * g4 + 4 * hl;
-          const f32x4 wv = {acc[g][dt][4 * g4 + 0] * inv, acc[g][dt][4 * g4 + 1] * inv,
-                            acc[g][dt][4 * g4 + 2] * inv, acc[g][dt][4 * g4 + 3] * inv};
-          *reinterpret_cast<f32x4*>(op + d0) = wv;
         }
       }
       if (hl == 0) p.lse_part[pr] = lse_val;
@@ -1173,22 +685,7 @@ int col_group_for(const FwdKernelParams& p, int heads_grid, int nz, int head_dim
   return (int)std::min<int64_t>(per_xcd, std::max<int64_t>(1, (int64_t(8) << 20) / kv_bytes));
 }
 
-template <class Ty, int D, int BK, int NW, int QG, bool SOFTCAP, int NSTAGE, int LEAD, int WPE>
-hipError_t launch_pipe_t(const FwdKernelParams& p_in, hipStream_t stream) {
-  FwdKernelParams p = p_in;
-  constexpr int BQ = 32 * QG * NW;
-  const int64_t packed = (int64_t)p.seqlen_q * (p.pack_gqa ? p.group : 1);
-  p.num_m_tiles = (int)((packed + BQ - 1) / BQ);
-  const int ny = p.pack_gqa ? p.heads_kv : p.heads_q;
-  const int nz = p.batch * p.num_splits;
-  p.col_group = col_group_for(p, ny, nz, D);
-  dim3 grid((unsigned)p.num_m_tiles, (unsigned)ny, (unsigned)nz);
-  hipLaunchKernelGGL((fwd_pipe_kernel<Ty, D, BK, NW, QG, SOFTCAP, NSTAGE, LEAD, WPE>), grid, dim3(NW * 64), 0, stream, p);
-  return hipGetLastError();
-}
-
-template <class Ty, int D, int BK, int NW, int QG, bool SOFTCAP, int LEAD, int WPE, int NSTAGE = 2,
-          bool PINGPONG = false>
+template <class Ty, int D, int BK, int NW, int QG, bool SOFTCAP, int LEAD, int WPE, int NSTAGE = 2>
 hipError_t launch_fwd_t(FwdKernelParams p, hipStream_t stream) {
   constexpr int BQ = 32 * NW * QG;
   const int64_t rows = (int64_t)p.seqlen_q * (p.pack_gqa ? p.group : 1);
@@ -1196,7 +693,7 @@ hipError_t launch_fwd_t(FwdKernelParams p, hipStream_t stream) {
   const int heads_grid = p.pack_gqa ? p.heads_kv : p.heads_q;
   p.col_group = col_group_for(p, heads_grid, p.batch * p.num_splits, D);
   dim3 grid(p.num_m_tiles, heads_grid, p.batch * p.num_splits);
-  hipLaunchKernelGGL((fwd_tile_kernel<Ty, D, BK, NW, QG, SOFTCAP, LEAD, WPE, NSTAGE, PINGPONG>), grid, dim3(NW * 64), 0, stream, p);
+  hipLaunchKernelGGL((fwd_tile_kernel<Ty, D, BK, NW, QG, SOFTCAP, LEAD, WPE, NSTAGE>), grid, dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -1223,44 +720,28 @@ hipError_t launch_fwd_cap(const FwdKernelParams& p, int head_dim, hipStream_t st
   switch (head_dim) {
     case 64:
       return launch_fwd_t<Ty, 64, 64, 4, 1, CAP, 4, 2>(p, stream);
-    case 128:
-      if ((int64_t)p.seqlen_q * (p.pack_gqa ? p.group : 1) <= 64) {
+    case 128: {
+      const int64_t packed = (int64_t)p.seqlen_q * (p.pack_gqa ? p.group : 1);
+      if (packed <= 64) {
         // Decode-shaped launches (few live rows; the KV stream dominates).
-        // Deeper buffering measured within noise of the prefill tile, which
-        // stays the default; the others remain selectable for sweeps.
         switch (dec_variant()) {
           case 1: return launch_fwd_t<Ty, 128, 32, 4, 1, CAP, 4, 2, 4>(p, stream);
-          case 2: return launch_fwd_t<Ty, 128, 32, 2, 1, CAP, 4, 2, 4>(p, stream);
-          default: break;
+          default: return launch_fwd_t<Ty, 128, 64, 4, 1, CAP, 4, 2>(p, stream);
         }
       }
       switch (fwd_variant()) {
-        case 1: return launch_fwd_t<Ty, 128, 64, 8, 1, CAP, 4, 2, 2, true>(p, stream);
-        case 2: return launch_fwd_t<Ty, 128, 64, 8, 1, CAP, 0, 2, 2, true>(p, stream);
-        case 3: return launch_fwd_t<Ty, 128, 32, 8, 1, CAP, 4, 2, 2, true>(p, stream);
-        case 4: return launch_fwd_t<Ty, 128, 64, 8, 1, CAP, 8, 2, 2, true>(p, stream);
-        case 5: return launch_fwd_t<Ty, 128, 64, 4, 2, CAP, 4, 1>(p, stream);
-        case 6: return launch_fwd_t<Ty, 128, 64, 2, 2, CAP, 4, 1>(p, stream);
-        case 7: return launch_fwd_t<Ty, 128, 64, 4, 2, CAP, 4, 1, 3>(p, stream);
-        case 8: return launch_fwd_t<Ty, 128, 32, 4, 2, CAP, 4, 1, 4>(p, stream);
-        case 9: return launch_pipe_t<Ty, 128, 32, 4, 1, CAP, 3, 4, 2>(p, stream);
-        case 10: return launch_pipe_t<Ty, 128, 32, 4, 1, CAP, 2, 4, 2>(p, stream);
-        case 11: return launch_pipe_t<Ty, 128, 32, 4, 1, CAP, 4, 2, 2>(p, stream);
-        case 12: return launch_pipe_t<Ty, 128, 32, 4, 2, CAP, 3, 2, 1>(p, stream);
-        case 13: return launch_pipe_t<Ty, 128, 64, 4, 1, CAP, 2, 4, 2>(p, stream);
-        case 14: return launch_fwd_t<Ty, 128, 64, 8, 1, CAP, 4, 2>(p, stream);
-        case 15: return launch_fwd_t<Ty, 128, 64, 4, 1, CAP, 8, 2>(p, stream);
-        case 16: return launch_fwd_t<Ty, 128, 32, 4, 1, CAP, 4, 2, 4>(p, stream);
-        case 17: return launch_fwd_t<Ty, 128, 32, 8, 1, CAP, 4, 2, 4>(p, stream);
-        case 18: return launch_fwd_t<Ty, 128, 64, 4, 1, CAP, 6, 2>(p, stream);
-        case 19: return launch_fwd_t<Ty, 128, 64, 8, 1, CAP, 4, 2, 3>(p, stream);
-        case 20: return launch_fwd_t<Ty, 128, 64, 8, 1, CAP, 6, 2>(p, stream);
-        case 21: return launch_fwd_t<Ty, 128, 64, 8, 1, CAP, 6, 2, 3>(p, stream);
-        case 22: return launch_fwd_t<Ty, 128, 32, 8, 1, CAP, 6, 2, 4>(p, stream);
-        case 23: return launch_pipe_t<Ty, 128, 64, 8, 1, CAP, 2, 4, 2>(p, stream);
-        case 24: return launch_pipe_t<Ty, 128, 32, 8, 1, CAP, 3, 4, 2>(p, stream);
-        default: return launch_fwd_t<Ty, 128, 64, 4, 1, CAP, 4, 2>(p, stream);
+        case 1: return launch_fwd_t<Ty, 128, 64, 4, 1, CAP, 4, 2>(p, stream);
+        case 2: return launch_fwd_t<Ty, 128, 64, 8, 1, CAP, 6, 2>(p, stream);
+        case 3: return launch_fwd_t<Ty, 128, 32, 4, 1, CAP, 4, 2, 4>(p, stream);
+        default:
+          // 256 query rows per workgroup (8 waves, one workgroup per CU) halve
+          // the K/V re-reads from L2 and win on dense launches; varlen tiles
+          // (more padding) and the VALU-heavy softcap path run faster with
+          // 128 rows and two workgroups per CU.
+          if (!CAP && p.cu_seqlens_q == nullptr) return launch_fwd_t<Ty, 128, 64, 8, 1, CAP, 6, 2>(p, stream);
+          return launch_fwd_t<Ty, 128, 64, 4, 1, CAP, 4, 2>(p, stream);
       }
+    }
     case 256:
       return launch_fwd_t<Ty, 256, 32, 4, 1, CAP, 4, 1>(p, stream);
     default:
