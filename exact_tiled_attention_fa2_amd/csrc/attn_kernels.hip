@@ -266,12 +266,18 @@ fwd_tile_kernel(const FwdKernelParams p) {
   (void)head;
 
   // ---------------------------------------------------------------- this lane's queries
-  // Group g of this wave covers packed rows [m0 + 32 (QG wave + g), +32).
+  // Row blocks of 32 QG packed rows are dealt to the waves so that the two
+  // waves sharing a SIMD (w and w + NW/2) hold an early and a late block:
+  // blocks 0, 2, 4, .. go to the first half, .., 5, 3, 1 to the second.  On
+  // causal diagonal tiles early blocks skip more fully masked steps, so this
+  // evens out the work per SIMD.  Group g of the wave covers packed rows
+  // [m0 + 32 (QG rb + g), +32).
+  const int rb = wave < NW / 2 ? 2 * wave : NW - 1 - 2 * (wave - NW / 2);
   int row[QG], hq[QG], kmin[QG], kmax[QG], grow_lo[QG], grow_hi[QG];
   bool q_valid[QG];
 #pragma unroll
   for (int g = 0; g < QG; ++g) {
-    const int gpq_lo = m0 + 32 * (QG * wave + g);
+    const int gpq_lo = m0 + 32 * (QG * rb + g);
     const int pq = gpq_lo + l32;
     q_valid[g] = pq < packed;
     row[g] = q_valid[g] ? pq / G : 0;
@@ -284,8 +290,16 @@ fwd_tile_kernel(const FwdKernelParams p) {
   }
 
   // A wave whose rows all lie past the end (decode packs only G x Sq rows)
-  // skips the compute and only takes part in the tile copies.
-  const bool wave_live = m0 + 32 * QG * wave < packed;
+  // skips the compute and only takes part in the tile copies; so does a wave
+  // on a KV step where none of its rows sees any key (the causal / window
+  // edge): every score would be masked, so the step changes nothing.
+  const bool wave_live = m0 + 32 * QG * rb < packed;
+  const int wk_lo = (wl >= 0) ? grow_lo[0] + off - wl : -0x40000000;
+  const int wk_hi = min(sk - 1, (wr >= 0) ? grow_hi[QG - 1] + off + wr : 0x3fffffff);
+  auto wave_sees = [&](int blk) __attribute__((always_inline)) -> bool {
+    const int j0 = blk * BK;
+    return j0 <= wk_hi && j0 + BK - 1 >= wk_lo;
+  };
 
   // Q fragments (B operand of S^T = K Q^T): 8 consecutive dims per k-step.
   u32x4 qf[QG][DS];
@@ -511,7 +525,7 @@ fwd_tile_kernel(const FwdKernelParams p) {
       copy_tile(kbase, k_rowb, kbuf(std::integral_constant<int, FILL>{}), blk + NSTAGE - 1);
       copy_tile(vbase, v_rowb, vbuf(std::integral_constant<int, FILL>{}), blk + NSTAGE - 1);
     }
-    if (wave_live) {  // waves whose rows are all padding only help with the copies
+    if (wave_live && wave_sees(blk)) {  // otherwise the wave only helps with the copies
       qk_part(kbuf(std::integral_constant<int, ST>{}));
       lead_qk();
       softmax_part(blk);
