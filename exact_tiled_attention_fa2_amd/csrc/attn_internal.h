@@ -31,6 +31,7 @@ struct FwdKernelParams {
   int32_t num_splits;
   int32_t num_m_tiles;  // query tiles per (batch, head) in the grid's x dimension (set by the launcher)
   int32_t col_group;    // (head, batch) columns per longest-first group (set by the launcher)
+  int32_t xcd_chunk;    // columns dealt to the XCDs in chunks of this many (set by the launcher)
   int32_t window_left, window_right;  // -1 unbounded; causal already folded into window_right
   float scale_log2;     // factor of the raw score inside exp2: scale*log2(e), or log2(e) with softcap
   float scale_ln;       // running max -> natural-log units: scale, or 1 with softcap
