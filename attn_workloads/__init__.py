@@ -143,3 +143,31 @@ def make_kvcache(seed, batch, seqlen_q, seqlen_k, heads_q, heads_kv, head_dim, d
             kc[b, n:] = float("nan")
             vc[b, n:] = float("nan")
     return q, kc, vc, lens.to(torch.int32).to(device)
+
+
+def page_cache(kc, vc, lens, page, seed, spare_pages=3):
+    """Scatter a contiguous cache [B, Sk, H, D] into a shuffled page pool.
+
+    Returns (pool_k, pool_v [num_pages, page, H, D], table int32 [B, ceil(Sk/page)]):
+    sequence b's i-th page lands in a random slot; spare slots and rows at or
+    past lens[b] hold NaN (they must never be read).  Input construction only.
+    """
+    b_, sk, h, d = kc.shape
+    per = -(-sk // page)
+    n_pages = b_ * per + spare_pages
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    slots = torch.randperm(n_pages, generator=g)
+    pool_k = torch.full((n_pages, page, h, d), float("nan"), dtype=kc.dtype, device=kc.device)
+    pool_v = torch.full_like(pool_k, float("nan"))
+    table = torch.zeros((b_, per), dtype=torch.int32)
+    lens_h = lens.cpu().tolist()
+    for b in range(b_):
+        for i in range(per):
+            s = int(slots[b * per + i])
+            table[b, i] = s
+            lo, hi = i * page, min((i + 1) * page, sk, max(int(lens_h[b]), 0))
+            if hi > lo:
+                pool_k[s, :hi - lo] = kc[b, lo:hi]
+                pool_v[s, :hi - lo] = vc[b, lo:hi]
+    return pool_k, pool_v, table.to(kc.device)
+

@@ -73,7 +73,9 @@ class KvcacheArgs(ctypes.Structure):
                 ("k_batch_stride", _i64), ("k_row_stride", _i64), ("k_head_stride", _i64),
                 ("v_batch_stride", _i64), ("v_row_stride", _i64), ("v_head_stride", _i64),
                 ("o_batch_stride", _i64), ("o_row_stride", _i64), ("o_head_stride", _i64),
-                ("opts", SoftmaxOpts)]
+                ("opts", SoftmaxOpts),
+                ("block_table", _vp), ("block_table_stride", _i32), ("page_block_size", _i32),
+                ("num_pages", _i32), ("reserved0", _i32)]
 
 
 _LIB = None
@@ -204,11 +206,26 @@ def attn_kvcache_workspace_bytes(batch, seqlen_q, heads_q, head_dim, num_splits)
 
 def attn_fwd_kvcache(q, k_cache, v_cache, cache_seqlens=None, num_splits=0, causal=False,
                      window=(-1, -1), softcap=0.0, softmax_scale=None, rescale_threshold=-1.0,
-                     out=None, lse=None, return_lse=True, workspace=None, stream=None):
-    """Split-KV attention against a cache: q [B, Sq, Hq, D], caches [B, Sk, Hkv, D]."""
-    _need_gpu(q, k_cache, v_cache, cache_seqlens)
+                     out=None, lse=None, return_lse=True, workspace=None, stream=None,
+                     block_table=None):
+    """Split-KV attention against a cache: q [B, Sq, Hq, D], caches [B, Sk, Hkv, D].
+
+    Paged cache: with block_table (int32 [B, max_pages_per_seq]) the caches are
+    [num_pages, page_block_size, Hkv, D] and the capacity per sequence is
+    max_pages_per_seq * page_block_size.
+    """
+    _need_gpu(q, k_cache, v_cache, cache_seqlens, block_table)
     b, sq, hq, d = q.shape
-    sk, hkv = k_cache.shape[1], k_cache.shape[2]
+    hkv = k_cache.shape[2]
+    if block_table is None:
+        sk = k_cache.shape[1]
+        paging = (None, 0, 0, 0)
+    else:
+        if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.stride(1) != 1:
+            raise TypeError("block_table must be an int32 [batch, pages] tensor with contiguous rows")
+        page = k_cache.shape[1]
+        sk = block_table.shape[1] * page
+        paging = (block_table, block_table.stride(0), page, k_cache.shape[0])
     if cache_seqlens is not None and cache_seqlens.dtype != torch.int32:
         raise TypeError("cache_seqlens must be int32")
     if out is None:
@@ -222,7 +239,8 @@ def attn_fwd_kvcache(q, k_cache, v_cache, cache_seqlens=None, num_splits=0, caus
     a = KvcacheArgs(_dtype_code(q), b, sq, sk, hq, hkv, d, splits, _ptr(q), _ptr(k_cache),
                     _ptr(v_cache), _ptr(cache_seqlens), _ptr(out), _ptr(lse),
                     *q.stride()[:3], *k_cache.stride()[:3], *v_cache.stride()[:3], *out.stride()[:3],
-                    _opts(causal, window, softcap, softmax_scale, rescale_threshold))
+                    _opts(causal, window, softcap, softmax_scale, rescale_threshold),
+                    _ptr(paging[0]), paging[1], paging[2], paging[3], 0)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().attn_fwd_kvcache(ctypes.byref(a), _ptr(workspace), ws_bytes, _stream(stream, q.device)),
            "attn_fwd_kvcache")

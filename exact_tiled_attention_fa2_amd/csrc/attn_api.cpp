@@ -187,6 +187,13 @@ int attn_fwd_kvcache(const attn_kvcache_args* a, void* workspace, size_t workspa
   if (a->batch == 0 || a->seqlen_q == 0) return ATTN_OK;
   if (a->q == nullptr || a->o == nullptr) return ATTN_E_NULL;
   if (a->seqlen_k > 0 && (a->k_cache == nullptr || a->v_cache == nullptr)) return ATTN_E_NULL;
+  if (a->block_table != nullptr) {
+    if (a->reserved0 != 0 || a->page_block_size <= 0 || a->page_block_size % 64 != 0) return ATTN_E_ARG;
+    if (a->num_pages <= 0 || a->block_table_stride <= 0 ||
+        (int64_t)a->block_table_stride * a->page_block_size < a->seqlen_k)
+      return ATTN_E_SHAPE;
+    if ((reinterpret_cast<uintptr_t>(a->block_table) & 3u) != 0) return ATTN_E_ALIGN;
+  }
   if (!aligned16(a->q) || !aligned16(a->k_cache) || !aligned16(a->v_cache) || !aligned16(a->o) ||
       !stride_ok(a->q_batch_stride) || !row_stride_ok(a->q_row_stride) || !stride_ok(a->q_head_stride) ||
       !stride_ok(a->k_batch_stride) || !row_stride_ok(a->k_row_stride) || !stride_ok(a->k_head_stride) ||
@@ -206,6 +213,12 @@ int attn_fwd_kvcache(const attn_kvcache_args* a, void* workspace, size_t workspa
   std::memset(&p, 0, sizeof(p));
   p.q = a->q; p.k = a->k_cache; p.v = a->v_cache; p.o = a->o; p.lse = a->lse;
   p.seqused_k = a->cache_seqlens;
+  if (a->block_table != nullptr) {
+    p.block_table = a->block_table;
+    p.bt_stride = a->block_table_stride;
+    p.page_size = a->page_block_size;
+    p.num_pages = a->num_pages;
+  }
   p.q_batch = a->q_batch_stride; p.q_row = a->q_row_stride; p.q_head = a->q_head_stride;
   p.k_batch = a->k_batch_stride; p.k_row = a->k_row_stride; p.k_head = a->k_head_stride;
   p.v_batch = a->v_batch_stride; p.v_row = a->v_row_stride; p.v_head = a->v_head_stride;

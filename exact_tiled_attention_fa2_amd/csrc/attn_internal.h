@@ -21,6 +21,8 @@ struct FwdKernelParams {
   const int32_t* cu_seqlens_q;  // varlen prefix sums [B+1] (null: dense)
   const int32_t* cu_seqlens_k;
   const int32_t* seqused_k;     // kv-cache valid lengths [B] (null: seqlen_k)
+  const int32_t* block_table;   // paged cache: page of (b, key / page_size) (null: contiguous)
+  int32_t bt_stride, page_size, num_pages;  // paged cache; k_batch / v_batch = page stride
   int64_t q_batch, q_row, q_head;
   int64_t k_batch, k_row, k_head;
   int64_t v_batch, v_row, v_head;

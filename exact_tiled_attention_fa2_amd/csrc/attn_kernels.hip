@@ -349,11 +349,14 @@ fwd_tile_kernel(const FwdKernelParams p) {
   // [(NW i + w) * 1024, +1024) of the tile; the lane that lands on row r,
   // chunk position pos fetches the global chunk pos ^ swizzle(r), which
   // produces the swizzled layout the operand reads expect.
+  // With a paged cache the batch term moves into the per-tile page lookup.
+  const bool paged = p.block_table != nullptr;
   const char* kbase = reinterpret_cast<const char*>(p.k) +
-                      2 * ((int64_t)b * p.k_batch + (int64_t)k_start * p.k_row + (int64_t)kvh * p.k_head);
+                      2 * ((paged ? 0 : (int64_t)b * p.k_batch + (int64_t)k_start * p.k_row) + (int64_t)kvh * p.k_head);
   const char* vbase = reinterpret_cast<const char*>(p.v) +
-                      2 * ((int64_t)b * p.v_batch + (int64_t)k_start * p.v_row + (int64_t)kvh * p.v_head);
+                      2 * ((paged ? 0 : (int64_t)b * p.v_batch + (int64_t)k_start * p.v_row) + (int64_t)kvh * p.v_head);
   const int64_t k_rowb = 2 * p.k_row, v_rowb = 2 * p.v_row;
+  const int64_t k_pageb = 2 * p.k_batch, v_pageb = 2 * p.v_batch;
   int cp_row[LOADS], cp_col[LOADS];  // tile row and global byte column of each copy
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
@@ -362,10 +365,16 @@ fwd_tile_kernel(const FwdKernelParams p) {
     cp_row[i] = r;
     cp_col[i] = (pos ^ (chunk_swizzle(r & 15) & SWZ_MASK)) << 4;
   }
-  auto copy_tile = [&](const char* gbase, int64_t rowb, char* tile, int blk) __attribute__((always_inline)) {
+  auto copy_tile = [&](const char* gbase, int64_t rowb, int64_t pageb, char* tile, int blk) __attribute__((always_inline)) {
     const int j0 = blk * BK;
+    const char* tb;  // row j0 of this tile
+    if (paged) {     // a tile never straddles pages (page size is a multiple of 64)
+      const int pg = min(max(p.block_table[(int64_t)b * p.bt_stride + j0 / p.page_size], 0), p.num_pages - 1);
+      tb = gbase + (int64_t)pg * pageb + (int64_t)(j0 % p.page_size) * rowb;
+    } else {
+      tb = gbase + (int64_t)j0 * rowb;
+    }
     if (j0 + BK <= sk) {
-      const char* tb = gbase + (int64_t)j0 * rowb;
 #pragma unroll
       for (int i = 0; i < LOADS; ++i)
         dma16(tb + (uint32_t)(cp_row[i] * (int)rowb + cp_col[i]), tile + (NW * i + wave) * 1024);
@@ -376,8 +385,8 @@ fwd_tile_kernel(const FwdKernelParams p) {
       // is never touched.
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
-        const int key = min(j0 + cp_row[i], sk - 1);
-        dma16(gbase + (int64_t)key * rowb + cp_col[i], tile + (NW * i + wave) * 1024);
+        const int r = min(cp_row[i], sk - 1 - j0);
+        dma16(tb + (int64_t)r * rowb + cp_col[i], tile + (NW * i + wave) * 1024);
       }
     }
   };
@@ -529,8 +538,8 @@ fwd_tile_kernel(const FwdKernelParams p) {
     constexpr int FILL = (ST + NSTAGE - 1) % NSTAGE;
     const int blk = blk_lo + r;
     if (r + NSTAGE - 1 < n) {
-      copy_tile(kbase, k_rowb, kbuf(std::integral_constant<int, FILL>{}), blk + NSTAGE - 1);
-      copy_tile(vbase, v_rowb, vbuf(std::integral_constant<int, FILL>{}), blk + NSTAGE - 1);
+      copy_tile(kbase, k_rowb, k_pageb, kbuf(std::integral_constant<int, FILL>{}), blk + NSTAGE - 1);
+      copy_tile(vbase, v_rowb, v_pageb, vbuf(std::integral_constant<int, FILL>{}), blk + NSTAGE - 1);
     }
     if (wave_live && wave_sees(blk)) {  // otherwise the wave only helps with the copies
       qk_part(kbuf(std::integral_constant<int, ST>{}));
@@ -557,18 +566,18 @@ fwd_tile_kernel(const FwdKernelParams p) {
 
   if (n > 0) {
     // Prologue: tiles of the first NSTAGE - 1 steps.
-    copy_tile(kbase, k_rowb, lds_k0, blk_lo);
-    copy_tile(vbase, v_rowb, lds_v0, blk_lo);
+    copy_tile(kbase, k_rowb, k_pageb, lds_k0, blk_lo);
+    copy_tile(vbase, v_rowb, v_pageb, lds_v0, blk_lo);
     if constexpr (NSTAGE > 2) {
       if (n > 1) {
-        copy_tile(kbase, k_rowb, lds_k1, blk_lo + 1);
-        copy_tile(vbase, v_rowb, lds_v1, blk_lo + 1);
+        copy_tile(kbase, k_rowb, k_pageb, lds_k1, blk_lo + 1);
+        copy_tile(vbase, v_rowb, v_pageb, lds_v1, blk_lo + 1);
       }
     }
     if constexpr (NSTAGE > 3) {
       if (n > 2) {
-        copy_tile(kbase, k_rowb, lds_k2, blk_lo + 2);
-        copy_tile(vbase, v_rowb, lds_v2, blk_lo + 2);
+        copy_tile(kbase, k_rowb, k_pageb, lds_k2, blk_lo + 2);
+        copy_tile(vbase, v_rowb, v_pageb, lds_v2, blk_lo + 2);
       }
     }
     if constexpr (NSTAGE > 2) {

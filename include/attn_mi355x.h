@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define ATTN_VERSION 100
+#define ATTN_VERSION 110
 
 enum attn_status {
   ATTN_OK = 0,
@@ -162,7 +162,21 @@ int attn_fwd_varlen(const attn_varlen_args* args, void* workspace, size_t worksp
  *   o like q, lse [batch, heads_q, seqlen_q] contiguous fp32 (may be NULL).
  *   workspace: attn_kvcache_workspace_bytes() bytes (fp32 partial outputs and
  *     LSEs of every split); may be NULL when that size is 0 (one split).
- * The result is independent of num_splits up to fp32 rounding.
+ * Paged cache (the paged KV caches of the Python API, "flash-attention"
+ * project survey page, csrc/flash_attn entry): when block_table is not NULL,
+ *   k_cache, v_cache are [num_pages, page_block_size, heads_kv, head_dim]
+ *     (k_batch_stride / v_batch_stride = stride between pages, the row
+ *     stride between rows of a page),
+ *   block_table: device int32 [batch, block_table_stride]; entry [b, i] is
+ *     the page that holds keys i*page_block_size .. (i+1)*page_block_size-1
+ *     of sequence b,
+ *   page_block_size: a positive multiple of 64 (a KV tile never straddles
+ *     pages), seqlen_k <= block_table_stride * page_block_size.
+ *   Entries outside [0, num_pages) are clamped into it: no memory outside the
+ *   cache is read, but the result is then unspecified.
+ *   With block_table NULL the four paging fields are ignored.
+ * The result is independent of num_splits up to fp32 rounding, and a paged
+ * cache gives the same bits as the contiguous cache it pages.
  */
 typedef struct attn_kvcache_args {
   int32_t dtype;
@@ -179,6 +193,11 @@ typedef struct attn_kvcache_args {
   int64_t v_batch_stride, v_row_stride, v_head_stride;
   int64_t o_batch_stride, o_row_stride, o_head_stride;
   attn_softmax_opts opts;
+  const int32_t* block_table; /* NULL: contiguous cache */
+  int32_t block_table_stride;
+  int32_t page_block_size;
+  int32_t num_pages;
+  int32_t reserved0;          /* must be 0 */
 } attn_kvcache_args;
 
 /* Split count the library picks when num_splits == 0 (never forced to 1

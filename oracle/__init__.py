@@ -39,6 +39,7 @@ from .attention import (  # noqa: F401
     attention_varlen_ref,
     attention_kvcache_ref,
     allowed_mask,
+    gather_pages,
 )
 from .tiled import tiled_ref  # noqa: F401
 from .metrics import rel_linf, cosine, lse_max_abs_err, compare  # noqa: F401

@@ -174,23 +174,46 @@ def attention_varlen_ref(q, k, v, cu_seqlens_q, cu_seqlens_k, **kw):
     return out, lse
 
 
-def attention_kvcache_ref(q, k_cache, v_cache, cache_seqlens=None, **kw):
+def gather_pages(pool, table_row, n):
+    """Rows 0..n-1 of one sequence of a paged cache, in key order.
+
+    pool [num_pages, page_size, Hkv, D]; table_row[i] is the page holding keys
+    i*page_size .. (i+1)*page_size - 1 (the paged KV cache of the Python API,
+    "flash-attention" project survey page, csrc/flash_attn entry; the layout
+    is this build's reading).  Only the pages covering the first n keys are
+    read.
+    """
+    page = pool.shape[1]
+    npages = -(-n // page)
+    rows = [pool[int(table_row[i])] for i in range(npages)]
+    if not rows:
+        return np.zeros((0,) + pool.shape[2:], dtype=pool.dtype)
+    return np.concatenate(rows, axis=0)[:n]
+
+
+def attention_kvcache_ref(q, k_cache, v_cache, cache_seqlens=None, block_table=None, **kw):
     """Attention of q [B, Sq, Hq, D] against the first cache_seqlens[b] rows of a cache.
 
-    k_cache/v_cache [B, Sk_max, Hkv, D].  Entries at or beyond the valid
-    length are not read at all (they may hold NaN).  Returns
-    (O [B, Sq, Hq, D], LSE [B, Hq, Sq]).
+    k_cache/v_cache [B, Sk_max, Hkv, D], or with block_table [B, pages_per_seq]
+    a page pool [num_pages, page_size, Hkv, D] (see gather_pages).  Entries at
+    or beyond the valid length are not read at all (they may hold NaN).
+    Returns (O [B, Sq, Hq, D], LSE [B, Hq, Sq]).
     """
     q = np.asarray(q, dtype=np.float64)
     batch = q.shape[0]
     if cache_seqlens is None:
-        cache_seqlens = [k_cache.shape[1]] * batch
+        cap = k_cache.shape[1] if block_table is None else len(block_table[0]) * k_cache.shape[1]
+        cache_seqlens = [cap] * batch
     out = np.zeros(q.shape[:3] + (v_cache.shape[3],), dtype=np.float64)
     lse = np.full((batch, q.shape[2], q.shape[1]), -np.inf, dtype=np.float64)
     for b in range(batch):
         n = int(cache_seqlens[b])
-        kb = np.asarray(k_cache[b:b + 1, :n], dtype=np.float64)
-        vb = np.asarray(v_cache[b:b + 1, :n], dtype=np.float64)
+        if block_table is None:
+            kb = np.asarray(k_cache[b:b + 1, :n], dtype=np.float64)
+            vb = np.asarray(v_cache[b:b + 1, :n], dtype=np.float64)
+        else:
+            kb = np.asarray(gather_pages(k_cache, block_table[b], n), dtype=np.float64)[None]
+            vb = np.asarray(gather_pages(v_cache, block_table[b], n), dtype=np.float64)[None]
         o_b, lse_b = attention_ref(q[b:b + 1], kb, vb, **kw)
         out[b] = o_b[0]
         lse[b] = lse_b[0]

@@ -274,6 +274,41 @@ def pin_decode_is_last_prefill_row():
     assert np.allclose(l1[:, :, 0], lse[:, :, -1], atol=1e-13)
 
 
+def pin_paged_cache_is_contiguous():
+    """A paged cache (pages scattered over a shuffled pool, the rest NaN) gives exactly the
+    result of the contiguous cache it pages, for lengths that end inside a page."""
+    rng = _rng(12)
+    b, sk, hkv, hq, d, page = 3, 20, 2, 4, 8, 4
+    q = rng.standard_normal((b, 2, hq, d))
+    k = rng.standard_normal((b, sk, hkv, d))
+    v = rng.standard_normal((b, sk, hkv, d))
+    lens = [13, 20, 1]
+    per = sk // page
+    pool_k = np.full((b * per + 3, page, hkv, d), np.nan)
+    pool_v = np.full((b * per + 3, page, hkv, d), np.nan)
+    slots = rng.permutation(b * per + 3)
+    table = np.zeros((b, per), dtype=np.int64)
+    for bi in range(b):
+        for i in range(per):
+            s_ = int(slots[bi * per + i])
+            table[bi, i] = s_
+            rows = slice(i * page, (i + 1) * page)
+            kk, vv = k[bi, rows].copy(), v[bi, rows].copy()
+            past = np.arange(i * page, (i + 1) * page) >= lens[bi]
+            kk[past] = np.nan                       # rows past the valid length are never read
+            vv[past] = np.nan
+            pool_k[s_], pool_v[s_] = kk, vv
+    for causal in (False, True):
+        o_c, l_c = oracle.attention_kvcache_ref(q, k, v, cache_seqlens=lens, causal=causal)
+        o_p, l_p = oracle.attention_kvcache_ref(q, pool_k, pool_v, cache_seqlens=lens,
+                                                block_table=table, causal=causal)
+        assert np.array_equal(o_c, o_p) and np.array_equal(l_c, l_p)
+    # the gather itself, row by row
+    for bi in range(b):
+        g = oracle.gather_pages(pool_k, table[bi], lens[bi])
+        assert np.array_equal(g, k[bi, :lens[bi]])
+
+
 # ---------------------------------------------------------------- library routines
 
 def _sdpa_ref(q, k, v, scale, mask_bool):
@@ -458,6 +493,7 @@ ALL_PINS = [
     pin_page_single_row_and_causal_row0,
     pin_page_lse_units,
     pin_decode_is_last_prefill_row,
+    pin_paged_cache_is_contiguous,
     pin_torch_sdpa,
     pin_varlen_block_diagonal,
     pin_gqa_is_repeated_mha,

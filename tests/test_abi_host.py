@@ -45,7 +45,7 @@ def test_library_exports_every_declared_function():
 
 def test_version_and_status_strings():
     h = _lib()
-    assert h.attn_version() == 100
+    assert h.attn_version() == 110
     for code in range(-9, 1):
         assert binding.status_string(code)
     assert binding.status_string(-1234) == "unknown status"
@@ -184,3 +184,32 @@ def test_kvcache_workspace_and_splits():
     assert h.attn_fwd_kvcache(ctypes.byref(ka), 16, need - 1, None) == binding.ATTN_E_WORKSPACE
     ka.num_splits = 999
     assert h.attn_fwd_kvcache(ctypes.byref(ka), 16, need, None) == binding.ATTN_E_ARG
+
+
+def test_kvcache_paged_validation():
+    """Page tables are checked on the host before any launch (fake device pointers here)."""
+    h = _lib()
+    ka = binding.KvcacheArgs(1, 2, 1, 512, 8, 2, 128, 1, 16, 16, 16, None, 16, None,
+                             8 * 128, 8 * 128, 128, 64 * 2 * 128, 2 * 128, 128,
+                             64 * 2 * 128, 2 * 128, 128, 8 * 128, 8 * 128, 128)
+    ka.opts = binding.SoftmaxOpts(0.0, 0, -1, -1, 0.0, -1.0)
+    ka.block_table, ka.block_table_stride, ka.page_block_size, ka.num_pages = 16, 8, 64, 20
+    def call():
+        return h.attn_fwd_kvcache(ctypes.byref(ka), None, 0, None)
+    ka.page_block_size = 96                      # not a multiple of 64
+    assert call() == binding.ATTN_E_ARG
+    ka.page_block_size = 0
+    assert call() == binding.ATTN_E_ARG
+    ka.page_block_size = 64
+    ka.reserved0 = 1
+    assert call() == binding.ATTN_E_ARG
+    ka.reserved0 = 0
+    ka.block_table_stride = 7                    # 7 * 64 < seqlen_k = 512
+    assert call() == binding.ATTN_E_SHAPE
+    ka.block_table_stride = 8
+    ka.num_pages = 0
+    assert call() == binding.ATTN_E_SHAPE
+    ka.num_pages = 20
+    ka.block_table = 18                          # not 4-byte aligned
+    assert call() == binding.ATTN_E_ALIGN
+

@@ -106,6 +106,19 @@ def _tiled_natural_exp(q_h, k_g, v_g, scale, causal, window, softcap, tau, block
         otiled.LOG2E = saved
 
 
+def _gather_row_shift(pool, table_row, n):
+    page = pool.shape[1]
+    flat = np.concatenate([pool[int(table_row[i])] for i in range(len(table_row))], axis=0)
+    return flat[1:n + 1] if n + 1 <= len(flat) else flat[:n]      # off by one row
+
+
+def _gather_page_order(pool, table_row, n):
+    page = pool.shape[1]
+    npages = -(-n // page)
+    rows = [pool[i] for i in range(npages)]                      # table ignored: pool order
+    return np.concatenate(rows, axis=0)[:n]
+
+
 MUTATIONS = {
     "causal_strict_lt": (oatt, "allowed_mask", _mask_causal_strict),
     "top_left_alignment": (oatt, "allowed_mask", _mask_top_left),
@@ -119,6 +132,8 @@ MUTATIONS = {
     "no_max_shift": (oatt, "_one_head", _one_head_no_max_shift),
     "tiled_keep_new_max": (otiled, "_tiled_one_head", _tiled_no_lagging),
     "tiled_wrong_exp_base": (otiled, "_tiled_one_head", _tiled_natural_exp),
+    "paged_row_off_by_one": (oatt, "gather_pages", _gather_row_shift),
+    "paged_table_ignored": (oatt, "gather_pages", _gather_page_order),
 }
 
 

@@ -164,6 +164,37 @@ def test_kvcache_small_nan_tail(case):
     gate_check(np64(o), ro, np64(lse), rl, dtype, f"kvcache {seed}")
 
 
+PAGED_SMALL = [
+    (61, 3, 1, 1000, 8, 2, 128, "bf16", 0, 64),
+    (62, 2, 3, 777, 8, 8, 64, "fp16", 5, 128),
+    (63, 2, 1, 500, 16, 2, 256, "fp16", 1, 64),
+    (64, 3, 1, 1000, 8, 2, 128, "bf16", 7, 256),
+]
+
+
+@pytest.mark.parametrize("case", PAGED_SMALL, ids=[f"s{c[0]}" for c in PAGED_SMALL])
+def test_kvcache_paged(case):
+    """Paged cache (shuffled pages, NaN in spare pages and past the valid lengths): the oracle's
+    answer, and for a fixed split count the same bits as the contiguous cache it pages."""
+    seed, b, sq, sk, hq, hkv, d, dtype, splits, page = case
+    print(f"[case] paged kvcache seed={seed} b={b} sq={sq} sk={sk} hq={hq} hkv={hkv} d={d} {dtype} "
+          f"splits={splits} page={page}", flush=True)
+    eng = _eng()
+    q, kc, vc, lens = W.make_kvcache(seed, b, sq, sk, hq, hkv, d, dtype, device="cuda",
+                                     random_lengths=True, nan_tail=True)
+    pk, pv, table = W.page_cache(kc, vc, lens, page, seed)
+    o, lse = eng.attn_fwd_kvcache(q, pk, pv, cache_seqlens=lens, num_splits=splits, causal=True,
+                                  block_table=table)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_kvcache_ref(np64(q), np64(pk), np64(pv), lens.cpu().numpy(),
+                                          block_table=table.cpu().numpy(), causal=True)
+    gate_check(np64(o), ro, np64(lse), rl, dtype, f"paged kvcache {seed}")
+    if splits:
+        oc, lc = eng.attn_fwd_kvcache(q, kc, vc, cache_seqlens=lens, num_splits=splits, causal=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o, oc) and torch.equal(lse, lc)
+
+
 def test_kvcache_split_invariance_and_prefill_match():
     """num_splits in {1, 2, 16, 37} agree; one split equals attn_fwd on the same cache."""
     print("[case] split invariance", flush=True)
