@@ -58,6 +58,9 @@ WORKLOADS = {
     "cfg5a_bf16_decode": dict(kind="kvcache", seed=1005, batch=32, seqlen_q=1, seqlen_k=32768,
                               heads_q=32, heads_kv=8, head_dim=128, dtype="bf16", causal=False,
                               window=(-1, -1), softcap=0.0, num_splits=16),
+    "cfg5a_bf16_decode_paged": dict(kind="kvcache", seed=1005, batch=32, seqlen_q=1, seqlen_k=32768,
+                                    heads_q=32, heads_kv=8, head_dim=128, dtype="bf16", causal=False,
+                                    window=(-1, -1), softcap=0.0, num_splits=16, page=256),
     "cfg5b_fp16_d256_causal": dict(kind="dense", seed=1006, batch=4, seqlen_q=4096,
                                    seqlen_k=4096, heads_q=32, heads_kv=8, head_dim=256,
                                    dtype="fp16", causal=True, window=(-1, -1), softcap=0.0),

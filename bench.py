@@ -185,6 +185,10 @@ def bench_kvcache(name, steps, warmup, torch, eng, W):
     c = W.WORKLOADS[name]
     q, kc, vc, lens = W.make_kvcache(c["seed"], c["batch"], c["seqlen_q"], c["seqlen_k"], c["heads_q"],
                                      c["heads_kv"], c["head_dim"], c["dtype"], device="cuda")
+    table = None
+    if c.get("page"):  # the same cache scattered over a shuffled page pool
+        kc, vc, table = W.page_cache(kc, vc, lens, c["page"], c["seed"])
+        torch.cuda.empty_cache()
     o = torch.empty_like(q)
     lse = torch.empty((c["batch"], c["heads_q"], c["seqlen_q"]), dtype=torch.float32, device="cuda")
     ws = torch.empty(eng.attn_kvcache_workspace_bytes(c["batch"], c["seqlen_q"], c["heads_q"],
@@ -193,7 +197,7 @@ def bench_kvcache(name, steps, warmup, torch, eng, W):
 
     def step():
         eng.attn_fwd_kvcache(q, kc, vc, cache_seqlens=lens, num_splits=c["num_splits"], out=o, lse=lse,
-                             workspace=ws)
+                             workspace=ws, block_table=table)
 
     ms = time_region(step, steps, warmup, torch)
     el = 2  # 16-bit
@@ -203,6 +207,7 @@ def bench_kvcache(name, steps, warmup, torch, eng, W):
     return {"workload": name, "ms_per_step": round(ms, 4), "value": round(gbs, 1), "unit": "GB/s",
             "bytes_per_step": bytes_alg, "num_splits": c["num_splits"],
             "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "peak": PEAK_HBM_GBS,
+            "page_block_size": c.get("page"),
             "note": "whole step (split kernel + combine); algorithmic bytes = K+V cache + Q + O + LSE"}
 
 

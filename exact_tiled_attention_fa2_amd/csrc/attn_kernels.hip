@@ -213,8 +213,10 @@ __device__ __forceinline__ bool tile_work(const FwdKernelParams& p, TileWork& w)
 // Forward tile kernel.  NW waves per workgroup, each owning QG groups of 32
 // query rows (BQ = 32 NW QG rows per workgroup); BK keys per KV step; LEAD
 // LDS operand reads kept in flight ahead of the MFMAs; WPE waves per SIMD;
-// NSTAGE K/V tile buffers (copies run NSTAGE - 1 steps ahead of compute).
-template <class Ty, int D, int BK, int NW, int QG, bool SOFTCAP, int LEAD, int WPE, int NSTAGE = 2>
+// NSTAGE K/V tile buffers (copies run NSTAGE - 1 steps ahead of compute);
+// PAGED: K/V rows come from a paged cache through p.block_table.
+template <class Ty, int D, int BK, int NW, int QG, bool SOFTCAP, int LEAD, int WPE, int NSTAGE = 2,
+          bool PAGED = false>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(WPE, WPE)))
 fwd_tile_kernel(const FwdKernelParams p) {
   constexpr int NT = NW * 64;           // threads per workgroup
@@ -350,7 +352,7 @@ fwd_tile_kernel(const FwdKernelParams p) {
   // chunk position pos fetches the global chunk pos ^ swizzle(r), which
   // produces the swizzled layout the operand reads expect.
   // With a paged cache the batch term moves into the per-tile page lookup.
-  const bool paged = p.block_table != nullptr;
+  constexpr bool paged = PAGED;
   const char* kbase = reinterpret_cast<const char*>(p.k) +
                       2 * ((paged ? 0 : (int64_t)b * p.k_batch + (int64_t)k_start * p.k_row) + (int64_t)kvh * p.k_head);
   const char* vbase = reinterpret_cast<const char*>(p.v) +
@@ -365,11 +367,16 @@ fwd_tile_kernel(const FwdKernelParams p) {
     cp_row[i] = r;
     cp_col[i] = (pos ^ (chunk_swizzle(r & 15) & SWZ_MASK)) << 4;
   }
-  auto copy_tile = [&](const char* gbase, int64_t rowb, int64_t pageb, char* tile, int blk) __attribute__((always_inline)) {
+  // Page holding KV step blk of a paged cache (clamped into the pool); a
+  // tile never straddles pages (the page size is a multiple of 64).
+  auto page_of = [&](int blk) __attribute__((always_inline)) -> int {
+    return min(max(p.block_table[(int64_t)b * p.bt_stride + blk * BK / p.page_size], 0), p.num_pages - 1);
+  };
+  auto copy_tile = [&](const char* gbase, int64_t rowb, int64_t pageb, char* tile, int blk, int pg)
+      __attribute__((always_inline)) {
     const int j0 = blk * BK;
     const char* tb;  // row j0 of this tile
-    if (paged) {     // a tile never straddles pages (page size is a multiple of 64)
-      const int pg = min(max(p.block_table[(int64_t)b * p.bt_stride + j0 / p.page_size], 0), p.num_pages - 1);
+    if constexpr (paged) {
       tb = gbase + (int64_t)pg * pageb + (int64_t)(j0 % p.page_size) * rowb;
     } else {
       tb = gbase + (int64_t)j0 * rowb;
@@ -531,6 +538,8 @@ fwd_tile_kernel(const FwdKernelParams p) {
     }
   };
 
+  int pg_next = 0;  // page of the next in-loop copy (paged cache)
+
   // One KV step r with its tiles in stage ST = r % NSTAGE.  The copies for
   // step r + NSTAGE - 1 stream into the stage step r - 1 released.
   auto step = [&](auto st, int r) __attribute__((always_inline)) {
@@ -538,8 +547,12 @@ fwd_tile_kernel(const FwdKernelParams p) {
     constexpr int FILL = (ST + NSTAGE - 1) % NSTAGE;
     const int blk = blk_lo + r;
     if (r + NSTAGE - 1 < n) {
-      copy_tile(kbase, k_rowb, k_pageb, kbuf(std::integral_constant<int, FILL>{}), blk + NSTAGE - 1);
-      copy_tile(vbase, v_rowb, v_pageb, vbuf(std::integral_constant<int, FILL>{}), blk + NSTAGE - 1);
+      const int pg = pg_next;  // looked up one step ahead, off the copy's critical path
+      if constexpr (paged) {
+        if (r + NSTAGE < n) pg_next = page_of(blk + NSTAGE);
+      }
+      copy_tile(kbase, k_rowb, k_pageb, kbuf(std::integral_constant<int, FILL>{}), blk + NSTAGE - 1, pg);
+      copy_tile(vbase, v_rowb, v_pageb, vbuf(std::integral_constant<int, FILL>{}), blk + NSTAGE - 1, pg);
     }
     if (wave_live && wave_sees(blk)) {  // otherwise the wave only helps with the copies
       qk_part(kbuf(std::integral_constant<int, ST>{}));
@@ -566,20 +579,26 @@ fwd_tile_kernel(const FwdKernelParams p) {
 
   if (n > 0) {
     // Prologue: tiles of the first NSTAGE - 1 steps.
-    copy_tile(kbase, k_rowb, k_pageb, lds_k0, blk_lo);
-    copy_tile(vbase, v_rowb, v_pageb, lds_v0, blk_lo);
+    {
+      const int pg0 = paged ? page_of(blk_lo) : 0;
+      copy_tile(kbase, k_rowb, k_pageb, lds_k0, blk_lo, pg0);
+      copy_tile(vbase, v_rowb, v_pageb, lds_v0, blk_lo, pg0);
+    }
     if constexpr (NSTAGE > 2) {
       if (n > 1) {
-        copy_tile(kbase, k_rowb, k_pageb, lds_k1, blk_lo + 1);
-        copy_tile(vbase, v_rowb, v_pageb, lds_v1, blk_lo + 1);
+        const int pg1 = paged ? page_of(blk_lo + 1) : 0;
+        copy_tile(kbase, k_rowb, k_pageb, lds_k1, blk_lo + 1, pg1);
+        copy_tile(vbase, v_rowb, v_pageb, lds_v1, blk_lo + 1, pg1);
       }
     }
     if constexpr (NSTAGE > 3) {
       if (n > 2) {
-        copy_tile(kbase, k_rowb, k_pageb, lds_k2, blk_lo + 2);
-        copy_tile(vbase, v_rowb, v_pageb, lds_v2, blk_lo + 2);
+        const int pg2 = paged ? page_of(blk_lo + 2) : 0;
+        copy_tile(kbase, k_rowb, k_pageb, lds_k2, blk_lo + 2, pg2);
+        copy_tile(vbase, v_rowb, v_pageb, lds_v2, blk_lo + 2, pg2);
       }
     }
+    pg_next = (paged && NSTAGE - 1 < n) ? page_of(blk_lo + NSTAGE - 1) : 0;
     if constexpr (NSTAGE > 2) {
       // step 0's tiles must have landed; later prologue copies may still fly
       const int later = min(NSTAGE - 2, n - 1);
@@ -715,7 +734,8 @@ int col_group_for(const FwdKernelParams& p, int heads_grid, int nz, int head_dim
   return (int)std::min<int64_t>(per_xcd, std::max<int64_t>(1, (int64_t(8) << 20) / kv_bytes));
 }
 
-template <class Ty, int D, int BK, int NW, int QG, bool SOFTCAP, int LEAD, int WPE, int NSTAGE = 2>
+template <class Ty, int D, int BK, int NW, int QG, bool SOFTCAP, int LEAD, int WPE, int NSTAGE = 2,
+          bool PAGED = false>
 hipError_t launch_fwd_t(FwdKernelParams p, hipStream_t stream) {
   constexpr int BQ = 32 * NW * QG;
   const int64_t rows = (int64_t)p.seqlen_q * (p.pack_gqa ? p.group : 1);
@@ -729,7 +749,7 @@ hipError_t launch_fwd_t(FwdKernelParams p, hipStream_t stream) {
     p.xcd_chunk = (p.cu_seqlens_q == nullptr && per_xcd > 0) ? per_xcd : 1;
   }
   dim3 grid(p.num_m_tiles, heads_grid, p.batch * p.num_splits);
-  hipLaunchKernelGGL((fwd_tile_kernel<Ty, D, BK, NW, QG, SOFTCAP, LEAD, WPE, NSTAGE>), grid, dim3(NW * 64), 0, stream, p);
+  hipLaunchKernelGGL((fwd_tile_kernel<Ty, D, BK, NW, QG, SOFTCAP, LEAD, WPE, NSTAGE, PAGED>), grid, dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -753,6 +773,14 @@ int dec_variant() {
 
 template <class Ty, bool CAP>
 hipError_t launch_fwd_cap(const FwdKernelParams& p, int head_dim, hipStream_t stream) {
+  if (p.block_table != nullptr) {  // paged cache: one tile shape per head dim
+    switch (head_dim) {
+      case 64: return launch_fwd_t<Ty, 64, 64, 4, 1, CAP, 4, 2, 2, true>(p, stream);
+      case 128: return launch_fwd_t<Ty, 128, 64, 4, 1, CAP, 4, 2, 2, true>(p, stream);
+      case 256: return launch_fwd_t<Ty, 256, 32, 4, 1, CAP, 4, 1, 2, true>(p, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (head_dim) {
     case 64:
       return launch_fwd_t<Ty, 64, 64, 4, 1, CAP, 4, 2>(p, stream);

@@ -285,12 +285,20 @@ def test_full_cfg3_varlen():
                "bf16", "cfg3")
 
 
-def test_full_cfg5a_decode():
-    c = W.WORKLOADS["cfg5a_bf16_decode"]
-    print("[case] full cfg5a decode", flush=True)
+@pytest.mark.parametrize("name", ["cfg5a_bf16_decode", "cfg5a_bf16_decode_paged"])
+def test_full_cfg5a_decode(name):
+    c = W.WORKLOADS[name]
+    print(f"[case] full {name}", flush=True)
     q, kc, vc, lens = W.make_kvcache(c["seed"], c["batch"], 1, c["seqlen_k"], c["heads_q"], c["heads_kv"],
                                      c["head_dim"], c["dtype"], device="cuda")
-    o, lse = _eng().attn_fwd_kvcache(q, kc, vc, cache_seqlens=lens, num_splits=c["num_splits"])
+    table = None
+    if c.get("page"):
+        pk, pv, table = W.page_cache(kc, vc, lens, c["page"], c["seed"])
+        o, lse = _eng().attn_fwd_kvcache(q, pk, pv, cache_seqlens=lens, num_splits=c["num_splits"],
+                                         block_table=table)
+        del pk, pv
+    else:
+        o, lse = _eng().attn_fwd_kvcache(q, kc, vc, cache_seqlens=lens, num_splits=c["num_splits"])
     torch.cuda.synchronize()
     rng = np.random.default_rng(5)
     g = c["heads_q"] // c["heads_kv"]
