@@ -37,7 +37,8 @@ _vp = ctypes.c_void_p
 
 class SoftmaxOpts(ctypes.Structure):
     _fields_ = [("softmax_scale", _f32), ("causal", _i32), ("window_left", _i32),
-                ("window_right", _i32), ("softcap", _f32), ("rescale_threshold", _f32)]
+                ("window_right", _i32), ("softcap", _f32), ("rescale_threshold", _f32),
+                ("alibi_slopes", _vp), ("alibi_batch_stride", _i64)]
 
 
 class FwdArgs(ctypes.Structure):
@@ -118,9 +119,19 @@ def _check(code, what):
         raise RuntimeError(f"{what} failed: {status_string(code)} (status {code})")
 
 
-def _opts(causal, window, softcap, softmax_scale, rescale_threshold):
+def _opts(causal, window, softcap, softmax_scale, rescale_threshold, alibi_slopes=None):
+    """The options struct; alibi_slopes: fp32 GPU tensor [Hq] or [B, Hq] (rows contiguous)."""
+    stride = 0
+    if alibi_slopes is not None:
+        if alibi_slopes.dtype != torch.float32 or alibi_slopes.dim() not in (1, 2) \
+                or alibi_slopes.stride(-1) != 1:
+            raise TypeError("alibi_slopes must be a float32 [heads_q] or [batch, heads_q] tensor "
+                            "with contiguous rows")
+        _need_gpu(alibi_slopes)
+        stride = alibi_slopes.stride(0) if alibi_slopes.dim() == 2 else 0
     return SoftmaxOpts(float(softmax_scale) if softmax_scale is not None else 0.0, int(bool(causal)),
-                       int(window[0]), int(window[1]), float(softcap), float(rescale_threshold))
+                       int(window[0]), int(window[1]), float(softcap), float(rescale_threshold),
+                       _ptr(alibi_slopes), stride)
 
 
 def _ptr(t):
@@ -145,7 +156,8 @@ def _need_gpu(*ts):
 
 
 def attn_fwd(q, k, v, causal=False, window=(-1, -1), softcap=0.0, softmax_scale=None,
-             rescale_threshold=-1.0, out=None, lse=None, return_lse=True, stream=None):
+             rescale_threshold=-1.0, out=None, lse=None, return_lse=True, stream=None,
+             alibi_slopes=None):
     """Dense attention forward: q [B, Sq, Hq, D], k/v [B, Sk, Hkv, D] -> (o, lse [B, Hq, Sq])."""
     _need_gpu(q, k, v)
     b, sq, hq, d = q.shape
@@ -156,7 +168,7 @@ def attn_fwd(q, k, v, causal=False, window=(-1, -1), softcap=0.0, softmax_scale=
         lse = torch.empty((b, hq, sq), dtype=torch.float32, device=q.device)
     a = FwdArgs(_dtype_code(q), b, sq, sk, hq, hkv, d, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
                 *q.stride()[:3], *k.stride()[:3], *v.stride()[:3], *out.stride()[:3],
-                _opts(causal, window, softcap, softmax_scale, rescale_threshold))
+                _opts(causal, window, softcap, softmax_scale, rescale_threshold, alibi_slopes))
     if q.stride(3) != 1 or k.stride(3) != 1 or v.stride(3) != 1 or out.stride(3) != 1:
         raise ValueError("the head dimension must be contiguous")
     if k.dtype != q.dtype or v.dtype != q.dtype or out.dtype != q.dtype:
@@ -171,7 +183,8 @@ def attn_varlen_workspace_bytes(batch, max_seqlen_q, heads_q, heads_kv, head_dim
 
 def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, causal=False,
                     window=(-1, -1), softcap=0.0, softmax_scale=None, rescale_threshold=-1.0,
-                    out=None, lse=None, return_lse=True, workspace=None, stream=None):
+                    out=None, lse=None, return_lse=True, workspace=None, stream=None,
+                    alibi_slopes=None):
     """Packed varlen forward: q [Tq, Hq, D], k/v [Tk, Hkv, D] -> (o, lse [Hq, Tq])."""
     _need_gpu(q, k, v, cu_seqlens_q, cu_seqlens_k)
     tq, hq, d = q.shape
@@ -189,7 +202,8 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
     a = VarlenArgs(_dtype_code(q), batch, tq, tk, int(max_seqlen_q), int(max_seqlen_k), hq, hkv, d,
                    _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q),
                    _ptr(cu_seqlens_k), *q.stride()[:2], *k.stride()[:2], *v.stride()[:2],
-                   *out.stride()[:2], _opts(causal, window, softcap, softmax_scale, rescale_threshold))
+                   *out.stride()[:2], _opts(causal, window, softcap, softmax_scale, rescale_threshold,
+                                              alibi_slopes))
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().attn_fwd_varlen(ctypes.byref(a), _ptr(workspace), ws_bytes, _stream(stream, q.device)),
            "attn_fwd_varlen")
@@ -207,7 +221,7 @@ def attn_kvcache_workspace_bytes(batch, seqlen_q, heads_q, head_dim, num_splits)
 def attn_fwd_kvcache(q, k_cache, v_cache, cache_seqlens=None, num_splits=0, causal=False,
                      window=(-1, -1), softcap=0.0, softmax_scale=None, rescale_threshold=-1.0,
                      out=None, lse=None, return_lse=True, workspace=None, stream=None,
-                     block_table=None):
+                     block_table=None, alibi_slopes=None):
     """Split-KV attention against a cache: q [B, Sq, Hq, D], caches [B, Sk, Hkv, D].
 
     Paged cache: with block_table (int32 [B, max_pages_per_seq]) the caches are
@@ -239,7 +253,7 @@ def attn_fwd_kvcache(q, k_cache, v_cache, cache_seqlens=None, num_splits=0, caus
     a = KvcacheArgs(_dtype_code(q), b, sq, sk, hq, hkv, d, splits, _ptr(q), _ptr(k_cache),
                     _ptr(v_cache), _ptr(cache_seqlens), _ptr(out), _ptr(lse),
                     *q.stride()[:3], *k_cache.stride()[:3], *v_cache.stride()[:3], *out.stride()[:3],
-                    _opts(causal, window, softcap, softmax_scale, rescale_threshold),
+                    _opts(causal, window, softcap, softmax_scale, rescale_threshold, alibi_slopes),
                     _ptr(paging[0]), paging[1], paging[2], paging[3], 0)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().attn_fwd_kvcache(ctypes.byref(a), _ptr(workspace), ws_bytes, _stream(stream, q.device)),

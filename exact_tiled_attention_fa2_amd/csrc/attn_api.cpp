@@ -32,6 +32,10 @@ int check_common(int32_t dtype, int32_t head_dim, int32_t heads_q, int32_t heads
   if (!std::isfinite(o.softmax_scale) || !std::isfinite(o.softcap) || o.softcap < 0.0f ||
       !std::isfinite(o.rescale_threshold))
     return ATTN_E_ARG;
+  if (o.alibi_slopes != nullptr) {
+    if (o.alibi_batch_stride < 0) return ATTN_E_ARG;
+    if ((reinterpret_cast<uintptr_t>(o.alibi_slopes) & 3u) != 0) return ATTN_E_ALIGN;
+  }
   return ATTN_OK;
 }
 
@@ -55,6 +59,11 @@ void resolve_opts(const attn_softmax_opts& o, int head_dim, FwdKernelParams& p) 
     p.scale_ln = scale;
   }
   p.tau = o.rescale_threshold < 0.0f ? 8.0f : o.rescale_threshold;
+  // ALiBi: the kernel works on raw scores (final score = scale_ln * raw), so
+  // it adds the bias divided by scale_ln.
+  p.alibi = o.alibi_slopes;
+  p.alibi_bstride = o.alibi_batch_stride;
+  p.alibi_inv_scale = 1.0f / p.scale_ln;
 }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH; }

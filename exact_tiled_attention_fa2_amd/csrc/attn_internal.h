@@ -40,6 +40,9 @@ struct FwdKernelParams {
   float softcap_pre;    // scale / softcap
   float softcap;        // 0: off
   float tau;            // rescale threshold, log2 units
+  const float* alibi;   // ALiBi slopes (null: off), slope(b, h) = alibi[b * alibi_bstride + h]
+  int64_t alibi_bstride;
+  float alibi_inv_scale;  // 1 / scale_ln: bias in raw-score units
 };
 
 struct CombineParams {

@@ -214,9 +214,10 @@ __device__ __forceinline__ bool tile_work(const FwdKernelParams& p, TileWork& w)
 // query rows (BQ = 32 NW QG rows per workgroup); BK keys per KV step; LEAD
 // LDS operand reads kept in flight ahead of the MFMAs; WPE waves per SIMD;
 // NSTAGE K/V tile buffers (copies run NSTAGE - 1 steps ahead of compute);
-// PAGED: K/V rows come from a paged cache through p.block_table.
+// PAGED: K/V rows come from a paged cache through p.block_table.  ALIBI: the
+// linear distance bias of p.alibi is added to the scores.
 template <class Ty, int D, int BK, int NW, int QG, bool SOFTCAP, int LEAD, int WPE, int NSTAGE = 2,
-          bool PAGED = false>
+          bool PAGED = false, bool ALIBI = false>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(WPE, WPE)))
 fwd_tile_kernel(const FwdKernelParams p) {
   constexpr int NT = NW * 64;           // threads per workgroup
@@ -297,6 +298,11 @@ fwd_tile_kernel(const FwdKernelParams p) {
     kmin[g] = (wl >= 0) ? row[g] + off - wl : -0x40000000;
     kmax[g] = min(sk - 1, (wr >= 0) ? row[g] + off + wr : 0x3fffffff);
   }
+  // ALiBi slope of this lane's query head, in raw-score units.
+  float slope[QG];
+#pragma unroll
+  for (int g = 0; g < QG; ++g)
+    slope[g] = ALIBI ? p.alibi[(int64_t)b * p.alibi_bstride + hq[g]] * p.alibi_inv_scale : 0.0f;
 
   // A wave whose rows all lie past the end (decode packs only G x Sq rows)
   // skips the compute and only takes part in the tile copies; so does a wave
@@ -448,6 +454,17 @@ fwd_tile_kernel(const FwdKernelParams p) {
 #pragma unroll
           for (int r2 = 0; r2 < 16; ++r2)
             sc[g][kt][r2] = transform_score<SOFTCAP>(sc[g][kt][r2], p.softcap_pre, p.softcap);
+      }
+      if constexpr (ALIBI) {
+        // -slope |i + off - key| with key = j0 + 4 hl + c, c fixed per register
+        const float d0 = (float)(row[g] + off - j0 - 4 * hl);
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+          for (int r2 = 0; r2 < 16; ++r2) {
+            const float c = (float)(32 * kt + 8 * (r2 >> 2) + (r2 & 3));
+            sc[g][kt][r2] = fmaf(-slope[g], fabsf(d0 - c), sc[g][kt][r2]);
+          }
       }
       const int full_lo = (wl >= 0) ? grow_hi[g] + off - wl : -0x40000000;
       const int full_hi = min(sk - 1, (wr >= 0) ? grow_lo[g] + off + wr : 0x3fffffff);
@@ -735,7 +752,7 @@ int col_group_for(const FwdKernelParams& p, int heads_grid, int nz, int head_dim
 }
 
 template <class Ty, int D, int BK, int NW, int QG, bool SOFTCAP, int LEAD, int WPE, int NSTAGE = 2,
-          bool PAGED = false>
+          bool PAGED = false, bool ALIBI = false>
 hipError_t launch_fwd_t(FwdKernelParams p, hipStream_t stream) {
   constexpr int BQ = 32 * NW * QG;
   const int64_t rows = (int64_t)p.seqlen_q * (p.pack_gqa ? p.group : 1);
@@ -749,7 +766,7 @@ hipError_t launch_fwd_t(FwdKernelParams p, hipStream_t stream) {
     p.xcd_chunk = (p.cu_seqlens_q == nullptr && per_xcd > 0) ? per_xcd : 1;
   }
   dim3 grid(p.num_m_tiles, heads_grid, p.batch * p.num_splits);
-  hipLaunchKernelGGL((fwd_tile_kernel<Ty, D, BK, NW, QG, SOFTCAP, LEAD, WPE, NSTAGE, PAGED>), grid, dim3(NW * 64), 0, stream, p);
+  hipLaunchKernelGGL((fwd_tile_kernel<Ty, D, BK, NW, QG, SOFTCAP, LEAD, WPE, NSTAGE, PAGED, ALIBI>), grid, dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -771,46 +788,54 @@ int dec_variant() {
   return v;
 }
 
-template <class Ty, bool CAP>
-hipError_t launch_fwd_cap(const FwdKernelParams& p, int head_dim, hipStream_t stream) {
+template <class Ty, bool CAP, bool AL>
+hipError_t launch_fwd_shape(const FwdKernelParams& p, int head_dim, hipStream_t stream) {
   if (p.block_table != nullptr) {  // paged cache: one tile shape per head dim
     switch (head_dim) {
-      case 64: return launch_fwd_t<Ty, 64, 64, 4, 1, CAP, 4, 2, 2, true>(p, stream);
-      case 128: return launch_fwd_t<Ty, 128, 64, 4, 1, CAP, 4, 2, 2, true>(p, stream);
-      case 256: return launch_fwd_t<Ty, 256, 32, 4, 1, CAP, 4, 1, 2, true>(p, stream);
+      case 64: return launch_fwd_t<Ty, 64, 64, 4, 1, CAP, 4, 2, 2, true, AL>(p, stream);
+      case 128: return launch_fwd_t<Ty, 128, 64, 4, 1, CAP, 4, 2, 2, true, AL>(p, stream);
+      case 256: return launch_fwd_t<Ty, 256, 32, 4, 1, CAP, 4, 1, 2, true, AL>(p, stream);
       default: return hipErrorInvalidValue;
     }
   }
   switch (head_dim) {
     case 64:
-      return launch_fwd_t<Ty, 64, 64, 4, 1, CAP, 4, 2>(p, stream);
+      return launch_fwd_t<Ty, 64, 64, 4, 1, CAP, 4, 2, 2, false, AL>(p, stream);
     case 128: {
       const int64_t packed = (int64_t)p.seqlen_q * (p.pack_gqa ? p.group : 1);
       if (packed <= 64) {
         // Decode-shaped launches (few live rows; the KV stream dominates).
-        switch (dec_variant()) {
-          case 1: return launch_fwd_t<Ty, 128, 32, 4, 1, CAP, 4, 2, 4>(p, stream);
-          default: return launch_fwd_t<Ty, 128, 64, 4, 1, CAP, 4, 2>(p, stream);
+        if constexpr (!AL) {
+          if (dec_variant() == 1) return launch_fwd_t<Ty, 128, 32, 4, 1, CAP, 4, 2, 4>(p, stream);
+        }
+        return launch_fwd_t<Ty, 128, 64, 4, 1, CAP, 4, 2, 2, false, AL>(p, stream);
+      }
+      if constexpr (!AL) {  // tile variants for tuning sweeps
+        switch (fwd_variant()) {
+          case 1: return launch_fwd_t<Ty, 128, 64, 4, 1, CAP, 4, 2>(p, stream);
+          case 2: return launch_fwd_t<Ty, 128, 64, 8, 1, CAP, 6, 2>(p, stream);
+          case 3: return launch_fwd_t<Ty, 128, 32, 4, 1, CAP, 4, 2, 4>(p, stream);
+          default: break;
         }
       }
-      switch (fwd_variant()) {
-        case 1: return launch_fwd_t<Ty, 128, 64, 4, 1, CAP, 4, 2>(p, stream);
-        case 2: return launch_fwd_t<Ty, 128, 64, 8, 1, CAP, 6, 2>(p, stream);
-        case 3: return launch_fwd_t<Ty, 128, 32, 4, 1, CAP, 4, 2, 4>(p, stream);
-        default:
-          // 256 query rows per workgroup (8 waves, one workgroup per CU) halve
-          // the K/V re-reads from L2 per FLOP and win on dense and varlen
-          // launches; the VALU-heavy softcap path runs faster with 128 rows
-          // and two workgroups per CU.
-          if (!CAP) return launch_fwd_t<Ty, 128, 64, 8, 1, CAP, 6, 2>(p, stream);
-          return launch_fwd_t<Ty, 128, 64, 4, 1, CAP, 4, 2>(p, stream);
-      }
+      // 256 query rows per workgroup (8 waves, one workgroup per CU) halve
+      // the K/V re-reads from L2 per FLOP and win on dense and varlen
+      // launches; the VALU-heavy softcap path runs faster with 128 rows
+      // and two workgroups per CU.
+      if (!CAP) return launch_fwd_t<Ty, 128, 64, 8, 1, CAP, 6, 2, 2, false, AL>(p, stream);
+      return launch_fwd_t<Ty, 128, 64, 4, 1, CAP, 4, 2, 2, false, AL>(p, stream);
     }
     case 256:
-      return launch_fwd_t<Ty, 256, 32, 4, 1, CAP, 4, 1>(p, stream);
+      return launch_fwd_t<Ty, 256, 32, 4, 1, CAP, 4, 1, 2, false, AL>(p, stream);
     default:
       return hipErrorInvalidValue;
   }
+}
+
+template <class Ty, bool CAP>
+hipError_t launch_fwd_cap(const FwdKernelParams& p, int head_dim, hipStream_t stream) {
+  return p.alibi != nullptr ? launch_fwd_shape<Ty, CAP, true>(p, head_dim, stream)
+                            : launch_fwd_shape<Ty, CAP, false>(p, head_dim, stream);
 }
 
 template <class Ty>

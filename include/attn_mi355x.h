@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define ATTN_VERSION 110
+#define ATTN_VERSION 120
 
 enum attn_status {
   ATTN_OK = 0,
@@ -77,7 +77,16 @@ enum attn_status {
 
 enum attn_dtype { ATTN_DTYPE_F16 = 0, ATTN_DTYPE_BF16 = 1 };
 
-/* Fields shared by the three entry points: features of the softmax. */
+/*
+ * Fields shared by the three entry points: features of the softmax.
+ * ALiBi (alibi_slopes among the public API features, "v1.7 / flash_attn
+ * 2.9.2.post1" section 2 and the API-path table of section 4): when
+ * alibi_slopes is not NULL, -slope(b, h) * |i + (Sk - Sq) - j| is added to
+ * the final score of query row i and key j (after scale and softcap, before
+ * masks and the softmax), with slope(b, h) = alibi_slopes[b *
+ * alibi_batch_stride + h], fp32 in device memory, 4-byte aligned
+ * (alibi_batch_stride 0: one slope per query head for every batch entry).
+ */
 typedef struct attn_softmax_opts {
   float softmax_scale;     /* <= 0: 1/sqrt(head_dim) */
   int32_t causal;          /* 0 or 1 */
@@ -85,6 +94,8 @@ typedef struct attn_softmax_opts {
   int32_t window_right;    /* -1 unbounded, >= 0 bound */
   float softcap;           /* 0: off, > 0: tanh cap */
   float rescale_threshold; /* < 0: default 8.0 */
+  const float* alibi_slopes;  /* NULL: no ALiBi bias */
+  int64_t alibi_batch_stride; /* elements between batch entries of alibi_slopes (>= 0) */
 } attn_softmax_opts;
 
 /*

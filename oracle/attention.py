@@ -31,6 +31,10 @@ Readings where the pages are silent (each one is listed in the design doc):
 * GQA: query head h reads KV head h // (Hq / Hkv) (contiguous groups).
 * LSE is in natural-log units with layout [B, Hq, Sq] (v1.7 section 4.6
   gives the shape; its printed range fits natural log).
+* ALiBi (named among the public API features, v1.7 section 2, and in its
+  API-path table, section 4; no formula is printed): the plainest reading,
+  -slope_h * |i + off - j| added to t_ij after the softcap and before the
+  mask, with a slope per query head (optionally per batch entry).
 """
 
 import numpy as np
@@ -39,6 +43,7 @@ __all__ = [
     "kv_head_of",
     "allowed_mask",
     "transformed_scores",
+    "alibi_bias",
     "attention_ref",
     "attention_varlen_ref",
     "attention_kvcache_ref",
@@ -79,8 +84,16 @@ def transformed_scores(q_rows, k_mat, scale, softcap=0.0):
     return s
 
 
+def alibi_bias(seqlen_q, seqlen_k, rows, slope):
+    """-slope * |i + off - j| for query rows ``rows`` and every key j (off = Sk - Sq)."""
+    off = seqlen_k - seqlen_q
+    i = np.asarray(rows, dtype=np.float64)[:, None]
+    j = np.arange(seqlen_k, dtype=np.float64)[None, :]
+    return -float(slope) * np.abs(i + off - j)
+
+
 def _one_head(q_h, k_g, v_g, rows, scale, causal, window_left, window_right, softcap,
-              chunk, want_probs):
+              chunk, want_probs, alibi_slope=None):
     """Exact attention of query rows ``rows`` of one head against one KV head.
 
     q_h [Sq, D], k_g/v_g [Sk, D] in fp64.  Returns O [R, D], LSE [R] and,
@@ -97,6 +110,8 @@ def _one_head(q_h, k_g, v_g, rows, scale, causal, window_left, window_right, sof
     for c0 in range(0, rows.shape[0], chunk):
         r = rows[c0:c0 + chunk]
         t = transformed_scores(q_h[r], k_g, scale, softcap)
+        if alibi_slope is not None:
+            t = t + alibi_bias(seqlen_q, seqlen_k, r, alibi_slope)
         ok = allowed_mask(seqlen_q, seqlen_k, r, causal, window_left, window_right)
         t = np.where(ok, t, -np.inf)
         has_key = ok.any(axis=1)
@@ -112,14 +127,22 @@ def _one_head(q_h, k_g, v_g, rows, scale, causal, window_left, window_right, sof
     return out, lse, probs
 
 
+def _slope(alibi_slopes, b, h):
+    if alibi_slopes is None:
+        return None
+    a = np.asarray(alibi_slopes, dtype=np.float64)
+    return a[h] if a.ndim == 1 else a[b, h]
+
+
 def attention_ref(q, k, v, scale=None, causal=False, window=(-1, -1), softcap=0.0,
-                  rows=None, return_probs=False, chunk=512):
+                  rows=None, return_probs=False, chunk=512, alibi_slopes=None):
     """Exact attention forward, plain definition, fp64.
 
     q [B, Sq, Hq, D]; k, v [B, Sk, Hkv, D] (any real dtype, upcast to fp64).
     ``scale`` defaults to 1/sqrt(D).  ``window`` = (left, right), -1 for
     unbounded.  ``rows`` optionally restricts the computation to those query
     rows (outputs then hold only those rows, in that order).
+    ``alibi_slopes`` [Hq] or [B, Hq] adds the ALiBi distance bias.
 
     Returns (O [B, R, Hq, D], LSE [B, Hq, R]) and, with ``return_probs``, the
     probability matrix P [B, Hq, R, Sk].  R = Sq unless ``rows`` is given.
@@ -140,7 +163,7 @@ def attention_ref(q, k, v, scale=None, causal=False, window=(-1, -1), softcap=0.
             g = kv_head_of(h, heads_q, heads_kv)
             o_bh, lse_bh, p_bh = _one_head(q[b, :, h, :], k[b, :, g, :], v[b, :, g, :], rows,
                                            scale, causal, window[0], window[1], softcap,
-                                           chunk, return_probs)
+                                           chunk, return_probs, _slope(alibi_slopes, b, h))
             out[b, :, h, :] = o_bh
             lse[b, h, :] = lse_bh
             if return_probs:
@@ -148,6 +171,16 @@ def attention_ref(q, k, v, scale=None, causal=False, window=(-1, -1), softcap=0.
     if return_probs:
         return out, lse, probs
     return out, lse
+
+
+def _batch_entry(kw, b):
+    """Keyword arguments for the one-sequence call of batch entry b (per-batch ALiBi slopes)."""
+    a = kw.get("alibi_slopes")
+    if a is None or np.asarray(a).ndim == 1:
+        return kw
+    kw = dict(kw)
+    kw["alibi_slopes"] = np.asarray(a)[b:b + 1]
+    return kw
 
 
 def attention_varlen_ref(q, k, v, cu_seqlens_q, cu_seqlens_k, **kw):
@@ -168,7 +201,8 @@ def attention_varlen_ref(q, k, v, cu_seqlens_q, cu_seqlens_k, **kw):
         q0, q1, k0, k1 = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
         if q1 == q0:
             continue
-        o_b, lse_b = attention_ref(q[None, q0:q1], k[None, k0:k1], v[None, k0:k1], **kw)
+        o_b, lse_b = attention_ref(q[None, q0:q1], k[None, k0:k1], v[None, k0:k1],
+                                   **_batch_entry(kw, b))
         out[q0:q1] = o_b[0]
         lse[:, q0:q1] = lse_b[0]
     return out, lse
@@ -214,7 +248,7 @@ def attention_kvcache_ref(q, k_cache, v_cache, cache_seqlens=None, block_table=N
         else:
             kb = np.asarray(gather_pages(k_cache, block_table[b], n), dtype=np.float64)[None]
             vb = np.asarray(gather_pages(v_cache, block_table[b], n), dtype=np.float64)[None]
-        o_b, lse_b = attention_ref(q[b:b + 1], kb, vb, **kw)
+        o_b, lse_b = attention_ref(q[b:b + 1], kb, vb, **_batch_entry(kw, b))
         out[b] = o_b[0]
         lse[b] = lse_b[0]
     return out, lse

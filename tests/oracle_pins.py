@@ -309,6 +309,52 @@ def pin_paged_cache_is_contiguous():
         assert np.array_equal(g, k[bi, :lens[bi]])
 
 
+def pin_alibi_closed_forms():
+    """ALiBi with Q = 0: every raw score is 0, so t_ij = -slope |i + off - j| and the weights
+    are geometric.  LSE_i = ln sum_d exp(-slope d) over the visible distances, O_i the matching
+    weighted mean of V (weights written out independently of the oracle)."""
+    rng = _rng(13)
+    slope = 0.37
+    for (sq, sk, causal) in [(9, 9, True), (9, 9, False), (3, 11, True), (1, 7, False)]:
+        q = np.zeros((1, sq, 2, 8))
+        k = rng.standard_normal((1, sk, 1, 8))
+        v = rng.standard_normal((1, sk, 1, 8))
+        out, lse = oracle.attention_ref(q, k, v, causal=causal, alibi_slopes=[slope, 2 * slope])
+        off = sk - sq
+        for h, sl in ((0, slope), (1, 2 * slope)):
+            for i in range(sq):
+                js = [j for j in range(sk) if (not causal or j <= i + off)]
+                w = [math.exp(-sl * abs(i + off - j)) for j in js]
+                tot = math.fsum(w)
+                assert abs(lse[0, h, i] - math.log(tot)) < 1e-12
+                o_ref = sum(wj * v[0, j, 0] for wj, j in zip(w, js)) / tot
+                assert np.allclose(out[0, i, h], o_ref, atol=1e-12)
+    # per-batch slopes [B, Hq] equal the [Hq] form when the rows agree
+    q = rng.standard_normal((2, 5, 2, 8))
+    k = rng.standard_normal((2, 5, 2, 8))
+    v = rng.standard_normal((2, 5, 2, 8))
+    o1, l1 = oracle.attention_ref(q, k, v, causal=True, alibi_slopes=[0.5, 0.25])
+    o2, l2 = oracle.attention_ref(q, k, v, causal=True, alibi_slopes=[[0.5, 0.25], [0.5, 0.25]])
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    o3, l3 = oracle.attention_ref(q, k, v, causal=True, alibi_slopes=[[0.5, 0.25], [0.0, 0.0]])
+    o4, l4 = oracle.attention_ref(q, k, v, causal=True)
+    assert np.array_equal(o3[1], o4[1]) and np.array_equal(l3[1], l4[1])
+
+
+def pin_alibi_after_softcap():
+    """One query, two keys, softcap 2: t_j = cap tanh(scale s_j / cap) - slope d_j, bias after
+    the cap (a cap applied to the biased score gives another LSE)."""
+    d = 4
+    q = np.zeros((1, 1, 1, d)); q[0, 0, 0, 0] = 3.0
+    k = np.zeros((1, 2, 1, d)); k[0, 0, 0, 0] = 1.5; k[0, 1, 0, 0] = -0.5
+    v = np.zeros((1, 2, 1, d)); v[0, 0, 0, 1] = 1.0; v[0, 1, 0, 2] = 1.0
+    scale, cap, slope = 0.5, 2.0, 0.8
+    _, lse = oracle.attention_ref(q, k, v, scale=scale, softcap=cap, alibi_slopes=[slope])
+    t0 = cap * math.tanh(scale * 4.5 / cap) - slope * 1.0     # key 0: distance off - 0 = 1
+    t1 = cap * math.tanh(scale * -1.5 / cap) - slope * 0.0    # key 1: distance 0
+    assert abs(lse[0, 0, 0] - math.log(math.exp(t0) + math.exp(t1))) < 1e-13
+
+
 # ---------------------------------------------------------------- library routines
 
 def _sdpa_ref(q, k, v, scale, mask_bool):
@@ -494,6 +540,8 @@ ALL_PINS = [
     pin_page_lse_units,
     pin_decode_is_last_prefill_row,
     pin_paged_cache_is_contiguous,
+    pin_alibi_closed_forms,
+    pin_alibi_after_softcap,
     pin_torch_sdpa,
     pin_varlen_block_diagonal,
     pin_gqa_is_repeated_mha,

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_function():
 
 def test_version_and_status_strings():
     h = _lib()
-    assert h.attn_version() == 110
+    assert h.attn_version() == 120
     for code in range(-9, 1):
         assert binding.status_string(code)
     assert binding.status_string(-1234) == "unknown status"
@@ -212,4 +212,15 @@ def test_kvcache_paged_validation():
     ka.num_pages = 20
     ka.block_table = 18                          # not 4-byte aligned
     assert call() == binding.ATTN_E_ALIGN
+
+
+def test_alibi_validation():
+    """ALiBi slopes are checked on the host (fake device pointers, no launch)."""
+    h = _lib()
+    a = _fwd_args()
+    a.opts.alibi_slopes = 18                     # not 4-byte aligned
+    assert h.attn_fwd(ctypes.byref(a), None) == binding.ATTN_E_ALIGN
+    a.opts.alibi_slopes = 16
+    a.opts.alibi_batch_stride = -1
+    assert h.attn_fwd(ctypes.byref(a), None) == binding.ATTN_E_ARG
 

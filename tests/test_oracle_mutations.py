@@ -119,6 +119,21 @@ def _gather_page_order(pool, table_row, n):
     return np.concatenate(rows, axis=0)[:n]
 
 
+def _alibi_sign(seqlen_q, seqlen_k, rows, slope):
+    return -_orig_alibi(seqlen_q, seqlen_k, rows, slope)         # bias added with the wrong sign
+
+
+def _alibi_no_offset(seqlen_q, seqlen_k, rows, slope):
+    return _orig_alibi(seqlen_k, seqlen_k, rows, slope)          # distance |i - j|, top-left
+
+
+def _alibi_scaled(seqlen_q, seqlen_k, rows, slope):
+    return _orig_alibi(seqlen_q, seqlen_k, rows, slope) * 0.5    # bias in pre-scale units
+
+
+_orig_alibi = oatt.alibi_bias
+
+
 MUTATIONS = {
     "causal_strict_lt": (oatt, "allowed_mask", _mask_causal_strict),
     "top_left_alignment": (oatt, "allowed_mask", _mask_top_left),
@@ -134,6 +149,9 @@ MUTATIONS = {
     "tiled_wrong_exp_base": (otiled, "_tiled_one_head", _tiled_natural_exp),
     "paged_row_off_by_one": (oatt, "gather_pages", _gather_row_shift),
     "paged_table_ignored": (oatt, "gather_pages", _gather_page_order),
+    "alibi_sign": (oatt, "alibi_bias", _alibi_sign),
+    "alibi_no_offset": (oatt, "alibi_bias", _alibi_no_offset),
+    "alibi_scaled": (oatt, "alibi_bias", _alibi_scaled),
 }
 
 

@@ -35,8 +35,12 @@ def _dense_case(seed, b, sq, sk, hq, hkv, d, dtype, **kw):
     torch.cuda.synchronize()
     ro, rl = oracle.attention_ref(np64(q), np64(k), np64(v), scale=kw.get("softmax_scale"),
                                   causal=kw.get("causal", False), window=kw.get("window", (-1, -1)),
-                                  softcap=kw.get("softcap", 0.0))
+                                  softcap=kw.get("softcap", 0.0), alibi_slopes=_np_or_none(kw.get("alibi_slopes")))
     return o, lse, ro, rl
+
+
+def _np_or_none(t):
+    return None if t is None else t.detach().cpu().numpy().astype(np.float64)
 
 
 # ------------------------------------------------------------------ small full-output parity
@@ -138,6 +142,59 @@ def test_varlen_small_full(case):
     cu_np = cu.cpu().numpy()
     ro, rl = oracle.attention_varlen_ref(np64(q), np64(k), np64(v), cu_np, cu_np, **kw)
     gate_check(np64(o), ro, np64(lse), rl, dtype, f"varlen {seed}")
+
+
+def _alibi_slopes(batch, heads, per_batch, device="cuda"):
+    """Geometric ALiBi slopes 2^(-8 (h + 1) / H); per batch entry scaled by (b + 1) / batch."""
+    base = torch.tensor([2.0 ** (-8.0 * (h + 1) / heads) for h in range(heads)], dtype=torch.float32)
+    if per_batch:
+        base = torch.stack([base * (b + 1) / batch for b in range(batch)])
+    return base.to(device)
+
+
+ALIBI_DENSE = [
+    (71, 2, 300, 300, 8, 2, 128, "bf16", dict(causal=True), False),
+    (72, 1, 200, 333, 4, 4, 64, "fp16", dict(causal=False), False),
+    (73, 2, 257, 257, 8, 2, 128, "bf16", dict(causal=True, softcap=30.0), True),
+    (74, 1, 130, 130, 4, 1, 256, "fp16", dict(causal=True, window=(64, 0)), True),
+]
+
+
+@pytest.mark.parametrize("case", ALIBI_DENSE, ids=[f"s{c[0]}" for c in ALIBI_DENSE])
+def test_alibi_dense(case):
+    seed, b, sq, sk, hq, hkv, d, dtype, kw, per_batch = case
+    print(f"[case] alibi dense seed={seed} b={b} sq={sq} sk={sk} hq={hq} hkv={hkv} d={d} {dtype} {kw} "
+          f"per_batch={per_batch}", flush=True)
+    sl = _alibi_slopes(b, hq, per_batch)
+    o, lse, ro, rl = _dense_case(seed, b, sq, sk, hq, hkv, d, dtype, alibi_slopes=sl, **kw)
+    gate_check(np64(o), ro, np64(lse), rl, dtype, f"alibi {seed}")
+
+
+def test_alibi_varlen_and_kvcache():
+    """ALiBi through the varlen and kv-cache entry points (contiguous and paged)."""
+    print("[case] alibi varlen + kvcache", flush=True)
+    eng = _eng()
+    lens = [100, 1, 300, 77]
+    q, k, v, cu, lens_t = W.make_varlen(75, len(lens), 1, 1, 8, 2, 128, "bf16", device="cuda", lengths=lens)
+    sl = _alibi_slopes(len(lens), 8, True)
+    o, lse = eng.attn_fwd_varlen(q, k, v, cu, cu, max(lens), max(lens), causal=True, alibi_slopes=sl)
+    torch.cuda.synchronize()
+    cu_np = cu.cpu().numpy()
+    ro, rl = oracle.attention_varlen_ref(np64(q), np64(k), np64(v), cu_np, cu_np, causal=True,
+                                         alibi_slopes=sl.cpu().numpy())
+    gate_check(np64(o), ro, np64(lse), rl, "bf16", "alibi varlen")
+    q, kc, vc, cl = W.make_kvcache(76, 3, 2, 900, 8, 2, 128, "bf16", device="cuda",
+                                   random_lengths=True, nan_tail=True)
+    sl = _alibi_slopes(3, 8, False)
+    ro, rl = oracle.attention_kvcache_ref(np64(q), np64(kc), np64(vc), cl.cpu().numpy(), causal=True,
+                                          alibi_slopes=sl.cpu().numpy())
+    o, lse = eng.attn_fwd_kvcache(q, kc, vc, cache_seqlens=cl, num_splits=3, causal=True, alibi_slopes=sl)
+    pk, pv, table = W.page_cache(kc, vc, cl, 64, 76)
+    op, lp = eng.attn_fwd_kvcache(q, pk, pv, cache_seqlens=cl, num_splits=3, causal=True, alibi_slopes=sl,
+                                  block_table=table)
+    torch.cuda.synchronize()
+    gate_check(np64(o), ro, np64(lse), rl, "bf16", "alibi kvcache")
+    assert torch.equal(o, op) and torch.equal(lse, lp)
 
 
 DECODE_SMALL = [
