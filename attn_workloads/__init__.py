@@ -31,6 +31,7 @@ __all__ = [
     "make_dense",
     "make_varlen",
     "make_kvcache",
+    "alibi_slopes",
     "k_ramp_factor",
 ]
 
@@ -61,6 +62,12 @@ WORKLOADS = {
     "cfg5a_bf16_decode_paged": dict(kind="kvcache", seed=1005, batch=32, seqlen_q=1, seqlen_k=32768,
                                     heads_q=32, heads_kv=8, head_dim=128, dtype="bf16", causal=False,
                                     window=(-1, -1), softcap=0.0, num_splits=16, page=256),
+    "cfg2a_bf16_causal_2k_alibi": dict(kind="dense", seed=1002, batch=4, seqlen_q=2048, seqlen_k=2048,
+                                       heads_q=16, heads_kv=16, head_dim=128, dtype="bf16", causal=True,
+                                       window=(-1, -1), softcap=0.0, alibi=True),
+    "cfg5a_bf16_decode_alibi": dict(kind="kvcache", seed=1005, batch=32, seqlen_q=1, seqlen_k=32768,
+                                    heads_q=32, heads_kv=8, head_dim=128, dtype="bf16", causal=False,
+                                    window=(-1, -1), softcap=0.0, num_splits=16, alibi=True),
     "cfg5b_fp16_d256_causal": dict(kind="dense", seed=1006, batch=4, seqlen_q=4096,
                                    seqlen_k=4096, heads_q=32, heads_kv=8, head_dim=256,
                                    dtype="fp16", causal=True, window=(-1, -1), softcap=0.0),
@@ -146,6 +153,18 @@ def make_kvcache(seed, batch, seqlen_q, seqlen_k, heads_q, heads_kv, head_dim, d
             kc[b, n:] = float("nan")
             vc[b, n:] = float("nan")
     return q, kc, vc, lens.to(torch.int32).to(device)
+
+
+def alibi_slopes(heads, batch=None, device="cpu"):
+    """fp32 ALiBi slopes: the geometric sequence 2^(-8 (h + 1) / heads) over the query heads.
+
+    With ``batch`` the result is [batch, heads], entry b scaled by (b + 1) / batch so that
+    each batch row differs; otherwise [heads].  Input construction only.
+    """
+    base = torch.tensor([2.0 ** (-8.0 * (h + 1) / heads) for h in range(heads)], dtype=torch.float32)
+    if batch is not None:
+        base = torch.stack([base * (b + 1) / batch for b in range(batch)])
+    return base.to(device)
 
 
 def page_cache(kc, vc, lens, page, seed, spare_pages=3):

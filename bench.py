@@ -104,6 +104,7 @@ def cpu_baseline(cfg, budget_s=20.0):
                            cfg["heads_kv"], cfg["head_dim"], cfg["dtype"], device="cpu",
                            k_ramp=cfg.get("k_ramp", False))
     g = cfg["heads_q"] // cfg["heads_kv"]
+    sl = W.alibi_slopes(cfg["heads_q"]).to(torch.float64).numpy() if cfg.get("alibi") else None
     pairs = visible_pairs(cfg["seqlen_q"], cfg["seqlen_k"], cfg["causal"], cfg["window"])
     flops_head = 4.0 * cfg["head_dim"] * pairs
     total = cfg["batch"] * cfg["heads_q"]
@@ -114,7 +115,7 @@ def cpu_baseline(cfg, budget_s=20.0):
                              k[b:b + 1, :, h // g:h // g + 1].to(torch.float64).numpy(),
                              v[b:b + 1, :, h // g:h // g + 1].to(torch.float64).numpy(),
                              scale=cfg.get("scale"), causal=cfg["causal"], window=cfg["window"],
-                             softcap=cfg["softcap"])
+                             softcap=cfg["softcap"], alibi_slopes=None if sl is None else sl[h:h + 1])
         done += 1
         if time.perf_counter() - t0 > budget_s:
             break
@@ -139,10 +140,11 @@ def bench_dense(name, steps, warmup, torch, eng, W):
                            device="cuda")
     o = torch.empty_like(q)
     lse = torch.empty((c["batch"], c["heads_q"], c["seqlen_q"]), dtype=torch.float32, device="cuda")
+    sl = W.alibi_slopes(c["heads_q"], device="cuda") if c.get("alibi") else None
 
     def step():
         eng.attn_fwd(q, k, v, causal=c["causal"], window=c["window"], softcap=c["softcap"],
-                     softmax_scale=c.get("scale"), out=o, lse=lse)
+                     softmax_scale=c.get("scale"), out=o, lse=lse, alibi_slopes=sl)
 
     ms = time_region(step, steps, warmup, torch)
     pairs = visible_pairs(c["seqlen_q"], c["seqlen_k"], c["causal"], c["window"])
@@ -151,7 +153,7 @@ def bench_dense(name, steps, warmup, torch, eng, W):
     config = {"workload": name, "batch": c["batch"], "seqlen_q": c["seqlen_q"], "seqlen_k": c["seqlen_k"],
               "heads_q": c["heads_q"], "heads_kv": c["heads_kv"], "head_dim": c["head_dim"],
               "causal": c["causal"], "window": list(c["window"]), "softcap": c["softcap"],
-              "flop_count": "4*D per visible (query, key) pair",
+              "alibi": bool(c.get("alibi")), "flop_count": "4*D per visible (query, key) pair",
               "flops_per_step": flops, "literal_formula_flops_per_step": literal,
               "literal_formula_tflops": round(literal / (ms * 1e-3) / 1e12, 3)}
     return ms, flops, config, c
@@ -194,10 +196,11 @@ def bench_kvcache(name, steps, warmup, torch, eng, W):
     ws = torch.empty(eng.attn_kvcache_workspace_bytes(c["batch"], c["seqlen_q"], c["heads_q"],
                                                       c["head_dim"], c["num_splits"]),
                      dtype=torch.uint8, device="cuda")
+    sl = W.alibi_slopes(c["heads_q"], device="cuda") if c.get("alibi") else None
 
     def step():
         eng.attn_fwd_kvcache(q, kc, vc, cache_seqlens=lens, num_splits=c["num_splits"], out=o, lse=lse,
-                             workspace=ws, block_table=table)
+                             workspace=ws, block_table=table, alibi_slopes=sl)
 
     ms = time_region(step, steps, warmup, torch)
     el = 2  # 16-bit
@@ -207,7 +210,7 @@ def bench_kvcache(name, steps, warmup, torch, eng, W):
     return {"workload": name, "ms_per_step": round(ms, 4), "value": round(gbs, 1), "unit": "GB/s",
             "bytes_per_step": bytes_alg, "num_splits": c["num_splits"],
             "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "peak": PEAK_HBM_GBS,
-            "page_block_size": c.get("page"),
+            "page_block_size": c.get("page"), "alibi": bool(c.get("alibi")),
             "note": "whole step (split kernel + combine); algorithmic bytes = K+V cache + Q + O + LSE"}
 
 

@@ -455,16 +455,31 @@ fwd_tile_kernel(const FwdKernelParams p) {
           for (int r2 = 0; r2 < 16; ++r2)
             sc[g][kt][r2] = transform_score<SOFTCAP>(sc[g][kt][r2], p.softcap_pre, p.softcap);
       }
+      // ALiBi bias -slope |d| with d = i + off - key = d0 - c, where key =
+      // j0 + 4 hl + c and c is fixed per register.  When the whole step lies
+      // on one side of every row's diagonal, |d| is linear in c: the registers
+      // take only +-slope c, and the lane constant -+slope d0 (kb) joins the
+      // block max and the exponent's offset instead of every score.
+      float kb = 0.0f;
       if constexpr (ALIBI) {
-        // -slope |i + off - key| with key = j0 + 4 hl + c, c fixed per register
         const float d0 = (float)(row[g] + off - j0 - 4 * hl);
+        if (grow_lo[g] + off >= j0 + BK - 1 || grow_hi[g] + off <= j0) {
+          const float sl = (grow_lo[g] + off >= j0 + BK - 1) ? slope[g] : -slope[g];
+          kb = -sl * d0;
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
+          for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-          for (int r2 = 0; r2 < 16; ++r2) {
-            const float c = (float)(32 * kt + 8 * (r2 >> 2) + (r2 & 3));
-            sc[g][kt][r2] = fmaf(-slope[g], fabsf(d0 - c), sc[g][kt][r2]);
-          }
+            for (int r2 = 0; r2 < 16; ++r2)
+              sc[g][kt][r2] = fmaf(sl, (float)(32 * kt + 8 * (r2 >> 2) + (r2 & 3)), sc[g][kt][r2]);
+        } else {
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int r2 = 0; r2 < 16; ++r2) {
+              const float c = (float)(32 * kt + 8 * (r2 >> 2) + (r2 & 3));
+              sc[g][kt][r2] = fmaf(-slope[g], fabsf(d0 - c), sc[g][kt][r2]);
+            }
+        }
       }
       const int full_lo = (wl >= 0) ? grow_hi[g] + off - wl : -0x40000000;
       const int full_hi = min(sk - 1, (wr >= 0) ? grow_lo[g] + off + wr : 0x3fffffff);
@@ -484,6 +499,7 @@ fwd_tile_kernel(const FwdKernelParams p) {
       for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
         for (int r2 = 0; r2 < 16; ++r2) mx = fmaxf(mx, sc[g][kt][r2]);
+      if constexpr (ALIBI) mx += kb;
       // ---- RescaleThreshold with max lagging.  While no row's block max
       // rises more than tau above its running max, the running max is kept
       // (no exchange between the two halves is needed for that).  Otherwise
@@ -503,7 +519,7 @@ fwd_tile_kernel(const FwdKernelParams p) {
       }
       // ---- P = exp2((s - m) c2) <= exp2(tau), row sum, 16-bit pack
       const float mg = (m_run[g] == -INFINITY) ? 0.0f : m_run[g];
-      const float nb = -mg * c2;
+      const float nb = ALIBI ? (kb - mg) * c2 : -mg * c2;
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll

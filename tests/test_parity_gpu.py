@@ -144,12 +144,8 @@ def test_varlen_small_full(case):
     gate_check(np64(o), ro, np64(lse), rl, dtype, f"varlen {seed}")
 
 
-def _alibi_slopes(batch, heads, per_batch, device="cuda"):
-    """Geometric ALiBi slopes 2^(-8 (h + 1) / H); per batch entry scaled by (b + 1) / batch."""
-    base = torch.tensor([2.0 ** (-8.0 * (h + 1) / heads) for h in range(heads)], dtype=torch.float32)
-    if per_batch:
-        base = torch.stack([base * (b + 1) / batch for b in range(batch)])
-    return base.to(device)
+def _alibi_slopes(batch, heads, per_batch):
+    return W.alibi_slopes(heads, batch if per_batch else None, device="cuda")
 
 
 ALIBI_DENSE = [
@@ -275,9 +271,11 @@ def _sampled_dense(name, n_heads_sampled=3, n_rows=24, **extra):
     q, k, v = W.make_dense(c["seed"], c["batch"], c["seqlen_q"], c["seqlen_k"], c["heads_q"],
                            c["heads_kv"], c["head_dim"], c["dtype"], k_ramp=c.get("k_ramp", False),
                            device="cuda", **extra)
+    sl = W.alibi_slopes(c["heads_q"], device="cuda") if c.get("alibi") else None
     o, lse = _eng().attn_fwd(q, k, v, causal=c["causal"], window=c["window"], softcap=c["softcap"],
-                             softmax_scale=c.get("scale"))
+                             softmax_scale=c.get("scale"), alibi_slopes=sl)
     torch.cuda.synchronize()
+    sl_np = None if sl is None else sl.cpu().numpy().astype(np.float64)
     rng = np.random.default_rng(c["seed"])
     g = c["heads_q"] // c["heads_kv"]
     outs, refs, lses, lrefs = [], [], [], []
@@ -288,7 +286,7 @@ def _sampled_dense(name, n_heads_sampled=3, n_rows=24, **extra):
         ro, rl = oracle.attention_ref(np64(q[b:b + 1, :, h:h + 1]), np64(k[b:b + 1, :, h // g:h // g + 1]),
                                       np64(v[b:b + 1, :, h // g:h // g + 1]), scale=c.get("scale"),
                                       causal=c["causal"], window=c["window"], softcap=c["softcap"],
-                                      rows=rows)
+                                      rows=rows, alibi_slopes=None if sl_np is None else sl_np[h:h + 1])
         outs.append(np64(o[b, torch.as_tensor(rows, device=o.device), h]))
         refs.append(ro[0, :, 0])
         lses.append(np64(lse[b, h, torch.as_tensor(rows, device=o.device)]))
@@ -303,6 +301,10 @@ def test_full_cfg2():
 
 def test_full_cfg2_kramp():
     _sampled_dense("cfg2r_bf16_causal_2k_kramp")
+
+
+def test_full_cfg2_alibi():
+    _sampled_dense("cfg2a_bf16_causal_2k_alibi")
 
 
 def test_full_cfg4():
@@ -342,20 +344,22 @@ def test_full_cfg3_varlen():
                "bf16", "cfg3")
 
 
-@pytest.mark.parametrize("name", ["cfg5a_bf16_decode", "cfg5a_bf16_decode_paged"])
+@pytest.mark.parametrize("name", ["cfg5a_bf16_decode", "cfg5a_bf16_decode_paged", "cfg5a_bf16_decode_alibi"])
 def test_full_cfg5a_decode(name):
     c = W.WORKLOADS[name]
     print(f"[case] full {name}", flush=True)
     q, kc, vc, lens = W.make_kvcache(c["seed"], c["batch"], 1, c["seqlen_k"], c["heads_q"], c["heads_kv"],
                                      c["head_dim"], c["dtype"], device="cuda")
     table = None
+    sl = W.alibi_slopes(c["heads_q"], device="cuda") if c.get("alibi") else None
     if c.get("page"):
         pk, pv, table = W.page_cache(kc, vc, lens, c["page"], c["seed"])
         o, lse = _eng().attn_fwd_kvcache(q, pk, pv, cache_seqlens=lens, num_splits=c["num_splits"],
-                                         block_table=table)
+                                         block_table=table, alibi_slopes=sl)
         del pk, pv
     else:
-        o, lse = _eng().attn_fwd_kvcache(q, kc, vc, cache_seqlens=lens, num_splits=c["num_splits"])
+        o, lse = _eng().attn_fwd_kvcache(q, kc, vc, cache_seqlens=lens, num_splits=c["num_splits"],
+                                         alibi_slopes=sl)
     torch.cuda.synchronize()
     rng = np.random.default_rng(5)
     g = c["heads_q"] // c["heads_kv"]
@@ -364,7 +368,8 @@ def test_full_cfg5a_decode(name):
         b = int(rng.integers(0, c["batch"]))
         h = int(rng.integers(0, c["heads_q"]))
         ro, rl = oracle.attention_ref(np64(q[b:b + 1, :, h:h + 1]), np64(kc[b:b + 1, :, h // g:h // g + 1]),
-                                      np64(vc[b:b + 1, :, h // g:h // g + 1]))
+                                      np64(vc[b:b + 1, :, h // g:h // g + 1]),
+                                      alibi_slopes=None if sl is None else np64(sl[h:h + 1]))
         outs.append(np64(o[b, :, h]))
         refs.append(ro[0, :, 0])
         lses.append(np64(lse[b, h]))
