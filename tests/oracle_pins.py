@@ -387,6 +387,29 @@ def pin_torch_sdpa():
     assert np.allclose(o, _sdpa_ref(q, k, v, scale, band), atol=1e-12)
 
 
+def pin_alibi_sdpa():
+    """ALiBi = torch SDPA (fp64) with the distance bias passed as an additive float mask, and -inf
+    where causal masking hides a key; random inputs, Sq != Sk both ways, GQA."""
+    rng = _rng(15)
+    for (sq, sk, causal) in [(13, 13, True), (7, 19, True), (19, 7, False), (11, 11, False)]:
+        b, hq, hkv, d = 2, 4, 2, 16
+        q = rng.standard_normal((b, sq, hq, d))
+        k = rng.standard_normal((b, sk, hkv, d))
+        v = rng.standard_normal((b, sk, hkv, d))
+        slopes = rng.uniform(0.05, 1.0, size=(b, hq))
+        scale = 0.3
+        out, _ = oracle.attention_ref(q, k, v, scale=scale, causal=causal, alibi_slopes=slopes)
+        i = np.arange(sq)[:, None] + (sk - sq)
+        j = np.arange(sk)[None, :]
+        dist = np.abs(i - j).astype(np.float64)
+        for bb in range(b):
+            mask = -slopes[bb][:, None, None] * dist[None]          # [Hq, Sq, Sk]
+            if causal:
+                mask = np.where(j <= i, mask, -np.inf)
+            ref = _sdpa_ref(q[bb:bb + 1], k[bb:bb + 1], v[bb:bb + 1], scale, mask[None])
+            assert np.allclose(out[bb:bb + 1], ref, atol=1e-12)
+
+
 def pin_varlen_block_diagonal():
     """Packed sequences = one long sequence under a block-diagonal causal mask (torch SDPA)."""
     rng = _rng(13)
@@ -542,6 +565,7 @@ ALL_PINS = [
     pin_paged_cache_is_contiguous,
     pin_alibi_closed_forms,
     pin_alibi_after_softcap,
+    pin_alibi_sdpa,
     pin_torch_sdpa,
     pin_varlen_block_diagonal,
     pin_gqa_is_repeated_mha,
