@@ -22,6 +22,9 @@ bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u
 bool stride_ok(int64_t s) { return s >= 0 && (s & 7) == 0; }
 bool row_stride_ok(int64_t s) { return stride_ok(s) && s < kMaxRowStride; }
 
+// A skipped rescale lets P reach 2^threshold; 2^15 still fits fp16 (max 65504).
+constexpr float kMaxRescaleThreshold = 15.0f;
+
 int check_common(int32_t dtype, int32_t head_dim, int32_t heads_q, int32_t heads_kv,
                  const attn_softmax_opts& o) {
   if (dtype != ATTN_DTYPE_F16 && dtype != ATTN_DTYPE_BF16) return ATTN_E_UNSUPPORTED;
@@ -30,7 +33,7 @@ int check_common(int32_t dtype, int32_t head_dim, int32_t heads_q, int32_t heads
   if (o.window_left < -1 || o.window_right < -1) return ATTN_E_WINDOW;
   if (o.causal != 0 && o.causal != 1) return ATTN_E_ARG;
   if (!std::isfinite(o.softmax_scale) || !std::isfinite(o.softcap) || o.softcap < 0.0f ||
-      !std::isfinite(o.rescale_threshold))
+      !std::isfinite(o.rescale_threshold) || o.rescale_threshold > kMaxRescaleThreshold)
     return ATTN_E_ARG;
   if (o.alibi_slopes != nullptr) {
     if (o.alibi_batch_stride < 0) return ATTN_E_ARG;

@@ -40,8 +40,10 @@
  *    before masking; 0 disables it.
  *  - softmax_scale <= 0 selects 1/sqrt(head_dim).
  *  - rescale_threshold < 0 selects the default 8.0 (16-bit inputs); 0 gives
- *    the classic always-rescale online softmax.  Any value >= 0 gives the
- *    same exact result up to rounding.
+ *    the classic always-rescale online softmax.  Any value in [0, 15] gives
+ *    the same exact result up to rounding; larger values are rejected
+ *    (ATTN_E_ARG), since a skipped rescale lets P reach 2^threshold and P is
+ *    rounded to the 16-bit input type (fp16 tops out at 65504).
  *  - LSE is natural-log, fp32.  A query row with no visible key gets O = 0
  *    and LSE = -inf.  `lse` may be NULL.
  *  - Results are deterministic: identical inputs give bit-identical outputs.

@@ -127,6 +127,8 @@ _BAD_FWD = [
     (dict(softcap=-1.0), binding.ATTN_E_ARG),
     (dict(softmax_scale=float("nan")), binding.ATTN_E_ARG),
     (dict(causal=2), binding.ATTN_E_ARG),
+    (dict(rescale_threshold=15.5), binding.ATTN_E_ARG),
+    (dict(rescale_threshold=float("inf")), binding.ATTN_E_ARG),
 ]
 
 
