@@ -1,4 +1,4 @@
-"""CPU oracle for exact attention forward -- TEST INFRASTRUCTURE ONLY.
+"""CPU oracle for exact attention (forward and backward) -- TEST INFRASTRUCTURE ONLY.
 
 This package is the plain, slow, obviously-correct reference the GPU library is
 checked against.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
@@ -13,7 +13,8 @@ Sources (web pages, cited by title and section):
   flash-attention fork -- section 1.2 "A-1 -- rescale threshold and max
   lagging" (threshold 8.0, max lagging, P <= 256), section 2 (public API
   features: causal, window, ALiBi, softcap, varlen, kv-cache), section 4.6
-  (edge probes: LSE shape [B, H, S], window (0,0) gives V).
+  (edge probes: LSE shape [B, H, S], window (0,0) gives V), section 4.4
+  (backward: dQ, dK, dV checked against an fp32 reference).
 * [v1.2]  release page "FA2 2.9.0 Kernel Changes in v1.2" -- section 1
   (softmax_rescale_o: scaled difference of old and new row max in log2
   units, rescale of O and row_sum), section 2 (scale_apply_exp2: exp2 of
@@ -26,6 +27,7 @@ Sources (web pages, cited by title and section):
 Modules:
 
 * ``attention``  -- the plain definition (full materialised softmax, fp64).
+* ``backward``   -- the gradients (dQ, dK, dV) of that definition, fp64.
 * ``tiled``      -- the tiled online-softmax algorithm with RescaleThreshold
   and max lagging, step by step in fp64 (pins the method's semantics).
 * ``metrics``    -- rel_Linf, cosine and LSE error as the gates use them.
@@ -41,5 +43,6 @@ from .attention import (  # noqa: F401
     allowed_mask,
     gather_pages,
 )
+from .backward import attention_bwd_ref, attention_bwd_varlen_ref  # noqa: F401
 from .tiled import tiled_ref  # noqa: F401
 from .metrics import rel_linf, cosine, lse_max_abs_err, compare  # noqa: F401

@@ -355,6 +355,147 @@ def pin_alibi_after_softcap():
     assert abs(lse[0, 0, 0] - math.log(math.exp(t0) + math.exp(t1))) < 1e-13
 
 
+# ---------------------------------------------------------------- backward
+
+def _torch_attention(q, k, v, scale, causal, window, softcap, slopes):
+    """An independent fp64 torch forward (autograd-ready): masks by masked_fill, GQA by
+    repeat_interleave, softcap by torch.tanh, ALiBi from a distance matrix."""
+    b, sq, hq, d = q.shape
+    sk, hkv = k.shape[1], k.shape[2]
+    g = hq // hkv
+    qt = q.permute(0, 2, 1, 3)
+    kt = k.repeat_interleave(g, dim=2).permute(0, 2, 1, 3)
+    vt = v.repeat_interleave(g, dim=2).permute(0, 2, 1, 3)
+    s = torch.matmul(qt, kt.transpose(-1, -2)) * scale
+    if softcap > 0:
+        s = softcap * torch.tanh(s / softcap)
+    i = torch.arange(sq, dtype=torch.float64)[:, None] + (sk - sq)
+    j = torch.arange(sk, dtype=torch.float64)[None, :]
+    if slopes is not None:
+        sl = torch.as_tensor(slopes, dtype=torch.float64)
+        sl = sl[None, :, None, None] if sl.ndim == 1 else sl[:, :, None, None]
+        s = s - sl * (i - j).abs()
+    keep = torch.ones(sq, sk, dtype=torch.bool)
+    if causal:
+        keep &= j <= i
+    if window[0] >= 0:
+        keep &= j >= i - window[0]
+    if window[1] >= 0:
+        keep &= j <= i + window[1]
+    s = s.masked_fill(~keep, float("-inf"))
+    return torch.matmul(torch.softmax(s, dim=-1), vt).permute(0, 2, 1, 3)
+
+
+def pin_bwd_autograd():
+    """dQ, dK, dV = fp64 torch autograd of an independently written forward (causal, window,
+    softcap, ALiBi, GQA, Sq != Sk; every row keeps at least one key)."""
+    rng = _rng(21)
+    cases = [
+        (2, 9, 9, 4, 2, 8, dict(causal=True)),
+        (1, 7, 12, 2, 2, 16, dict(causal=True, softcap=1.5)),
+        (2, 11, 11, 6, 3, 8, dict(causal=False, window=(3, 2))),
+        (1, 10, 10, 4, 1, 8, dict(causal=True, window=(4, 0), softcap=2.0, slopes=[0.3, 0.1, 0.7, 0.05])),
+        (2, 8, 8, 2, 2, 8, dict(causal=False, slopes=[[0.2, 0.5], [0.9, 0.0]])),
+    ]
+    for (b, sq, sk, hq, hkv, d, kw) in cases:
+        q = rng.standard_normal((b, sq, hq, d))
+        k = rng.standard_normal((b, sk, hkv, d))
+        v = rng.standard_normal((b, sk, hkv, d))
+        do = rng.standard_normal((b, sq, hq, d))
+        scale = 0.6
+        causal, window = kw.get("causal", False), kw.get("window", (-1, -1))
+        softcap, slopes = kw.get("softcap", 0.0), kw.get("slopes")
+        tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+        o = _torch_attention(tq, tk, tv, scale, causal, window, softcap, slopes)
+        (o * torch.from_numpy(do)).sum().backward()
+        dq, dk, dv = oracle.attention_bwd_ref(q, k, v, do, scale=scale, causal=causal, window=window,
+                                              softcap=softcap, alibi_slopes=slopes)
+        for mine, ref in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+            assert np.allclose(mine, ref.numpy(), atol=1e-11, rtol=1e-11)
+
+
+def pin_bwd_finite_differences():
+    """Central differences of sum(dO * O) through the (pinned) forward oracle, every input
+    coordinate of a tiny causal, windowed, softcapped, ALiBi, GQA problem."""
+    rng = _rng(22)
+    b, sq, sk, hq, hkv, d = 1, 4, 6, 2, 1, 3
+    q = rng.standard_normal((b, sq, hq, d))
+    k = rng.standard_normal((b, sk, hkv, d))
+    v = rng.standard_normal((b, sk, hkv, d))
+    do = rng.standard_normal((b, sq, hq, d))
+    kw = dict(scale=0.8, causal=True, window=(3, -1), softcap=1.7, alibi_slopes=[0.25, 0.6])
+
+    def loss(q_, k_, v_):
+        o, _ = oracle.attention_ref(q_, k_, v_, **kw)
+        return float((o * do).sum())
+
+    dq, dk, dv = oracle.attention_bwd_ref(q, k, v, do, **kw)
+    h = 1e-5
+    for x, grad, slot in ((q, dq, 0), (k, dk, 1), (v, dv, 2)):
+        for idx in np.ndindex(x.shape):
+            args = [q, k, v]
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args[slot] = xp
+            fp = loss(*args)
+            args[slot] = xm
+            fm = loss(*args)
+            assert abs((fp - fm) / (2 * h) - grad[idx]) < 1e-7, (slot, idx)
+
+
+def pin_bwd_invariants():
+    """Softmax Jacobian facts: sum_j dV_j = sum of dO over rows with a key; without softcap
+    sum_j dK_j = 0 and dQ does not change when every K row moves by the same vector; rows
+    with no visible key get dQ = 0 and add nothing to dK, dV."""
+    rng = _rng(23)
+    b, sq, sk, hq, hkv, d = 2, 12, 9, 4, 2, 8
+    q = rng.standard_normal((b, sq, hq, d))
+    k = rng.standard_normal((b, sk, hkv, d))
+    v = rng.standard_normal((b, sk, hkv, d))
+    do = rng.standard_normal((b, sq, hq, d))
+    kw = dict(causal=True, alibi_slopes=[0.1, 0.2, 0.3, 0.4])
+    dq, dk, dv = oracle.attention_bwd_ref(q, k, v, do, **kw)
+    g = hq // hkv
+    live = sq - sk   # causal with Sq > Sk: rows 0 .. Sq-Sk-1 see no key
+    for bb in range(b):
+        for kvh in range(hkv):
+            heads = range(kvh * g, (kvh + 1) * g)
+            want = sum(do[bb, live:, h].sum(axis=0) for h in heads)
+            assert np.allclose(dv[bb, :, kvh].sum(axis=0), want, atol=1e-12)
+            assert np.allclose(dk[bb, :, kvh].sum(axis=0), 0.0, atol=1e-12)
+    assert np.all(dq[:, :live] == 0.0)
+    shift = rng.standard_normal(d)
+    dq2, _, _ = oracle.attention_bwd_ref(q, k + shift, v, do, **kw)
+    assert np.allclose(dq2, dq, atol=1e-12)
+    # the empty rows' dO does not reach dK or dV
+    do3 = do.copy()
+    do3[:, :live] = rng.standard_normal(do3[:, :live].shape)
+    _, dk3, dv3 = oracle.attention_bwd_ref(q, k, v, do3, **kw)
+    assert np.array_equal(dk3, dk) and np.array_equal(dv3, dv)
+
+
+def pin_bwd_varlen_is_per_sequence():
+    """Packed-sequence backward = the dense backward of each sequence on its own."""
+    rng = _rng(24)
+    lens = [5, 1, 0, 8]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    hq, hkv, d = 4, 2, 8
+    q = rng.standard_normal((cu[-1], hq, d))
+    k = rng.standard_normal((cu[-1], hkv, d))
+    v = rng.standard_normal((cu[-1], hkv, d))
+    do = rng.standard_normal((cu[-1], hq, d))
+    dq, dk, dv = oracle.attention_bwd_varlen_ref(q, k, v, do, cu, cu, causal=True)
+    for s in range(len(lens)):
+        a, z = cu[s], cu[s + 1]
+        if z == a:
+            continue
+        rq, rk, rv = oracle.attention_bwd_ref(q[None, a:z], k[None, a:z], v[None, a:z], do[None, a:z],
+                                              causal=True)
+        assert np.array_equal(dq[a:z], rq[0]) and np.array_equal(dk[a:z], rk[0])
+        assert np.array_equal(dv[a:z], rv[0])
+
+
 # ---------------------------------------------------------------- library routines
 
 def _sdpa_ref(q, k, v, scale, mask_bool):
@@ -566,6 +707,10 @@ ALL_PINS = [
     pin_alibi_closed_forms,
     pin_alibi_after_softcap,
     pin_alibi_sdpa,
+    pin_bwd_autograd,
+    pin_bwd_finite_differences,
+    pin_bwd_invariants,
+    pin_bwd_varlen_is_per_sequence,
     pin_torch_sdpa,
     pin_varlen_block_diagonal,
     pin_gqa_is_repeated_mha,

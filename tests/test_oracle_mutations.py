@@ -3,8 +3,10 @@
 This shows the pins are strong enough: a dropped scale, an off-by-one mask,
 top-left instead of bottom-right alignment, a wrong GQA head map, a
 transposed operand, softcap on the unscaled score, log2 instead of natural
-log, a missing max shift, a window bound read as unbounded, or the
-superseded keep-new-max skip rule must each make at least one pin fail.
+log, a missing max shift, a window bound read as unbounded, the superseded
+keep-new-max skip rule, or a backward without the softmax row term, the
+softcap derivative, the scale or the GQA sum must each make at least one pin
+fail.
 """
 
 import contextlib
@@ -14,6 +16,7 @@ import pytest
 
 import oracle_pins
 from oracle import attention as oatt
+from oracle import backward as obwd
 from oracle import tiled as otiled
 
 _orig_mask = oatt.allowed_mask
@@ -134,6 +137,32 @@ def _alibi_scaled(seqlen_q, seqlen_k, rows, slope):
 _orig_alibi = oatt.alibi_bias
 
 
+def _bwd_no_rowsum(p, dp):
+    return p * dp                                                # softmax Jacobian without the row term
+
+
+def _bwd_no_softcap_factor(dt, u, scale, softcap):
+    return scale * dt                                            # tanh derivative dropped
+
+
+def _bwd_softcap_factor_linear(dt, u, scale, softcap):
+    if softcap > 0.0:
+        dt = dt * (1.0 - np.abs(np.tanh(u / softcap)))           # 1 - |tanh| instead of 1 - tanh^2
+    return scale * dt
+
+
+def _bwd_no_scale(dt, u, scale, softcap):
+    if softcap > 0.0:
+        th = np.tanh(u / softcap)
+        dt = dt * (1.0 - th * th)
+    return dt                                                    # d<Q,K> missing the scale
+
+
+def _bwd_gqa_overwrite(dk, dv, dk_h, dv_h):
+    dk[...] = dk_h                                               # last query head wins
+    dv[...] = dv_h
+
+
 MUTATIONS = {
     "causal_strict_lt": (oatt, "allowed_mask", _mask_causal_strict),
     "top_left_alignment": (oatt, "allowed_mask", _mask_top_left),
@@ -152,6 +181,11 @@ MUTATIONS = {
     "alibi_sign": (oatt, "alibi_bias", _alibi_sign),
     "alibi_no_offset": (oatt, "alibi_bias", _alibi_no_offset),
     "alibi_scaled": (oatt, "alibi_bias", _alibi_scaled),
+    "bwd_no_rowsum": (obwd, "softmax_backward", _bwd_no_rowsum),
+    "bwd_no_softcap_factor": (obwd, "score_backward", _bwd_no_softcap_factor),
+    "bwd_softcap_factor_linear": (obwd, "score_backward", _bwd_softcap_factor_linear),
+    "bwd_no_scale": (obwd, "score_backward", _bwd_no_scale),
+    "bwd_gqa_overwrite": (obwd, "_add_kv_grad", _bwd_gqa_overwrite),
 }
 
 
