@@ -29,7 +29,9 @@ sys.path.insert(0, ROOT)
 METRIC = "attn fwd TFLOP/s (4·B·H·Sq·Sk·D) & % MFMA peak; decode HBM GB/s"
 PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0}  # MI355X dense MFMA, published
 PEAK_HBM_GBS = 8000.0                                  # MI355X HBM3E, published
-KERNEL_SRC = os.path.join(ROOT, "exact_tiled_attention_fa2_amd", "csrc", "attn_kernels.hip")
+# Sources the forward tile kernel is compiled from (their hash keys the traffic record).
+KERNEL_SRCS = [os.path.join(ROOT, "exact_tiled_attention_fa2_amd", "csrc", n)
+               for n in ("attn_kernels.hip", "attn_device.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_cfg2.json")
 
 
@@ -55,8 +57,11 @@ def visible_pairs(sq, sk, causal, window):
 
 
 def kernel_sha():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def load_traffic():

@@ -8,7 +8,8 @@
 // step, the exp2-domain probabilities with the -inf guard, the first KV step
 // that never skips, and the split-KV variant of the row-block kernel).
 //
-// Layout of one workgroup (256 threads = 4 wave64s, 128 query rows):
+// Layout of one workgroup (NW wave64s: 8 for the dense D = 128 tiles, 4 for
+// softcap, D = 64/256 and decode; 32 query rows per wave):
 //  * Each wave owns 32 query rows.  Scores are computed transposed,
 //    S^T = K Q^T, with v_mfma_f32_32x32x16: A = a 32-key slice of K read
 //    from LDS, B = the wave's Q fragment held in VGPRs for the whole loop.
@@ -23,12 +24,12 @@
 //    row-major V tile in LDS with ds_read_b64_tr_b16, whose 16-lane
 //    transpose hands lane l the element l % 4 of the rows addressed by
 //    lanes 4j + l / 4 -- two such reads give the 8 keys of one lane.
-//  * K and V tiles (BK keys x D) stream HBM -> VGPR -> LDS with 16-byte
-//    coalesced loads, double-buffered in LDS (one barrier per KV step); the
-//    global loads of step j+1 are in flight while step j computes.  16-byte
-//    chunks of a row are XOR-swizzled so that both the K reads (8/16 rows,
-//    same chunk) and the transposing V reads (4 rows x 2 chunks) hit
-//    distinct banks.
+//  * K and V tiles (BK keys x D) stream HBM -> LDS with 16-byte
+//    global_load_lds copies (no VGPR staging), double-buffered in LDS (one
+//    barrier per KV step); the copies of step j+1 are in flight while step j
+//    computes.  16-byte chunks of a row are XOR-swizzled so that both the K
+//    reads (8/16 rows, same chunk) and the transposing V reads (4 rows x 2
+//    chunks) hit distinct banks.
 //  * Masks run only on KV steps that cross a mask edge for the wave; steps
 //    that are fully masked for a wave are skipped by that wave.
 //  * Keys at or beyond the valid length are never loaded (the last partial
@@ -42,85 +43,11 @@
 #include <algorithm>
 #include <type_traits>
 
+#include "attn_device.h"
 #include "attn_internal.h"
 
 namespace attn {
 namespace {
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-constexpr float kLog2e = 1.4426950408889634f;
-
-struct TypeBF16 {
-  static __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-  }
-  // Two fp32 -> one packed pair, round to nearest even.
-  static __device__ __forceinline__ uint32_t pack(float x, float y) {
-    f32x2 v = {x, y};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-  }
-};
-
-struct TypeF16 {
-  static __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ uint32_t pack(float x, float y) {
-    f32x2 v = {x, y};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
-  }
-};
-
-// XOR pattern for the 16-byte chunk index of LDS row r (r taken mod 16).
-// Rows 0..15 map to 16 distinct values, so the K operand reads (16 rows, one
-// chunk each) cover all banks.  Within each group of 4 consecutive rows that
-// starts at a multiple of 4 the pattern differs in bits 2-3 only, so the
-// transposing V reads (4 rows x 4 adjacent chunks per 32 lanes) also land on
-// 16 distinct chunk positions.
-__device__ __forceinline__ int chunk_swizzle(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-template <bool SOFTCAP>
-__device__ __forceinline__ float transform_score(float s, float pre, float cap) {
-  if constexpr (SOFTCAP) {
-    // cap * tanh(s * pre) with tanh(x) = 1 - 2 / (exp(2x) + 1); saturates to +-cap.
-    float e = fast_exp2(s * pre * (2.0f * kLog2e));
-    return cap * (1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f));
-  } else {
-    return s;
-  }
-}
-
-// One 16-byte HBM -> LDS copy per lane (global_load_lds_dwordx4): lane l of
-// the wave writes LDS bytes [lds + 16 l, lds + 16 l + 16); `lds` must be
-// wave-uniform.  No VGPR is used for the data.
-__device__ __forceinline__ void dma16(const void* g, const char* lds) {
-  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(g),
-                                   (__attribute__((address_space(3))) void*)(lds), 16, 0, 0);
-}
-
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
-
-// s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt in bits 3:0 and 15:14), other counters untouched.
-template <int N>
-__device__ __forceinline__ void wait_vmem_le() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 // Work item of one workgroup.  Work items are (query tile, head, batch x
 // split).  Workgroups are dealt round-robin to the 8 XCDs (each with its own
