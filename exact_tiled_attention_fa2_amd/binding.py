@@ -79,6 +79,29 @@ class KvcacheArgs(ctypes.Structure):
                 ("num_pages", _i32), ("reserved0", _i32)]
 
 
+_STRIDES3 = [f"{t}_{k}_stride" for t in ("q", "k", "v", "o", "do", "dq", "dk", "dv")
+             for k in ("batch", "row", "head")]
+_STRIDES2 = [f"{t}_{k}_stride" for t in ("q", "k", "v", "o", "do", "dq", "dk", "dv")
+             for k in ("row", "head")]
+
+
+class BwdArgs(ctypes.Structure):
+    _fields_ = [("dtype", _i32), ("batch", _i32), ("seqlen_q", _i32), ("seqlen_k", _i32),
+                ("heads_q", _i32), ("heads_kv", _i32), ("head_dim", _i32),
+                ("q", _vp), ("k", _vp), ("v", _vp), ("o", _vp), ("dout", _vp), ("lse", _vp),
+                ("dq", _vp), ("dk", _vp), ("dv", _vp)] + \
+               [(n, _i64) for n in _STRIDES3] + [("opts", SoftmaxOpts)]
+
+
+class BwdVarlenArgs(ctypes.Structure):
+    _fields_ = [("dtype", _i32), ("batch", _i32), ("total_q", _i32), ("total_k", _i32),
+                ("max_seqlen_q", _i32), ("max_seqlen_k", _i32), ("heads_q", _i32),
+                ("heads_kv", _i32), ("head_dim", _i32),
+                ("q", _vp), ("k", _vp), ("v", _vp), ("o", _vp), ("dout", _vp), ("lse", _vp),
+                ("dq", _vp), ("dk", _vp), ("dv", _vp), ("cu_seqlens_q", _vp), ("cu_seqlens_k", _vp)] + \
+               [(n, _i64) for n in _STRIDES2] + [("opts", SoftmaxOpts)]
+
+
 _LIB = None
 
 
@@ -102,6 +125,14 @@ def lib():
         h.attn_kvcache_workspace_bytes.restype = ctypes.c_size_t
         h.attn_kvcache_num_splits.argtypes = [_i32] * 6
         h.attn_kvcache_num_splits.restype = _i32
+        h.attn_bwd.argtypes = [ctypes.POINTER(BwdArgs), _vp, ctypes.c_size_t, _vp]
+        h.attn_bwd.restype = ctypes.c_int
+        h.attn_bwd_workspace_bytes.argtypes = [_i32] * 3
+        h.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+        h.attn_bwd_varlen.argtypes = [ctypes.POINTER(BwdVarlenArgs), _vp, ctypes.c_size_t, _vp]
+        h.attn_bwd_varlen.restype = ctypes.c_int
+        h.attn_bwd_varlen_workspace_bytes.argtypes = [_i32] * 2
+        h.attn_bwd_varlen_workspace_bytes.restype = ctypes.c_size_t
         h.attn_status_string.argtypes = [ctypes.c_int]
         h.attn_status_string.restype = ctypes.c_char_p
         h.attn_version.argtypes = []
@@ -259,6 +290,77 @@ def attn_fwd_kvcache(q, k_cache, v_cache, cache_seqlens=None, num_splits=0, caus
     _check(lib().attn_fwd_kvcache(ctypes.byref(a), _ptr(workspace), ws_bytes, _stream(stream, q.device)),
            "attn_fwd_kvcache")
     return out, lse
+
+
+def attn_bwd_workspace_bytes(batch, seqlen_q, heads_q):
+    return int(lib().attn_bwd_workspace_bytes(batch, seqlen_q, heads_q))
+
+
+def _same_dtype(ref, *ts):
+    for t in ts:
+        if t.dtype != ref.dtype:
+            raise TypeError("q, k, v, o, dout and the gradients must share one dtype")
+        if t.stride(-1) != 1:
+            raise ValueError("the head dimension must be contiguous")
+
+
+def attn_bwd(q, k, v, o, lse, dout, causal=False, window=(-1, -1), softcap=0.0, softmax_scale=None,
+             dq=None, dk=None, dv=None, workspace=None, stream=None, alibi_slopes=None):
+    """Gradients of attn_fwd: q, o, dout [B, Sq, Hq, D], k, v [B, Sk, Hkv, D], lse [B, Hq, Sq]
+    (from attn_fwd with the same options) -> (dq, dk, dv)."""
+    _need_gpu(q, k, v, o, lse, dout)
+    b, sq, hq, d = q.shape
+    sk, hkv = k.shape[1], k.shape[2]
+    dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
+    dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
+    dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
+    _same_dtype(q, k, v, o, dout, dq, dk, dv)
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (b, hq, sq):
+        raise TypeError("lse must be a contiguous float32 [batch, heads_q, seqlen_q] tensor")
+    need = attn_bwd_workspace_bytes(b, sq, hq)
+    if need > 0 and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    a = BwdArgs(_dtype_code(q), b, sq, sk, hq, hkv, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
+                _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                *[s for t in (q, k, v, o, dout, dq, dk, dv) for s in t.stride()[:3]],
+                _opts(causal, window, softcap, softmax_scale, -1.0, alibi_slopes))
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().attn_bwd(ctypes.byref(a), _ptr(workspace), ws_bytes, _stream(stream, q.device)), "attn_bwd")
+    return dq, dk, dv
+
+
+def attn_bwd_varlen_workspace_bytes(total_q, heads_q):
+    return int(lib().attn_bwd_varlen_workspace_bytes(total_q, heads_q))
+
+
+def attn_bwd_varlen(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                    causal=False, window=(-1, -1), softcap=0.0, softmax_scale=None, dq=None, dk=None,
+                    dv=None, workspace=None, stream=None, alibi_slopes=None):
+    """Gradients of attn_fwd_varlen: q, o, dout [Tq, Hq, D], k, v [Tk, Hkv, D], lse [Hq, Tq]."""
+    _need_gpu(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k)
+    tq, hq, d = q.shape
+    tk, hkv = k.shape[0], k.shape[1]
+    batch = cu_seqlens_q.shape[0] - 1
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
+    dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
+    dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
+    _same_dtype(q, k, v, o, dout, dq, dk, dv)
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (hq, tq):
+        raise TypeError("lse must be a contiguous float32 [heads_q, total_q] tensor")
+    need = attn_bwd_varlen_workspace_bytes(tq, hq)
+    if need > 0 and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    a = BwdVarlenArgs(_dtype_code(q), batch, tq, tk, int(max_seqlen_q), int(max_seqlen_k), hq, hkv, d,
+                      _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                      _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                      *[s for t in (q, k, v, o, dout, dq, dk, dv) for s in t.stride()[:2]],
+                      _opts(causal, window, softcap, softmax_scale, -1.0, alibi_slopes))
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().attn_bwd_varlen(ctypes.byref(a), _ptr(workspace), ws_bytes, _stream(stream, q.device)),
+           "attn_bwd_varlen")
+    return dq, dk, dv
 
 
 def default_scale(head_dim):

@@ -69,6 +69,24 @@ void resolve_opts(const attn_softmax_opts& o, int head_dim, FwdKernelParams& p) 
   p.alibi_inv_scale = 1.0f / p.scale_ln;
 }
 
+// The backward's constants: the same score units as the forward, plus the
+// plain scale (dQ, dK) and 1 / softcap (the softcap derivative).
+void resolve_bwd_opts(const attn_softmax_opts& o, int head_dim, attn::BwdKernelParams& p) {
+  FwdKernelParams f;
+  std::memset(&f, 0, sizeof(f));
+  resolve_opts(o, head_dim, f);
+  p.window_left = f.window_left;
+  p.window_right = f.window_right;
+  p.scale = o.softmax_scale > 0.0f ? o.softmax_scale : 1.0f / std::sqrt((float)head_dim);
+  p.scale_log2 = f.scale_log2;
+  p.softcap_pre = f.softcap_pre;
+  p.softcap = f.softcap;
+  p.inv_softcap = f.softcap > 0.0f ? 1.0f / f.softcap : 0.0f;
+  p.alibi = f.alibi;
+  p.alibi_bstride = f.alibi_bstride;
+  p.alibi_inv_scale = f.alibi_inv_scale;
+}
+
 int launch_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH; }
 
 int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
@@ -254,6 +272,120 @@ int attn_fwd_kvcache(const attn_kvcache_args* a, void* workspace, size_t workspa
   c.o_batch = a->o_batch_stride; c.o_row = a->o_row_stride; c.o_head = a->o_head_stride;
   c.batch = a->batch; c.seqlen_q = a->seqlen_q; c.heads_q = a->heads_q; c.num_splits = splits;
   return launch_status(attn::launch_combine(c, a->dtype, a->head_dim, (hipStream_t)stream));
+}
+
+size_t attn_bwd_workspace_bytes(int32_t batch, int32_t seqlen_q, int32_t heads_q) {
+  if (batch <= 0 || seqlen_q <= 0 || heads_q <= 0) return 0;
+  return (size_t)batch * heads_q * seqlen_q * sizeof(float);
+}
+
+int attn_bwd(const attn_bwd_args* a, void* workspace, size_t workspace_bytes, void* stream) {
+  if (a == nullptr) return ATTN_E_NULL;
+  int st = check_common(a->dtype, a->head_dim, a->heads_q, a->heads_kv, a->opts);
+  if (st != ATTN_OK) return st;
+  if (a->head_dim == 256) return ATTN_E_UNSUPPORTED;
+  if (a->batch < 0 || a->seqlen_q < 0 || a->seqlen_k < 0) return ATTN_E_SHAPE;
+  if (a->batch == 0 || (a->seqlen_q == 0 && a->seqlen_k == 0)) return ATTN_OK;
+  if (a->seqlen_q > 0 && (a->q == nullptr || a->o == nullptr || a->dout == nullptr || a->lse == nullptr ||
+                          a->dq == nullptr))
+    return ATTN_E_NULL;
+  if (a->seqlen_k > 0 && (a->k == nullptr || a->v == nullptr || a->dk == nullptr || a->dv == nullptr))
+    return ATTN_E_NULL;
+  if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o) || !aligned16(a->dout) ||
+      !aligned16(a->dq) || !aligned16(a->dk) || !aligned16(a->dv) ||
+      !stride_ok(a->q_batch_stride) || !row_stride_ok(a->q_row_stride) || !stride_ok(a->q_head_stride) ||
+      !stride_ok(a->k_batch_stride) || !row_stride_ok(a->k_row_stride) || !stride_ok(a->k_head_stride) ||
+      !stride_ok(a->v_batch_stride) || !row_stride_ok(a->v_row_stride) || !stride_ok(a->v_head_stride) ||
+      !stride_ok(a->o_batch_stride) || !row_stride_ok(a->o_row_stride) || !stride_ok(a->o_head_stride) ||
+      !stride_ok(a->do_batch_stride) || !row_stride_ok(a->do_row_stride) || !stride_ok(a->do_head_stride) ||
+      !stride_ok(a->dq_batch_stride) || !row_stride_ok(a->dq_row_stride) || !stride_ok(a->dq_head_stride) ||
+      !stride_ok(a->dk_batch_stride) || !row_stride_ok(a->dk_row_stride) || !stride_ok(a->dk_head_stride) ||
+      !stride_ok(a->dv_batch_stride) || !row_stride_ok(a->dv_row_stride) || !stride_ok(a->dv_head_stride))
+    return ATTN_E_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(a->lse) & 3u) != 0) return ATTN_E_ALIGN;
+  const size_t need = attn_bwd_workspace_bytes(a->batch, a->seqlen_q, a->heads_q);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
+    return ATTN_E_WORKSPACE;
+
+  attn::BwdKernelParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.q = a->q; p.k = a->k; p.v = a->v; p.o = a->o; p.dout = a->dout; p.lse = a->lse;
+  p.dsum = static_cast<float*>(workspace);
+  p.dq = a->dq; p.dk = a->dk; p.dv = a->dv;
+  p.q_batch = a->q_batch_stride; p.q_row = a->q_row_stride; p.q_head = a->q_head_stride;
+  p.k_batch = a->k_batch_stride; p.k_row = a->k_row_stride; p.k_head = a->k_head_stride;
+  p.v_batch = a->v_batch_stride; p.v_row = a->v_row_stride; p.v_head = a->v_head_stride;
+  p.o_batch = a->o_batch_stride; p.o_row = a->o_row_stride; p.o_head = a->o_head_stride;
+  p.do_batch = a->do_batch_stride; p.do_row = a->do_row_stride; p.do_head = a->do_head_stride;
+  p.dq_batch = a->dq_batch_stride; p.dq_row = a->dq_row_stride; p.dq_head = a->dq_head_stride;
+  p.dk_batch = a->dk_batch_stride; p.dk_row = a->dk_row_stride; p.dk_head = a->dk_head_stride;
+  p.dv_batch = a->dv_batch_stride; p.dv_row = a->dv_row_stride; p.dv_head = a->dv_head_stride;
+  p.lse_batch = (int64_t)a->heads_q * a->seqlen_q;
+  p.lse_head = a->seqlen_q;
+  p.batch = a->batch; p.seqlen_q = a->seqlen_q; p.seqlen_k = a->seqlen_k;
+  p.heads_q = a->heads_q; p.heads_kv = a->heads_kv; p.group = a->heads_q / a->heads_kv;
+  p.total_q = (int32_t)std::min<int64_t>((int64_t)a->batch * a->seqlen_q, INT32_MAX);
+  if ((int64_t)a->batch * a->seqlen_q > INT32_MAX) return ATTN_E_SHAPE;
+  resolve_bwd_opts(a->opts, a->head_dim, p);
+  return launch_status(attn::launch_bwd(p, a->dtype, a->head_dim, (hipStream_t)stream));
+}
+
+size_t attn_bwd_varlen_workspace_bytes(int32_t total_q, int32_t heads_q) {
+  if (total_q <= 0 || heads_q <= 0) return 0;
+  return (size_t)total_q * heads_q * sizeof(float);
+}
+
+int attn_bwd_varlen(const attn_bwd_varlen_args* a, void* workspace, size_t workspace_bytes, void* stream) {
+  if (a == nullptr) return ATTN_E_NULL;
+  int st = check_common(a->dtype, a->head_dim, a->heads_q, a->heads_kv, a->opts);
+  if (st != ATTN_OK) return st;
+  if (a->head_dim == 256) return ATTN_E_UNSUPPORTED;
+  if (a->batch < 0 || a->total_q < 0 || a->total_k < 0 || a->max_seqlen_q < 0 || a->max_seqlen_k < 0)
+    return ATTN_E_SHAPE;
+  if (a->batch == 0 || (a->total_q == 0 && a->total_k == 0)) return ATTN_OK;
+  if (a->cu_seqlens_q == nullptr || a->cu_seqlens_k == nullptr) return ATTN_E_NULL;
+  if (a->total_q > 0 && (a->q == nullptr || a->o == nullptr || a->dout == nullptr || a->lse == nullptr ||
+                         a->dq == nullptr))
+    return ATTN_E_NULL;
+  if (a->total_k > 0 && (a->k == nullptr || a->v == nullptr || a->dk == nullptr || a->dv == nullptr))
+    return ATTN_E_NULL;
+  if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o) || !aligned16(a->dout) ||
+      !aligned16(a->dq) || !aligned16(a->dk) || !aligned16(a->dv) ||
+      !row_stride_ok(a->q_row_stride) || !stride_ok(a->q_head_stride) ||
+      !row_stride_ok(a->k_row_stride) || !stride_ok(a->k_head_stride) ||
+      !row_stride_ok(a->v_row_stride) || !stride_ok(a->v_head_stride) ||
+      !row_stride_ok(a->o_row_stride) || !stride_ok(a->o_head_stride) ||
+      !row_stride_ok(a->do_row_stride) || !stride_ok(a->do_head_stride) ||
+      !row_stride_ok(a->dq_row_stride) || !stride_ok(a->dq_head_stride) ||
+      !row_stride_ok(a->dk_row_stride) || !stride_ok(a->dk_head_stride) ||
+      !row_stride_ok(a->dv_row_stride) || !stride_ok(a->dv_head_stride))
+    return ATTN_E_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(a->lse) & 3u) != 0) return ATTN_E_ALIGN;
+  const size_t need = attn_bwd_varlen_workspace_bytes(a->total_q, a->heads_q);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
+    return ATTN_E_WORKSPACE;
+
+  attn::BwdKernelParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.q = a->q; p.k = a->k; p.v = a->v; p.o = a->o; p.dout = a->dout; p.lse = a->lse;
+  p.dsum = static_cast<float*>(workspace);
+  p.dq = a->dq; p.dk = a->dk; p.dv = a->dv;
+  p.cu_seqlens_q = a->cu_seqlens_q; p.cu_seqlens_k = a->cu_seqlens_k;
+  p.q_row = a->q_row_stride; p.q_head = a->q_head_stride;
+  p.k_row = a->k_row_stride; p.k_head = a->k_head_stride;
+  p.v_row = a->v_row_stride; p.v_head = a->v_head_stride;
+  p.o_row = a->o_row_stride; p.o_head = a->o_head_stride;
+  p.do_row = a->do_row_stride; p.do_head = a->do_head_stride;
+  p.dq_row = a->dq_row_stride; p.dq_head = a->dq_head_stride;
+  p.dk_row = a->dk_row_stride; p.dk_head = a->dk_head_stride;
+  p.dv_row = a->dv_row_stride; p.dv_head = a->dv_head_stride;
+  p.lse_batch = 0;
+  p.lse_head = a->total_q;
+  p.batch = a->batch; p.seqlen_q = a->max_seqlen_q; p.seqlen_k = a->max_seqlen_k;
+  p.heads_q = a->heads_q; p.heads_kv = a->heads_kv; p.group = a->heads_q / a->heads_kv;
+  p.total_q = a->total_q;
+  resolve_bwd_opts(a->opts, a->head_dim, p);
+  return launch_status(attn::launch_bwd(p, a->dtype, a->head_dim, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -1,0 +1,645 @@
+// Exact attention backward for gfx950 (CDNA4): dQ, dK, dV from the forward's
+// saved LSE (the pages list the backward among the library's kernels and check
+// its gradients against an fp32 reference: release page "v1.7 / flash_attn
+// 2.9.2.post1", section 4.4; the forward's rescale threshold does not enter
+// it, "FA2 2.9.0 Kernel Changes in v1.2", section 1).  For the loss whose
+// gradient with respect to O is dO, with P recomputed from the scores and LSE:
+//
+//     dV = P^T dO,   dP = dO V^T,   dT = P (dP - D),   D_i = <dO_i, O_i>
+//     dQ = scale * (dT g) K,   dK = scale * (dT g)^T Q
+//
+// where g = 1 - tanh^2 is the softcap derivative (1 without softcap) and
+// D_i = sum_j P_ij dP_ij = <dO_i, O_i> is the softmax Jacobian's row term.
+//
+// Three kernels, in stream order, no atomics (every output element has one
+// owner, so the result is deterministic):
+//  * bwd_dot_kernel: D = rowsum(dO * O) in fp32 (HBM-bound, one pass).
+//  * bwd_dkdv_kernel: one workgroup per 128-key tile of one KV head.  A wave
+//    owns 32 keys, holds their K and V rows as MFMA B operands in VGPRs and
+//    walks the query tiles of every query head of its GQA group: S = Q K^T
+//    and dP = dO V^T (A = Q / dO rows read from LDS), then the elementwise
+//    P and dS, then dV^T += dO^T P and dK^T += Q^T dS (A = Q^T / dO^T read
+//    transposed from the same LDS tiles with ds_read_b64_tr_b16, B = the
+//    packed P / dS registers).  In these accumulators a lane holds one key.
+//  * bwd_dq_kernel: one workgroup per 128-query tile of one query head, the
+//    forward's orientation (a lane holds one query): S^T = K Q^T and
+//    dP^T = V dO^T (A = K / V rows from LDS, B = Q / dO held in VGPRs), the
+//    elementwise dS^T, then dQ^T += K^T dS^T (A = K^T read transposed from
+//    the K tile).  It recomputes S and dP, which the dK/dV kernel also
+//    forms: seven tile products instead of five, traded for no atomics.
+// Q/dO (dK/dV kernel) and K/V (dQ kernel) tiles stream HBM -> LDS with
+// global_load_lds in the forward's XOR-swizzled layout, double-buffered.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "attn_device.h"
+#include "attn_internal.h"
+
+namespace attn {
+namespace {
+
+// One packed 16-bit pair -> two fp32 (exact).
+template <class Ty>
+__device__ __forceinline__ f32x2 unpack2(uint32_t u) {
+  if constexpr (std::is_same<Ty, TypeBF16>::value) {
+    return f32x2{__builtin_bit_cast(float, u << 16), __builtin_bit_cast(float, u & 0xffff0000u)};
+  } else {
+    return __builtin_convertvector(__builtin_bit_cast(f16x2, u), f32x2);
+  }
+}
+
+struct SeqRange {
+  int q_start, k_start, sq, sk;
+};
+
+__device__ __forceinline__ SeqRange seq_range(const BwdKernelParams& p, int b) {
+  SeqRange r{0, 0, p.seqlen_q, p.seqlen_k};
+  if (p.cu_seqlens_q != nullptr) {
+    r.q_start = p.cu_seqlens_q[b];
+    r.sq = p.cu_seqlens_q[b + 1] - r.q_start;
+    r.k_start = p.cu_seqlens_k[b];
+    r.sk = p.cu_seqlens_k[b + 1] - r.k_start;
+  }
+  return r;
+}
+
+// LSE in exp2 units, with a row that saw no key (LSE = -inf) mapped to +inf
+// so that every recomputed P of that row is exp2(-inf) = 0.
+__device__ __forceinline__ float lse_to_exp2(float l) { return l == -INFINITY ? INFINITY : l * kLog2e; }
+
+// ---------------------------------------------------------------- D = rowsum(dO * O)
+// D/8 consecutive lanes cover one (token, head) row, 8 elements each.
+template <class Ty, int D>
+__global__ void __launch_bounds__(256) bwd_dot_kernel(const BwdKernelParams p) {
+  constexpr int CHR = D / 8;
+  constexpr int RPB = 256 / CHR;
+  const int64_t nrows = (int64_t)p.total_q * p.heads_q;
+  const int64_t r = (int64_t)blockIdx.x * RPB + threadIdx.x / CHR;
+  const int c = threadIdx.x % CHR;
+  float acc = 0.0f;
+  int64_t didx = 0;
+  if (r < nrows) {
+    const int h = (int)(r % p.heads_q);
+    const int64_t tq = r / p.heads_q;  // dense: b * seqlen_q + row; varlen: packed row
+    int b = 0;
+    int64_t row = tq;
+    if (p.cu_seqlens_q == nullptr) {
+      b = (int)(tq / p.seqlen_q);
+      row = tq - (int64_t)b * p.seqlen_q;
+    }
+    const uint16_t* op = reinterpret_cast<const uint16_t*>(p.o) + b * p.o_batch + row * p.o_row +
+                         h * p.o_head + 8 * c;
+    const uint16_t* gp = reinterpret_cast<const uint16_t*>(p.dout) + b * p.do_batch + row * p.do_row +
+                         h * p.do_head + 8 * c;
+    const u32x4 ov = *reinterpret_cast<const u32x4*>(op);
+    const u32x4 gv = *reinterpret_cast<const u32x4*>(gp);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x2 a = unpack2<Ty>(ov[i]);
+      const f32x2 g = unpack2<Ty>(gv[i]);
+      acc = fmaf(a[0], g[0], acc);
+      acc = fmaf(a[1], g[1], acc);
+    }
+    didx = (int64_t)b * p.lse_batch + (int64_t)h * p.lse_head + row;
+  }
+#pragma unroll
+  for (int o = CHR / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+  if (r < nrows && c == 0) p.dsum[didx] = acc;
+}
+
+// HBM -> LDS copy of a tile of NR rows (one 16-byte chunk per lane per copy)
+// in the forward's swizzled layout; rows at or past `valid` re-read row
+// valid - 1 (their results are masked).
+template <int NR, int D, int NT>
+struct TileCopier {
+  static constexpr int CH = D / 8;
+  static constexpr int ROWB = D * 2;
+  static constexpr int LOADS = NR * CH / NT;
+  static constexpr int SWZ_MASK = CH < 16 ? CH - 1 : 15;
+  static_assert(LOADS >= 1 && (NR * CH) % NT == 0, "tile must split evenly over the workgroup");
+  int row[LOADS], col[LOADS];
+  __device__ __forceinline__ void init(int wave, int lane, int nw) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int u = (nw * i + wave) * 64 + lane;
+      const int r = u / CH, pos = u % CH;
+      row[i] = r;
+      col[i] = (pos ^ (chunk_swizzle(r & 15) & SWZ_MASK)) << 4;
+    }
+  }
+  // tb: byte address of tile row 0; rowb: bytes between rows; valid: rows that exist.
+  __device__ __forceinline__ void copy(const char* tb, int64_t rowb, int valid, char* tile, int wave,
+                                       int nw) const {
+    if (valid >= NR) {
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i)
+        dma16(tb + (uint32_t)(row[i] * (int)rowb + col[i]), tile + (nw * i + wave) * 1024);
+    } else {
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const int r = min(row[i], valid - 1);
+        dma16(tb + (int64_t)r * rowb + col[i], tile + (nw * i + wave) * 1024);
+      }
+    }
+  }
+};
+
+// Per-lane LDS byte offsets of the MFMA operands in the swizzled layout:
+// row reads (A operand of a 32-row slice, 8 consecutive dims per lane) and
+// transposing reads (A operand that contracts over 16 rows).
+template <int D>
+struct OperandOffsets {
+  static constexpr int CH = D / 8;
+  static constexpr int ROWB = D * 2;
+  static constexpr int DS = D / 16;
+  static constexpr int DT = D / 32;
+  static constexpr int SWZ_MASK = CH < 16 ? CH - 1 : 15;
+  int row_off[DS];
+  int tr_off[2][DT];
+  __device__ __forceinline__ void init(int lane) {
+    const int l32 = lane & 31, hl = lane >> 5;
+    const int sw = chunk_swizzle(lane & 15) & SWZ_MASK;
+#pragma unroll
+    for (int t = 0; t < DS; ++t) row_off[t] = l32 * ROWB + (((2 * t + hl) ^ sw) << 4);
+    const int cl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+    for (int r2 = 0; r2 < 2; ++r2) {
+      const int vrow = 4 * hl + 8 * r2 + ((lane & 15) >> 2);
+      const int x = cl ^ (chunk_swizzle(vrow) & SWZ_MASK);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) tr_off[r2][dt] = vrow * ROWB + (((4 * dt) ^ x) << 4) + ((lane & 1) << 3);
+    }
+  }
+};
+
+// A operand for the contraction over the 16 rows of slice ks of a tile,
+// 32 dims of block dt: two transposing reads.
+template <int D>
+__device__ __forceinline__ u32x4 tr_operand(const char* tile, const OperandOffsets<D>& o, int ks, int dt) {
+  constexpr int ROWB = D * 2;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + ks * 16 * ROWB + o.tr_off[0][dt]));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + ks * 16 * ROWB + o.tr_off[1][dt]));
+  const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
+  const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
+  return u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+}
+
+// Store a [D x 32] accumulator (lane = row of the output, registers = dims
+// 32 dt + 8 (r / 4) + 4 (lane / 32) + r % 4) times `mul` as 16-bit.
+template <class Ty, int D>
+__device__ __forceinline__ void store_rows(uint16_t* dst, const f32x16 (&acc)[D / 32], float mul, int hl) {
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d0 = 32 * dt + 8 * g4 + 4 * hl;
+      u32x2 w;
+      w[0] = Ty::pack(acc[dt][4 * g4 + 0] * mul, acc[dt][4 * g4 + 1] * mul);
+      w[1] = Ty::pack(acc[dt][4 * g4 + 2] * mul, acc[dt][4 * g4 + 3] * mul);
+      *reinterpret_cast<u32x2*>(dst + d0) = w;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- dK, dV
+template <class Ty, int D, bool SOFTCAP, bool ALIBI>
+__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+bwd_dkdv_kernel(const BwdKernelParams p) {
+  constexpr int NW = 4;
+  constexpr int NT = NW * 64;
+  constexpr int BQ = 64;            // queries per step
+  constexpr int QB = BQ / 32;       // 32-query MFMA blocks per step
+  constexpr int BN = 32 * NW;       // keys per workgroup
+  constexpr int ROWB = D * 2;
+  constexpr int TILEB = BQ * ROWB;
+  constexpr int DS = D / 16;
+  constexpr int DT = D / 32;
+  constexpr int KS = BQ / 16;       // 16-query contraction slices per step
+  using Copier = TileCopier<BQ, D, NT>;
+
+  __shared__ __attribute__((aligned(16))) char lds_q0[TILEB];
+  __shared__ __attribute__((aligned(16))) char lds_q1[TILEB];
+  __shared__ __attribute__((aligned(16))) char lds_g0[TILEB];
+  __shared__ __attribute__((aligned(16))) char lds_g1[TILEB];
+  __shared__ __attribute__((aligned(16))) float lds_lse[2][BQ];
+  __shared__ __attribute__((aligned(16))) float lds_dd[2][BQ];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hl = lane >> 5;
+
+  const int kvh = blockIdx.y, b = blockIdx.z;
+  const SeqRange sr = seq_range(p, b);
+  const int sq = sr.sq, sk = sr.sk, off = sk - sq;
+  const int n0 = blockIdx.x * BN;
+  if (n0 >= sk) return;
+  const int wl = p.window_left, wr = p.window_right;
+  const int G = p.group;
+
+  // This lane's key and the wave's key range.
+  const int wk_lo = n0 + 32 * wave;
+  const int key = wk_lo + l32;
+  const bool key_valid = key < sk;
+  const int keyc = key_valid ? key : sk - 1;
+  const bool wave_live = wk_lo < sk;
+  const int wk_hi = min(sk - 1, wk_lo + 31);
+
+  // K and V rows of this lane's key: B operands (8 consecutive dims per k-step).
+  u32x4 kf[DS], vf[DS];
+  {
+    const uint16_t* kp = reinterpret_cast<const uint16_t*>(p.k) + b * p.k_batch +
+                         (int64_t)(sr.k_start + keyc) * p.k_row + kvh * p.k_head;
+    const uint16_t* vp = reinterpret_cast<const uint16_t*>(p.v) + b * p.v_batch +
+                         (int64_t)(sr.k_start + keyc) * p.v_row + kvh * p.v_head;
+#pragma unroll
+    for (int t = 0; t < DS; ++t) {
+      kf[t] = *reinterpret_cast<const u32x4*>(kp + 16 * t + 8 * hl);
+      vf[t] = *reinterpret_cast<const u32x4*>(vp + 16 * t + 8 * hl);
+    }
+  }
+
+  // Queries that see some key of this workgroup.
+  const int wg_hi = min(sk - 1, n0 + BN - 1);
+  const int q_lo = (wr >= 0) ? max(0, n0 - off - wr) : 0;
+  const int q_hi = (wl >= 0) ? min(sq - 1, wg_hi - off + wl) : sq - 1;
+  const int qblk_lo = q_lo / BQ;
+  const int nsph = (q_hi >= q_lo) ? (q_hi / BQ + 1 - qblk_lo) : 0;  // steps per query head
+  const int n = G * nsph;
+
+  OperandOffsets<D> oo;
+  oo.init(lane);
+  Copier cp;
+  cp.init(wave, lane, NW);
+
+  f32x16 acc_dk[DT], acc_dv[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    acc_dk[dt] = f32x16{};
+    acc_dv[dt] = f32x16{};
+  }
+
+  const float c2 = p.scale_log2;
+  const float icap = p.inv_softcap;
+
+  auto head_of = [&](int r) __attribute__((always_inline)) { return kvh * G + r / nsph; };
+  auto q0_of = [&](int r) __attribute__((always_inline)) { return (qblk_lo + r % nsph) * BQ; };
+  // Copies of step r into stage st, and the (guarded) LSE / D loads of its queries.
+  float st_lse = 0.0f, st_dd = 0.0f;
+  auto issue = [&](int r, char* qt, char* gt) __attribute__((always_inline)) {
+    const int h = head_of(r), q0 = q0_of(r);
+    const char* qb = reinterpret_cast<const char*>(p.q) +
+                     2 * (b * p.q_batch + (int64_t)(sr.q_start + q0) * p.q_row + h * p.q_head);
+    const char* gb = reinterpret_cast<const char*>(p.dout) +
+                     2 * (b * p.do_batch + (int64_t)(sr.q_start + q0) * p.do_row + h * p.do_head);
+    cp.copy(qb, 2 * p.q_row, sq - q0, qt, wave, NW);
+    cp.copy(gb, 2 * p.do_row, sq - q0, gt, wave, NW);
+    if (tid < BQ) {
+      const int q = q0 + tid;
+      const int64_t li = b * p.lse_batch + (int64_t)h * p.lse_head + sr.q_start + q;
+      st_lse = q < sq ? p.lse[li] : -INFINITY;
+      st_dd = q < sq ? p.dsum[li] : 0.0f;
+    }
+  };
+  auto stage_rows = [&](int st) __attribute__((always_inline)) {
+    if (tid < BQ) {
+      lds_lse[st][tid] = lse_to_exp2(st_lse);
+      lds_dd[st][tid] = st_dd;
+    }
+  };
+
+  auto step = [&](auto stc, int r) __attribute__((always_inline)) {
+    constexpr int ST = decltype(stc)::value;
+    char* q_cur = ST == 0 ? lds_q0 : lds_q1;
+    char* g_cur = ST == 0 ? lds_g0 : lds_g1;
+    if (r + 1 < n) issue(r + 1, ST == 0 ? lds_q1 : lds_q0, ST == 0 ? lds_g1 : lds_g0);
+    const int h = head_of(r), q0 = q0_of(r);
+    const int qv_hi = min(sq - 1, q0 + BQ - 1);
+    const bool sees = wave_live && (wr < 0 || wk_lo <= qv_hi + off + wr) && (wl < 0 || wk_hi >= q0 + off - wl);
+    if (sees) {
+      f32x16 s[QB], dp[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        s[qb] = f32x16{};
+        dp[qb] = f32x16{};
+      }
+#pragma unroll
+      for (int t = 0; t < DS; ++t) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(q_cur + qb * 32 * ROWB + oo.row_off[t]);
+          s[qb] = Ty::mfma(a, kf[t], s[qb]);
+          const u32x4 a2 = *reinterpret_cast<const u32x4*>(g_cur + qb * 32 * ROWB + oo.row_off[t]);
+          dp[qb] = Ty::mfma(a2, vf[t], dp[qb]);
+        }
+      }
+      float slope = 0.0f;
+      if constexpr (ALIBI) slope = p.alibi[b * p.alibi_bstride + h] * p.alibi_inv_scale;
+      // Every (query, key) pair of the step and wave visible: no mask work.
+      const bool full = q0 + BQ - 1 < sq && wk_lo + 31 < sk && (wr < 0 || wk_lo + 31 <= q0 + off + wr) &&
+                        (wl < 0 || wk_lo >= q0 + BQ - 1 + off - wl);
+      uint32_t pp[QB][8], ps[QB][8];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int qo = 32 * qb + 8 * g4 + 4 * hl;  // first of this lane's 4 consecutive queries
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lds_lse[ST][qo]);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&lds_dd[ST][qo]);
+          float pv[4], dv[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int rr = 4 * g4 + i;
+            const int q = q0 + qo + i;
+            float x = s[qb][rr];
+            float gcap = 1.0f;
+            if constexpr (SOFTCAP) {
+              x = transform_score<true>(x, p.softcap_pre, p.softcap);
+              const float th = x * icap;
+              gcap = fmaf(-th, th, 1.0f);
+            }
+            if constexpr (ALIBI) x = fmaf(-slope, fabsf((float)(q + off - key)), x);
+            if (!full) {
+              const bool vis = q < sq && key < sk && (wr < 0 || key <= q + off + wr) && (wl < 0 || key >= q + off - wl);
+              if (!vis) x = -INFINITY;
+            }
+            const float pr = fast_exp2(fmaf(x, c2, -l4[i]));
+            pv[i] = pr;
+            float d = pr * (dp[qb][rr] - d4[i]);
+            if constexpr (SOFTCAP) d *= gcap;
+            dv[i] = d;
+          }
+          pp[qb][2 * g4] = Ty::pack(pv[0], pv[1]);
+          pp[qb][2 * g4 + 1] = Ty::pack(pv[2], pv[3]);
+          ps[qb][2 * g4] = Ty::pack(dv[0], dv[1]);
+          ps[qb][2 * g4 + 1] = Ty::pack(dv[2], dv[3]);
+        }
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS, contracting over the step's queries
+      // in the order the score registers hold them.
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 bp = {pp[ks >> 1][4 * (ks & 1) + 0], pp[ks >> 1][4 * (ks & 1) + 1],
+                          pp[ks >> 1][4 * (ks & 1) + 2], pp[ks >> 1][4 * (ks & 1) + 3]};
+        const u32x4 bs = {ps[ks >> 1][4 * (ks & 1) + 0], ps[ks >> 1][4 * (ks & 1) + 1],
+                          ps[ks >> 1][4 * (ks & 1) + 2], ps[ks >> 1][4 * (ks & 1) + 3]};
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          acc_dv[dt] = Ty::mfma(tr_operand<D>(g_cur, oo, ks, dt), bp, acc_dv[dt]);
+          acc_dk[dt] = Ty::mfma(tr_operand<D>(q_cur, oo, ks, dt), bs, acc_dk[dt]);
+        }
+      }
+    }
+    wait_vmem();
+    if (r + 1 < n) stage_rows(ST ^ 1);
+    __syncthreads();
+  };
+
+  if (n > 0) {
+    issue(0, lds_q0, lds_g0);
+    wait_vmem();
+    stage_rows(0);
+    __syncthreads();
+    int r = 0;
+    for (; r + 2 <= n; r += 2) {
+      step(std::integral_constant<int, 0>{}, r);
+      step(std::integral_constant<int, 1>{}, r + 1);
+    }
+    if (r < n) step(std::integral_constant<int, 0>{}, r);
+  }
+
+  if (key_valid) {
+    uint16_t* dkp = reinterpret_cast<uint16_t*>(p.dk) + b * p.dk_batch + (int64_t)(sr.k_start + key) * p.dk_row +
+                    kvh * p.dk_head;
+    uint16_t* dvp = reinterpret_cast<uint16_t*>(p.dv) + b * p.dv_batch + (int64_t)(sr.k_start + key) * p.dv_row +
+                    kvh * p.dv_head;
+    store_rows<Ty, D>(dkp, acc_dk, p.scale, hl);
+    store_rows<Ty, D>(dvp, acc_dv, 1.0f, hl);
+  }
+}
+
+// ---------------------------------------------------------------- dQ
+template <class Ty, int D, bool SOFTCAP, bool ALIBI>
+__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+bwd_dq_kernel(const BwdKernelParams p) {
+  constexpr int NW = 4;
+  constexpr int NT = NW * 64;
+  constexpr int BK = 64;            // keys per step
+  constexpr int BQ = 32 * NW;       // queries per workgroup
+  constexpr int ROWB = D * 2;
+  constexpr int TILEB = BK * ROWB;
+  constexpr int KT = BK / 32;
+  constexpr int DS = D / 16;
+  constexpr int DT = D / 32;
+  constexpr int KS = BK / 16;
+  using Copier = TileCopier<BK, D, NT>;
+
+  __shared__ __attribute__((aligned(16))) char lds_k0[TILEB];
+  __shared__ __attribute__((aligned(16))) char lds_k1[TILEB];
+  __shared__ __attribute__((aligned(16))) char lds_v0[TILEB];
+  __shared__ __attribute__((aligned(16))) char lds_v1[TILEB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hl = lane >> 5;
+
+  const int head = blockIdx.y, b = blockIdx.z;
+  const SeqRange sr = seq_range(p, b);
+  const int sq = sr.sq, sk = sr.sk, off = sk - sq;
+  const int m0 = ((int)gridDim.x - 1 - (int)blockIdx.x) * BQ;  // longest (causal) tiles first
+  if (m0 >= sq) return;
+  const int kvh = head / p.group;
+  const int wl = p.window_left, wr = p.window_right;
+
+  const int row = m0 + 32 * wave + l32;
+  const bool q_valid = row < sq;
+  const int rowc = q_valid ? row : sq - 1;
+  const int kmin = (wl >= 0) ? row + off - wl : -0x40000000;
+  const int kmax = min(sk - 1, (wr >= 0) ? row + off + wr : 0x3fffffff);
+  const int wrow_lo = m0 + 32 * wave;
+  const int wrow_hi = min(sq - 1, wrow_lo + 31);
+  const bool wave_live = wrow_lo < sq;
+  const int wk_lo = (wl >= 0) ? wrow_lo + off - wl : -0x40000000;
+  const int wk_hi = min(sk - 1, (wr >= 0) ? wrow_hi + off + wr : 0x3fffffff);
+  const int full_lo = (wl >= 0) ? wrow_hi + off - wl : -0x40000000;
+  const int full_hi = min(sk - 1, (wr >= 0) ? wrow_lo + off + wr : 0x3fffffff);
+
+  // KV steps of the tile.
+  const int row_hi = min(sq - 1, m0 + BQ - 1);
+  const int n_lo = (wl >= 0) ? max(0, m0 + off - wl) : 0;
+  const int n_hi = (wr >= 0) ? min(sk, row_hi + off + wr + 1) : sk;
+  const int blk_lo = n_lo / BK;
+  const int n = (n_hi > n_lo) ? (n_hi + BK - 1) / BK - blk_lo : 0;
+
+  // Q and dO rows of this lane's query: B operands.
+  u32x4 qf[DS], gf[DS];
+  {
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q) + b * p.q_batch +
+                         (int64_t)(sr.q_start + rowc) * p.q_row + head * p.q_head;
+    const uint16_t* gp = reinterpret_cast<const uint16_t*>(p.dout) + b * p.do_batch +
+                         (int64_t)(sr.q_start + rowc) * p.do_row + head * p.do_head;
+#pragma unroll
+    for (int t = 0; t < DS; ++t) {
+      qf[t] = *reinterpret_cast<const u32x4*>(qp + 16 * t + 8 * hl);
+      gf[t] = *reinterpret_cast<const u32x4*>(gp + 16 * t + 8 * hl);
+    }
+  }
+  const int64_t li = b * p.lse_batch + (int64_t)head * p.lse_head + sr.q_start + rowc;
+  const float lse2 = q_valid ? lse_to_exp2(p.lse[li]) : INFINITY;
+  const float dd = q_valid ? p.dsum[li] : 0.0f;
+  float slope = 0.0f;
+  if constexpr (ALIBI) slope = p.alibi[b * p.alibi_bstride + head] * p.alibi_inv_scale;
+
+  OperandOffsets<D> oo;
+  oo.init(lane);
+  Copier cp;
+  cp.init(wave, lane, NW);
+  const char* kbase = reinterpret_cast<const char*>(p.k) +
+                      2 * (b * p.k_batch + (int64_t)sr.k_start * p.k_row + kvh * p.k_head);
+  const char* vbase = reinterpret_cast<const char*>(p.v) +
+                      2 * (b * p.v_batch + (int64_t)sr.k_start * p.v_row + kvh * p.v_head);
+  auto issue = [&](int blk, char* kt, char* vt) __attribute__((always_inline)) {
+    const int j0 = blk * BK;
+    cp.copy(kbase + (int64_t)j0 * 2 * p.k_row, 2 * p.k_row, sk - j0, kt, wave, NW);
+    cp.copy(vbase + (int64_t)j0 * 2 * p.v_row, 2 * p.v_row, sk - j0, vt, wave, NW);
+  };
+
+  f32x16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
+  const float c2 = p.scale_log2;
+  const float icap = p.inv_softcap;
+
+  auto step = [&](auto stc, int r) __attribute__((always_inline)) {
+    constexpr int ST = decltype(stc)::value;
+    char* k_cur = ST == 0 ? lds_k0 : lds_k1;
+    char* v_cur = ST == 0 ? lds_v0 : lds_v1;
+    const int blk = blk_lo + r;
+    if (r + 1 < n) issue(blk + 1, ST == 0 ? lds_k1 : lds_k0, ST == 0 ? lds_v1 : lds_v0);
+    const int j0 = blk * BK;
+    if (wave_live && j0 <= wk_hi && j0 + BK - 1 >= wk_lo) {
+      f32x16 s[KT], dp[KT];
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        s[kt] = f32x16{};
+        dp[kt] = f32x16{};
+      }
+#pragma unroll
+      for (int t = 0; t < DS; ++t) {
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(k_cur + kt * 32 * ROWB + oo.row_off[t]);
+          s[kt] = Ty::mfma(a, qf[t], s[kt]);
+          const u32x4 a2 = *reinterpret_cast<const u32x4*>(v_cur + kt * 32 * ROWB + oo.row_off[t]);
+          dp[kt] = Ty::mfma(a2, gf[t], dp[kt]);
+        }
+      }
+      const bool full = j0 >= full_lo && j0 + BK - 1 <= full_hi;
+      uint32_t ps[KT][8];
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+        for (int r2 = 0; r2 < 16; r2 += 2) {
+          float dv[2];
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const int rr = r2 + i;
+            const int kk = j0 + 32 * kt + 8 * (rr >> 2) + 4 * hl + (rr & 3);
+            float x = s[kt][rr];
+            float gcap = 1.0f;
+            if constexpr (SOFTCAP) {
+              x = transform_score<true>(x, p.softcap_pre, p.softcap);
+              const float th = x * icap;
+              gcap = fmaf(-th, th, 1.0f);
+            }
+            if constexpr (ALIBI) x = fmaf(-slope, fabsf((float)(row + off - kk)), x);
+            if (!full && (kk < kmin || kk > kmax)) x = -INFINITY;
+            const float pr = fast_exp2(fmaf(x, c2, -lse2));
+            float d = pr * (dp[kt][rr] - dd);
+            if constexpr (SOFTCAP) d *= gcap;
+            dv[i] = d;
+          }
+          ps[kt][r2 >> 1] = Ty::pack(dv[0], dv[1]);
+        }
+      }
+      // dQ^T += K^T dS^T, contracting over the step's keys in register order.
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 bs = {ps[ks >> 1][4 * (ks & 1) + 0], ps[ks >> 1][4 * (ks & 1) + 1],
+                          ps[ks >> 1][4 * (ks & 1) + 2], ps[ks >> 1][4 * (ks & 1) + 3]};
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) acc[dt] = Ty::mfma(tr_operand<D>(k_cur, oo, ks, dt), bs, acc[dt]);
+      }
+    }
+    wait_vmem();
+    __syncthreads();
+  };
+
+  if (n > 0) {
+    issue(blk_lo, lds_k0, lds_v0);
+    wait_vmem();
+    __syncthreads();
+    int r = 0;
+    for (; r + 2 <= n; r += 2) {
+      step(std::integral_constant<int, 0>{}, r);
+      step(std::integral_constant<int, 1>{}, r + 1);
+    }
+    if (r < n) step(std::integral_constant<int, 0>{}, r);
+  }
+
+  if (q_valid) {
+    uint16_t* dqp = reinterpret_cast<uint16_t*>(p.dq) + b * p.dq_batch + (int64_t)(sr.q_start + row) * p.dq_row +
+                    head * p.dq_head;
+    store_rows<Ty, D>(dqp, acc, p.scale, hl);
+  }
+}
+
+// D first (both gradient kernels read it), then dK/dV, then dQ; a kernel
+// whose grid would be empty (no queries, or no keys) is not launched.
+template <class Ty, int D, bool SOFTCAP, bool ALIBI>
+hipError_t launch_bwd_t(const BwdKernelParams& p, hipStream_t stream) {
+  if (p.total_q > 0 && p.seqlen_q > 0) {
+    constexpr int RPB = 256 / (D / 8);
+    const int64_t rows = (int64_t)p.total_q * p.heads_q;
+    const dim3 grid((unsigned)((rows + RPB - 1) / RPB));
+    hipLaunchKernelGGL((bwd_dot_kernel<Ty, D>), grid, dim3(256), 0, stream, p);
+  }
+  if (p.seqlen_k > 0) {
+    const dim3 grid((unsigned)((p.seqlen_k + 127) / 128), p.heads_kv, p.batch);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<Ty, D, SOFTCAP, ALIBI>), grid, dim3(256), 0, stream, p);
+  }
+  if (p.seqlen_q > 0) {
+    const dim3 grid((unsigned)((p.seqlen_q + 127) / 128), p.heads_q, p.batch);
+    hipLaunchKernelGGL((bwd_dq_kernel<Ty, D, SOFTCAP, ALIBI>), grid, dim3(256), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+template <class Ty, int D>
+hipError_t launch_bwd_d(const BwdKernelParams& p, hipStream_t stream) {
+  const bool cap = p.softcap > 0.0f, al = p.alibi != nullptr;
+  if (cap) return al ? launch_bwd_t<Ty, D, true, true>(p, stream) : launch_bwd_t<Ty, D, true, false>(p, stream);
+  return al ? launch_bwd_t<Ty, D, false, true>(p, stream) : launch_bwd_t<Ty, D, false, false>(p, stream);
+}
+
+template <class Ty>
+hipError_t launch_bwd_ty(const BwdKernelParams& p, int head_dim, hipStream_t stream) {
+  if (head_dim == 64) return launch_bwd_d<Ty, 64>(p, stream);
+  if (head_dim == 128) return launch_bwd_d<Ty, 128>(p, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdKernelParams& p, int dtype, int head_dim, hipStream_t stream) {
+  if (p.batch <= 0 || p.heads_q <= 0) return hipSuccess;
+  return dtype == 1 ? launch_bwd_ty<TypeBF16>(p, head_dim, stream) : launch_bwd_ty<TypeF16>(p, head_dim, stream);
+}
+
+}  // namespace attn

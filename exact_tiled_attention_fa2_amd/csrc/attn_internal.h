@@ -1,5 +1,5 @@
 // Internal interface between the host C-ABI layer (attn_api.cpp) and the
-// HIP kernels (attn_kernels.hip).  Not part of the public ABI.
+// HIP kernels (attn_kernels.hip, attn_bwd.hip).  Not part of the public ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -54,10 +54,49 @@ struct CombineParams {
   int32_t batch, seqlen_q, heads_q, num_splits;
 };
 
+// Everything the backward kernels need, resolved on the host.  Strides are in
+// elements; dsum (D = rowsum(dO * O), fp32) and lse share one indexing:
+// b * lse_batch + h * lse_head + (q_start + row).
+struct BwdKernelParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  float* dsum;          // workspace, written by the dot kernel
+  void* dq;
+  void* dk;
+  void* dv;
+  const int32_t* cu_seqlens_q;  // varlen prefix sums [B+1] (null: dense)
+  const int32_t* cu_seqlens_k;
+  int64_t q_batch, q_row, q_head;
+  int64_t k_batch, k_row, k_head;
+  int64_t v_batch, v_row, v_head;
+  int64_t o_batch, o_row, o_head;
+  int64_t do_batch, do_row, do_head;
+  int64_t dq_batch, dq_row, dq_head;
+  int64_t dk_batch, dk_row, dk_head;
+  int64_t dv_batch, dv_row, dv_head;
+  int64_t lse_batch, lse_head;
+  int32_t batch, seqlen_q, seqlen_k, heads_q, heads_kv, group;
+  int32_t total_q;       // rows of the dot kernel's sweep: batch * seqlen_q (dense) or total_q (varlen)
+  int32_t window_left, window_right;  // causal folded into window_right
+  float scale;           // softmax scale (dQ, dK = scale * sum of dS products)
+  float scale_log2;      // raw (or capped) score -> exp2 argument, as in the forward
+  float softcap_pre;     // scale / softcap
+  float softcap;         // 0: off
+  float inv_softcap;     // 1 / softcap
+  const float* alibi;    // ALiBi slopes (null: off)
+  int64_t alibi_bstride;
+  float alibi_inv_scale; // bias in the units of the (capped) score
+};
+
 constexpr int kBlockM = 128;  // nominal query rows per workgroup (split-count heuristic)
 
 // Host-side launchers (return a hipError_t).
 hipError_t launch_fwd(const FwdKernelParams& p, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, int dtype, int head_dim, hipStream_t stream);
+hipError_t launch_bwd(const BwdKernelParams& p, int dtype, int head_dim, hipStream_t stream);
 
 }  // namespace attn

@@ -1,6 +1,6 @@
 /*
- * attn_mi355x.h -- C ABI of the exact tiled attention forward library for
- * AMD Instinct MI355X (gfx950).
+ * attn_mi355x.h -- C ABI of the exact tiled attention library (forward and
+ * backward) for AMD Instinct MI355X (gfx950).
  *
  * The library computes exact attention forward
  *
@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define ATTN_VERSION 120
+#define ATTN_VERSION 130
 
 enum attn_status {
   ATTN_OK = 0,
@@ -221,6 +221,93 @@ size_t attn_kvcache_workspace_bytes(int32_t batch, int32_t seqlen_q, int32_t hea
                                     int32_t head_dim, int32_t num_splits);
 int attn_fwd_kvcache(const attn_kvcache_args* args, void* workspace, size_t workspace_bytes,
                      void* stream);
+
+/*
+ * attn_bwd -- gradients of attn_fwd: dQ, dK, dV for a loss whose gradient
+ * with respect to O is dO (the backward kernels the pages list and check
+ * against an fp32 reference: "v1.7 / flash_attn 2.9.2.post1" section 4.4).
+ * With P recomputed from the scores and the forward's LSE:
+ *     dV = P^T dO,  dT = P (dO V^T - D),  D_i = <dO_i, O_i>,
+ *     dQ = scale (dT g) K,  dK = scale (dT g)^T Q,
+ * g = 1 - (t / softcap)^2 with softcap (t the capped score), else 1; the
+ * ALiBi bias adds no term.  Under GQA dK, dV of a KV head sum over its query
+ * heads.
+ *   q, o, dout [batch, seqlen_q, heads_q, head_dim]
+ *   k, v [batch, seqlen_k, heads_kv, head_dim]
+ *   lse [batch, heads_q, seqlen_q] contiguous fp32: the LSE attn_fwd returned
+ *     for the same inputs and options (a row with LSE = -inf gets dQ = 0 and
+ *     adds nothing to dK, dV).
+ *   dq like q; dk, dv like k (written, 16-bit).
+ *   opts as for attn_fwd; rescale_threshold is not used (the backward does
+ *     not run the online softmax).
+ *   workspace: attn_bwd_workspace_bytes() bytes (fp32 D per query row).
+ *   head_dim 64 or 128 (256: ATTN_E_UNSUPPORTED).
+ * No atomics: every output element has one owner, so results are
+ * deterministic.
+ */
+typedef struct attn_bwd_args {
+  int32_t dtype;
+  int32_t batch, seqlen_q, seqlen_k, heads_q, heads_kv, head_dim;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  int64_t q_batch_stride, q_row_stride, q_head_stride;
+  int64_t k_batch_stride, k_row_stride, k_head_stride;
+  int64_t v_batch_stride, v_row_stride, v_head_stride;
+  int64_t o_batch_stride, o_row_stride, o_head_stride;
+  int64_t do_batch_stride, do_row_stride, do_head_stride;
+  int64_t dq_batch_stride, dq_row_stride, dq_head_stride;
+  int64_t dk_batch_stride, dk_row_stride, dk_head_stride;
+  int64_t dv_batch_stride, dv_row_stride, dv_head_stride;
+  attn_softmax_opts opts;
+} attn_bwd_args;
+
+size_t attn_bwd_workspace_bytes(int32_t batch, int32_t seqlen_q, int32_t heads_q);
+int attn_bwd(const attn_bwd_args* args, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_bwd_varlen -- gradients of attn_fwd_varlen (the pages check the
+ * varlen backward for finite gradients, "v1.7 / flash_attn 2.9.2.post1"
+ * section 4.4).  Layouts as in attn_fwd_varlen: q, o, dout, dq
+ * [total_q, heads_q, head_dim]; k, v, dk, dv [total_k, heads_kv, head_dim];
+ * lse [heads_q, total_q] fp32 from attn_fwd_varlen; cu_seqlens_q/_k device
+ * int32 [batch + 1]; max_seqlen_q/_k host upper bounds.  workspace:
+ * attn_bwd_varlen_workspace_bytes() bytes.
+ */
+typedef struct attn_bwd_varlen_args {
+  int32_t dtype;
+  int32_t batch, total_q, total_k, max_seqlen_q, max_seqlen_k, heads_q, heads_kv, head_dim;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  const int32_t* cu_seqlens_q;
+  const int32_t* cu_seqlens_k;
+  int64_t q_row_stride, q_head_stride;
+  int64_t k_row_stride, k_head_stride;
+  int64_t v_row_stride, v_head_stride;
+  int64_t o_row_stride, o_head_stride;
+  int64_t do_row_stride, do_head_stride;
+  int64_t dq_row_stride, dq_head_stride;
+  int64_t dk_row_stride, dk_head_stride;
+  int64_t dv_row_stride, dv_head_stride;
+  attn_softmax_opts opts;
+} attn_bwd_varlen_args;
+
+size_t attn_bwd_varlen_workspace_bytes(int32_t total_q, int32_t heads_q);
+int attn_bwd_varlen(const attn_bwd_varlen_args* args, void* workspace, size_t workspace_bytes,
+                    void* stream);
 
 /* Human-readable text of a status code (static storage). */
 const char* attn_status_string(int status);

@@ -34,7 +34,7 @@ def _declared_functions():
 def test_library_exports_every_declared_function():
     h = _lib()
     names = _declared_functions()
-    assert {"attn_fwd", "attn_fwd_varlen", "attn_fwd_kvcache"} <= set(names)
+    assert {"attn_fwd", "attn_fwd_varlen", "attn_fwd_kvcache", "attn_bwd", "attn_bwd_varlen"} <= set(names)
     for n in names:
         assert hasattr(h, n), f"{n} declared in the header but not exported"
     out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True,
@@ -45,7 +45,7 @@ def test_library_exports_every_declared_function():
 
 def test_version_and_status_strings():
     h = _lib()
-    assert h.attn_version() == 120
+    assert h.attn_version() == 130
     for code in range(-9, 1):
         assert binding.status_string(code)
     assert binding.status_string(-1234) == "unknown status"
@@ -61,6 +61,8 @@ int main(void) {
   printf("attn_fwd_args size %zu\n", sizeof(attn_fwd_args));
   printf("attn_varlen_args size %zu\n", sizeof(attn_varlen_args));
   printf("attn_kvcache_args size %zu\n", sizeof(attn_kvcache_args));
+  printf("attn_bwd_args size %zu\n", sizeof(attn_bwd_args));
+  printf("attn_bwd_varlen_args size %zu\n", sizeof(attn_bwd_varlen_args));
   %FIELDS%
   return 0;
 }
@@ -69,7 +71,8 @@ int main(void) {
 
 def test_struct_layouts_match_binding():
     structs = {"attn_softmax_opts": binding.SoftmaxOpts, "attn_fwd_args": binding.FwdArgs,
-               "attn_varlen_args": binding.VarlenArgs, "attn_kvcache_args": binding.KvcacheArgs}
+               "attn_varlen_args": binding.VarlenArgs, "attn_kvcache_args": binding.KvcacheArgs,
+               "attn_bwd_args": binding.BwdArgs, "attn_bwd_varlen_args": binding.BwdVarlenArgs}
     fields = "\n".join(f"F({c}, {f})" for c, py in structs.items() for f, _ in py._fields_)
     with tempfile.TemporaryDirectory() as d:
         src = os.path.join(d, "layout.c")
@@ -226,3 +229,71 @@ def test_alibi_validation():
     a.opts.alibi_batch_stride = -1
     assert h.attn_fwd(ctypes.byref(a), None) == binding.ATTN_E_ARG
 
+
+
+def _bwd_args(**over):
+    """A valid dense backward argument block with fake (aligned) device pointers."""
+    b, sq, sk, hq, hkv, d = 2, 64, 64, 4, 2, 128
+    a = binding.BwdArgs()
+    vals = dict(dtype=1, batch=b, seqlen_q=sq, seqlen_k=sk, heads_q=hq, heads_kv=hkv, head_dim=d,
+                q=16, k=16, v=16, o=16, dout=16, lse=16, dq=16, dk=16, dv=16)
+    for t, h in (("q", hq), ("o", hq), ("do", hq), ("dq", hq), ("k", hkv), ("v", hkv), ("dk", hkv), ("dv", hkv)):
+        s = sq if h == hq else sk
+        vals[f"{t}_batch_stride"] = s * h * d
+        vals[f"{t}_row_stride"] = h * d
+        vals[f"{t}_head_stride"] = d
+    opts = dict(softmax_scale=0.0, causal=1, window_left=-1, window_right=-1, softcap=0.0,
+                rescale_threshold=-1.0)
+    for k, v in over.items():
+        if k in opts:
+            opts[k] = v
+        else:
+            vals[k] = v
+    for k, v in vals.items():
+        setattr(a, k, v)
+    a.opts = binding.SoftmaxOpts(**opts)
+    return a
+
+
+_BAD_BWD = [
+    (dict(head_dim=256), binding.ATTN_E_UNSUPPORTED),
+    (dict(dtype=3), binding.ATTN_E_UNSUPPORTED),
+    (dict(heads_q=3), binding.ATTN_E_HEADS),
+    (dict(seqlen_q=-1), binding.ATTN_E_SHAPE),
+    (dict(dout=None), binding.ATTN_E_NULL),
+    (dict(lse=None), binding.ATTN_E_NULL),
+    (dict(dk=None), binding.ATTN_E_NULL),
+    (dict(dq=24), binding.ATTN_E_ALIGN),
+    (dict(dv_row_stride=2 * 128 + 2), binding.ATTN_E_ALIGN),
+    (dict(lse=18), binding.ATTN_E_ALIGN),
+    (dict(window_left=-3), binding.ATTN_E_WINDOW),
+    (dict(softcap=-2.0), binding.ATTN_E_ARG),
+]
+
+
+@pytest.mark.parametrize("over,code", _BAD_BWD, ids=[str(o) for o, _ in _BAD_BWD])
+def test_attn_bwd_rejects_bad_arguments(over, code):
+    h = _lib()
+    need = binding.attn_bwd_workspace_bytes(2, 64, 4)
+    assert h.attn_bwd(ctypes.byref(_bwd_args(**over)), 16, need, None) == code
+
+
+def test_bwd_workspace_and_empty_problems():
+    h = _lib()
+    need = binding.attn_bwd_workspace_bytes(2, 64, 4)
+    assert need == 2 * 64 * 4 * 4
+    assert binding.attn_bwd_workspace_bytes(0, 64, 4) == 0
+    assert binding.attn_bwd_varlen_workspace_bytes(1000, 8) == 1000 * 8 * 4
+    a = _bwd_args()
+    assert h.attn_bwd(ctypes.byref(a), None, 0, None) == binding.ATTN_E_WORKSPACE
+    assert h.attn_bwd(ctypes.byref(a), 16, need - 4, None) == binding.ATTN_E_WORKSPACE
+    assert h.attn_bwd(ctypes.byref(a), 24, need, None) == binding.ATTN_E_WORKSPACE   # misaligned
+    assert h.attn_bwd(None, None, 0, None) == binding.ATTN_E_NULL
+    assert h.attn_bwd_varlen(None, None, 0, None) == binding.ATTN_E_NULL
+    empty = _bwd_args(batch=0, q=None, k=None, v=None, o=None, dout=None, lse=None, dq=None, dk=None, dv=None)
+    assert h.attn_bwd(ctypes.byref(empty), None, 0, None) == 0
+    va = binding.BwdVarlenArgs(1, 3, 0, 0, 0, 0, 4, 4, 64)
+    va.opts = binding.SoftmaxOpts(0.0, 0, -1, -1, 0.0, -1.0)
+    assert h.attn_bwd_varlen(ctypes.byref(va), None, 0, None) == 0
+    va.total_q, va.total_k, va.max_seqlen_q, va.max_seqlen_k = 10, 10, 5, 5
+    assert h.attn_bwd_varlen(ctypes.byref(va), None, 0, None) == binding.ATTN_E_NULL  # cu_seqlens

@@ -1,0 +1,159 @@
+"""GPU parity of the backward (attn_bwd, attn_bwd_varlen) against the fp64 CPU oracle.
+
+The HIP path runs its own forward (attn_fwd) for O and LSE and then its
+backward; the oracle computes the gradients from Q, K, V and dO alone.  Every
+input is seeded and synthetic.  Gates (rel_Linf = max |g - g_ref| / max
+|g_ref| per gradient tensor, cosine over the tensor) are derived from the
+arithmetic: P and dS enter the MFMAs rounded to the 16-bit input type, O is
+16-bit in D = rowsum(dO * O), and the gradients are stored in 16 bits -- a
+few roundings of unit roundoff u (2^-8 bf16, 2^-11 fp16) per element, so
+rel_Linf <= 10 u and 1 - cosine <= 1e-4 (bf16) / 1e-5 (fp16).  A gradient
+whose exact value is zero everywhere (window (0, 0): P = 1 on the diagonal
+makes dT = P (dP - D) vanish) is held to an absolute bound instead.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import attn_workloads as W
+import oracle
+from gpu_common import gpu_required, np64
+
+pytestmark = pytest.mark.gpu
+
+# rel_Linf and cosine gates per dtype (see the module docstring).
+BWD_GATES = {"fp16": (5e-3, 0.99999), "bf16": (4e-2, 0.9999)}
+ZERO_REF_ABS = 1e-4   # |g| bound where the exact gradient is 0 (inputs are O(1))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    gpu_required()
+
+
+def _eng():
+    import exact_tiled_attention_fa2_amd as eng
+    return eng
+
+
+def grad_check(got, ref, dtype, what):
+    got = np.asarray(got, dtype=np.float64)
+    if np.max(np.abs(ref)) < 1e-12:
+        mx = float(np.max(np.abs(got)))
+        print(f"[parity] {what}: exact gradient is 0, max |g| = {mx:.3e}", flush=True)
+        assert np.all(np.isfinite(got)) and mx <= ZERO_REF_ABS, f"{what}: {mx}"
+        return
+    rl = oracle.rel_linf(got, ref)
+    cs = oracle.cosine(got, ref)
+    fin = bool(np.all(np.isfinite(got)))
+    print(f"[parity] {what}: rel_linf={rl:.3e} cosine={cs:.7f} max_abs={np.max(np.abs(got - ref)):.3e}",
+          flush=True)
+    rel_gate, cos_gate = BWD_GATES[dtype]
+    assert fin, f"{what}: non-finite gradient"
+    assert rl <= rel_gate and cs >= cos_gate, f"{what}: rel_linf {rl} cosine {cs}"
+
+
+def _dout(seed, shape, dtype):
+    g = torch.Generator(device="cuda").manual_seed(seed + 7777)
+    return W.randn16(shape, dtype, g, device="cuda")
+
+
+def _opts_np(kw):
+    out = dict(kw)
+    if out.get("alibi_slopes") is not None:
+        out["alibi_slopes"] = out["alibi_slopes"].cpu().numpy().astype(np.float64)
+    return out
+
+
+DENSE = [
+    # seed, b, sq, sk, hq, hkv, d, dtype, options
+    (81, 1, 200, 200, 4, 4, 128, "fp16", dict(causal=True)),
+    (82, 2, 300, 300, 8, 2, 128, "bf16", dict(causal=True)),
+    (83, 1, 130, 333, 4, 2, 64, "fp16", dict(causal=False)),
+    (84, 1, 257, 257, 4, 1, 128, "bf16", dict(causal=True, window=(64, 0), softcap=30.0)),
+    (85, 2, 190, 190, 4, 4, 64, "fp16", dict(causal=True, alibi=True)),
+    (86, 1, 300, 100, 2, 2, 128, "bf16", dict(causal=True)),          # rows with no key
+    (87, 1, 64, 64, 2, 1, 128, "fp16", dict(causal=False, window=(0, 0))),
+    (88, 2, 97, 161, 6, 3, 64, "bf16", dict(causal=False, softcap=5.0, alibi=True)),
+]
+
+
+@pytest.mark.parametrize("case", DENSE, ids=[f"s{c[0]}" for c in DENSE])
+def test_bwd_dense(case):
+    seed, b, sq, sk, hq, hkv, d, dtype, kw = case
+    kw = dict(kw)
+    print(f"[case] bwd dense seed={seed} b={b} sq={sq} sk={sk} hq={hq} hkv={hkv} d={d} {dtype} {kw}", flush=True)
+    if kw.pop("alibi", False):
+        kw["alibi_slopes"] = W.alibi_slopes(hq, b, device="cuda")
+    eng = _eng()
+    q, k, v = W.make_dense(seed, b, sq, sk, hq, hkv, d, dtype, device="cuda")
+    do = _dout(seed, (b, sq, hq, d), dtype)
+    o, lse = eng.attn_fwd(q, k, v, **kw)
+    dq, dk, dv = eng.attn_bwd(q, k, v, o, lse, do, **kw)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.attention_bwd_ref(np64(q), np64(k), np64(v), np64(do), **_opts_np(kw))
+    grad_check(np64(dq), rq, dtype, f"dQ {seed}")
+    grad_check(np64(dk), rk, dtype, f"dK {seed}")
+    grad_check(np64(dv), rv, dtype, f"dV {seed}")
+    if sq > sk and kw.get("causal"):
+        assert torch.all(dq[:, : sq - sk] == 0)
+
+
+def test_bwd_varlen():
+    """Packed sequences (one of length 1, one empty), GQA, causal."""
+    print("[case] bwd varlen", flush=True)
+    eng = _eng()
+    lens = [100, 1, 0, 257, 64]
+    q, k, v, cu, lens = W.make_varlen(89, len(lens), 1, 1, 8, 2, 128, "bf16", device="cuda", lengths=lens)
+    do = _dout(89, tuple(q.shape), "bf16")
+    o, lse = eng.attn_fwd_varlen(q, k, v, cu, cu, max(lens), max(lens), causal=True)
+    dq, dk, dv = eng.attn_bwd_varlen(q, k, v, o, lse, do, cu, cu, max(lens), max(lens), causal=True)
+    torch.cuda.synchronize()
+    cu_np = cu.cpu().numpy()
+    rq, rk, rv = oracle.attention_bwd_varlen_ref(np64(q), np64(k), np64(v), np64(do), cu_np, cu_np, causal=True)
+    grad_check(np64(dq), rq, "bf16", "varlen dQ")
+    grad_check(np64(dk), rk, "bf16", "varlen dK")
+    grad_check(np64(dv), rv, "bf16", "varlen dV")
+
+
+def test_bwd_deterministic():
+    """No atomics: two calls give the same bits."""
+    print("[case] bwd determinism", flush=True)
+    eng = _eng()
+    q, k, v = W.make_dense(90, 2, 333, 333, 8, 2, 128, "bf16", device="cuda")
+    do = _dout(90, tuple(q.shape), "bf16")
+    o, lse = eng.attn_fwd(q, k, v, causal=True)
+    g1 = eng.attn_bwd(q, k, v, o, lse, do, causal=True)
+    g2 = eng.attn_bwd(q, k, v, o, lse, do, causal=True)
+    torch.cuda.synchronize()
+    for a, c in zip(g1, g2):
+        assert torch.equal(a, c)
+
+
+def test_bwd_pages_gradient_check():
+    """The pages' backward check: fp16, S = 1024, causal, gradients against a high-precision
+    reference (here the fp64 oracle); all four (batch, head) pairs in full."""
+    print("[case] bwd fp16 1024 causal", flush=True)
+    eng = _eng()
+    b, s, h, d = 2, 1024, 2, 128
+    q, k, v = W.make_dense(91, b, s, s, h, h, d, "fp16", device="cuda")
+    do = _dout(91, (b, s, h, d), "fp16")
+    o, lse = eng.attn_fwd(q, k, v, causal=True)
+    dq, dk, dv = eng.attn_bwd(q, k, v, o, lse, do, causal=True)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.attention_bwd_ref(np64(q), np64(k), np64(v), np64(do), causal=True)
+    for name, g, r in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        grad_check(np64(g), r, "fp16", f"1024 {name}")
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_bwd_finite_2k(dtype):
+    """The pages' finiteness probe: S = 2048, causal, both dtypes: every gradient finite."""
+    print(f"[case] bwd finite 2048 {dtype}", flush=True)
+    eng = _eng()
+    q, k, v = W.make_dense(92, 2, 2048, 2048, 8, 8, 128, dtype, device="cuda")
+    do = _dout(92, tuple(q.shape), dtype)
+    o, lse = eng.attn_fwd(q, k, v, causal=True)
+    for g in eng.attn_bwd(q, k, v, o, lse, do, causal=True):
+        assert torch.isfinite(g).all()
