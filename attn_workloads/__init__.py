@@ -68,6 +68,12 @@ WORKLOADS = {
     "cfg5a_bf16_decode_alibi": dict(kind="kvcache", seed=1005, batch=32, seqlen_q=1, seqlen_k=32768,
                                     heads_q=32, heads_kv=8, head_dim=128, dtype="bf16", causal=False,
                                     window=(-1, -1), softcap=0.0, num_splits=16, alibi=True),
+    "bwd_cfg2_bf16_causal_2k": dict(kind="bwd", seed=1002, batch=4, seqlen_q=2048, seqlen_k=2048,
+                                    heads_q=16, heads_kv=16, head_dim=128, dtype="bf16", causal=True,
+                                    window=(-1, -1), softcap=0.0),
+    "bwd_fp16_causal_1k": dict(kind="bwd", seed=1007, batch=4, seqlen_q=1024, seqlen_k=1024,
+                               heads_q=16, heads_kv=16, head_dim=128, dtype="fp16", causal=True,
+                               window=(-1, -1), softcap=0.0),
     "cfg5b_fp16_d256_causal": dict(kind="dense", seed=1006, batch=4, seqlen_q=4096,
                                    seqlen_k=4096, heads_q=32, heads_kv=8, head_dim=256,
                                    dtype="fp16", causal=True, window=(-1, -1), softcap=0.0),

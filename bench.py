@@ -219,6 +219,34 @@ def bench_kvcache(name, steps, warmup, torch, eng, W):
             "note": "whole step (split kernel + combine); algorithmic bytes = K+V cache + Q + O + LSE"}
 
 
+def bench_bwd(name, steps, warmup, torch, eng, W):
+    """One attn_bwd call per step (the dot, dK/dV and dQ kernels); O and LSE come from one
+    forward call before the timed region."""
+    c = W.WORKLOADS[name]
+    q, k, v = W.make_dense(c["seed"], c["batch"], c["seqlen_q"], c["seqlen_k"], c["heads_q"],
+                           c["heads_kv"], c["head_dim"], c["dtype"], device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(c["seed"] + 7777)
+    do = W.randn16(tuple(q.shape), c["dtype"], g, device="cuda")
+    o, lse = eng.attn_fwd(q, k, v, causal=c["causal"], window=c["window"], softcap=c["softcap"])
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(eng.attn_bwd_workspace_bytes(c["batch"], c["seqlen_q"], c["heads_q"]),
+                     dtype=torch.uint8, device="cuda")
+
+    def step():
+        eng.attn_bwd(q, k, v, o, lse, do, causal=c["causal"], window=c["window"], softcap=c["softcap"],
+                     dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    ms = time_region(step, steps, warmup, torch)
+    pairs = visible_pairs(c["seqlen_q"], c["seqlen_k"], c["causal"], c["window"])
+    flops = 10.0 * c["head_dim"] * pairs * c["batch"] * c["heads_q"]
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_MFMA_TFLOPS[c["dtype"]]
+    return {"workload": name, "ms_per_step": round(ms, 4), "value": round(tflops, 2), "unit": "TFLOP/s",
+            "frac_of_mfma_peak": round(tflops / peak, 4), "peak": peak, "flops_per_step": flops,
+            "note": "backward (D, dK/dV, dQ kernels); algorithmic FLOPs = 10*D per visible pair "
+                    "(five tile products); the kernels run seven (S and dP formed twice, no atomics)"}
+
+
 def run_copy(steps, warmup, torch):
     n = 1 << 30  # bytes per buffer
     a = torch.ones(n // 4, dtype=torch.float32, device="cuda")
@@ -273,6 +301,22 @@ def main():
         print(json.dumps(line), flush=True)
         return
 
+    if c["kind"] == "bwd":
+        sec = bench_bwd(args.workload, args.steps, args.warmup, torch, eng, W)
+        line = {"metric": "attn bwd TFLOP/s (10*D per visible pair) & % MFMA peak", "value": sec["value"],
+                "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                "ms_per_step": sec["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+                "vs_baseline": None, "dtype": c["dtype"], "data": "synthetic",
+                "config": {"workload": args.workload, **{k: c[k] for k in ("batch", "seqlen_q", "seqlen_k",
+                                                                           "heads_q", "heads_kv", "head_dim",
+                                                                           "causal")}},
+                "roofline": {"bound": "mfma", "achieved": sec["value"], "peak": sec["peak"], "unit": "TFLOP/s",
+                             "frac": sec["frac_of_mfma_peak"], "traffic": None,
+                             "kernel": "bwd_dot + bwd_dkdv + bwd_dq (one attn_bwd call per step)"},
+                "note": sec["note"]}
+        print(json.dumps(line), flush=True)
+        return
+
     if c["kind"] == "varlen":
         ms, flops, config, cfg = bench_varlen(args.workload, args.steps, args.warmup, torch, eng, W)
     else:
@@ -293,6 +337,10 @@ def main():
         torch.cuda.empty_cache()
         line["secondary"] = [bench_kvcache("cfg5a_bf16_decode", max(5, args.steps // 5),
                                            max(2, args.warmup // 10), torch, eng, W)]
+        torch.cuda.empty_cache()
+        log("secondary: backward of the headline workload")
+        line["secondary"].append(bench_bwd("bwd_cfg2_bf16_causal_2k", max(5, args.steps // 4),
+                                           max(20, args.warmup // 4), torch, eng, W))
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline and c["kind"] == "dense":
         log("cpu baseline (oracle on a bounded sample)")

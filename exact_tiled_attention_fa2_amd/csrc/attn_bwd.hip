@@ -217,15 +217,31 @@ bwd_dkdv_kernel(const BwdKernelParams p) {
   constexpr int TILEB = BQ * ROWB;
   constexpr int DS = D / 16;
   constexpr int DT = D / 32;
-  constexpr int KS = BQ / 16;       // 16-query contraction slices per step
+  constexpr int LEAD = 4;           // LDS operand reads issued ahead of the MFMAs
   using Copier = TileCopier<BQ, D, NT>;
 
+  // Three stages of Q and dO tiles (copies run two steps ahead of compute);
+  // the LSE / D rows of a step are staged one step ahead.
   __shared__ __attribute__((aligned(16))) char lds_q0[TILEB];
   __shared__ __attribute__((aligned(16))) char lds_q1[TILEB];
+  __shared__ __attribute__((aligned(16))) char lds_q2[TILEB];
   __shared__ __attribute__((aligned(16))) char lds_g0[TILEB];
   __shared__ __attribute__((aligned(16))) char lds_g1[TILEB];
+  __shared__ __attribute__((aligned(16))) char lds_g2[TILEB];
   __shared__ __attribute__((aligned(16))) float lds_lse[2][BQ];
   __shared__ __attribute__((aligned(16))) float lds_dd[2][BQ];
+  auto qbuf = [&](auto st) __attribute__((always_inline)) -> char* {
+    constexpr int S = decltype(st)::value;
+    if constexpr (S == 0) return lds_q0;
+    else if constexpr (S == 1) return lds_q1;
+    else return lds_q2;
+  };
+  auto gbuf = [&](auto st) __attribute__((always_inline)) -> char* {
+    constexpr int S = decltype(st)::value;
+    if constexpr (S == 0) return lds_g0;
+    else if constexpr (S == 1) return lds_g1;
+    else return lds_g2;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -286,18 +302,28 @@ bwd_dkdv_kernel(const BwdKernelParams p) {
   const float c2 = p.scale_log2;
   const float icap = p.inv_softcap;
 
-  auto head_of = [&](int r) __attribute__((always_inline)) { return kvh * G + r / nsph; };
-  auto q0_of = [&](int r) __attribute__((always_inline)) { return (qblk_lo + r % nsph) * BQ; };
-  // Copies of step r into stage st, and the (guarded) LSE / D loads of its queries.
-  float st_lse = 0.0f, st_dd = 0.0f;
-  auto issue = [&](int r, char* qt, char* gt) __attribute__((always_inline)) {
-    const int h = head_of(r), q0 = q0_of(r);
+  // Steps walk the query tiles of each query head of the group in turn; a
+  // step's (head, first query) advances by one tile, wrapping to the next head.
+  auto advance = [&](int& h, int& q0) __attribute__((always_inline)) {
+    q0 += BQ;
+    if (q0 >= (qblk_lo + nsph) * BQ) {
+      q0 = qblk_lo * BQ;
+      ++h;
+    }
+  };
+  // Tile copies of step (h, q0) into stage buffers qt / gt (2 LOADS per lane).
+  auto issue = [&](int h, int q0, char* qt, char* gt) __attribute__((always_inline)) {
     const char* qb = reinterpret_cast<const char*>(p.q) +
                      2 * (b * p.q_batch + (int64_t)(sr.q_start + q0) * p.q_row + h * p.q_head);
     const char* gb = reinterpret_cast<const char*>(p.dout) +
                      2 * (b * p.do_batch + (int64_t)(sr.q_start + q0) * p.do_row + h * p.do_head);
     cp.copy(qb, 2 * p.q_row, sq - q0, qt, wave, NW);
     cp.copy(gb, 2 * p.do_row, sq - q0, gt, wave, NW);
+  };
+  // The (guarded) LSE / D loads of step r's queries, kept in registers until
+  // they are staged to LDS at the end of the previous step.
+  float st_lse = 0.0f, st_dd = 0.0f;
+  auto issue_rows = [&](int h, int q0) __attribute__((always_inline)) {
     if (tid < BQ) {
       const int q = q0 + tid;
       const int64_t li = b * p.lse_batch + (int64_t)h * p.lse_head + sr.q_start + q;
@@ -312,50 +338,71 @@ bwd_dkdv_kernel(const BwdKernelParams p) {
     }
   };
 
+  // Step r computes on stage ST = r % 3.  Its row loads (for r + 1) are
+  // issued before its copies (for r + 2), so waiting until only the newest
+  // 2 LOADS copies are outstanding retires everything step r + 1 needs.
+  int h = kvh * G, q0 = qblk_lo * BQ;  // position of the step being computed
   auto step = [&](auto stc, int r) __attribute__((always_inline)) {
     constexpr int ST = decltype(stc)::value;
-    char* q_cur = ST == 0 ? lds_q0 : lds_q1;
-    char* g_cur = ST == 0 ? lds_g0 : lds_g1;
-    if (r + 1 < n) issue(r + 1, ST == 0 ? lds_q1 : lds_q0, ST == 0 ? lds_g1 : lds_g0);
-    const int h = head_of(r), q0 = q0_of(r);
+    constexpr int FILL = (ST + 2) % 3;
+    char* q_cur = qbuf(stc);
+    char* g_cur = gbuf(stc);
+    int h1 = h, q1 = q0;
+    advance(h1, q1);
+    int h2 = h1, q2 = q1;
+    advance(h2, q2);
+    if (r + 1 < n) issue_rows(h1, q1);
+    if (r + 2 < n) issue(h2, q2, qbuf(std::integral_constant<int, FILL>{}), gbuf(std::integral_constant<int, FILL>{}));
     const int qv_hi = min(sq - 1, q0 + BQ - 1);
     const bool sees = wave_live && (wr < 0 || wk_lo <= qv_hi + off + wr) && (wl < 0 || wk_hi >= q0 + off - wl);
     if (sees) {
-      f32x16 s[QB], dp[QB];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        s[qb] = f32x16{};
-        dp[qb] = f32x16{};
-      }
-#pragma unroll
-      for (int t = 0; t < DS; ++t) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(q_cur + qb * 32 * ROWB + oo.row_off[t]);
-          s[qb] = Ty::mfma(a, kf[t], s[qb]);
-          const u32x4 a2 = *reinterpret_cast<const u32x4*>(g_cur + qb * 32 * ROWB + oo.row_off[t]);
-          dp[qb] = Ty::mfma(a2, vf[t], dp[qb]);
-        }
-      }
       float slope = 0.0f;
       if constexpr (ALIBI) slope = p.alibi[b * p.alibi_bstride + h] * p.alibi_inv_scale;
       // Every (query, key) pair of the step and wave visible: no mask work.
       const bool full = q0 + BQ - 1 < sq && wk_lo + 31 < sk && (wr < 0 || wk_lo + 31 <= q0 + off + wr) &&
                         (wl < 0 || wk_lo >= q0 + BQ - 1 + off - wl);
-      uint32_t pp[QB][8], ps[QB][8];
+      // The step's 32-query blocks one after the other (fewer live registers).
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
+        // One wave per SIMD hides no LDS latency behind another wave: all of
+        // the block's operand reads are issued before its MFMAs.
+        u32x4 aq[DS], ag[DS];
+#pragma unroll
+        for (int t = 0; t < DS; ++t) {
+          aq[t] = *reinterpret_cast<const u32x4*>(q_cur + qb * 32 * ROWB + oo.row_off[t]);
+          ag[t] = *reinterpret_cast<const u32x4*>(g_cur + qb * 32 * ROWB + oo.row_off[t]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int t = 0; t < DS; ++t) {
+          s = Ty::mfma(aq[t], kf[t], s);
+          dp = Ty::mfma(ag[t], vf[t], dp);
+        }
+        // The transposed operands of the block's two 16-query slices, read
+        // while the elementwise work below runs.
+        u32x4 tg[2][DT], tq[2][DT];
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            tg[k2][dt] = tr_operand<D>(g_cur, oo, 2 * qb + k2, dt);
+            tq[k2][dt] = tr_operand<D>(q_cur, oo, 2 * qb + k2, dt);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        uint32_t pp[8], ps[8];
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int qo = 32 * qb + 8 * g4 + 4 * hl;  // first of this lane's 4 consecutive queries
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lds_lse[ST][qo]);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&lds_dd[ST][qo]);
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lds_lse[r & 1][qo]);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&lds_dd[r & 1][qo]);
           float pv[4], dv[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int rr = 4 * g4 + i;
             const int q = q0 + qo + i;
-            float x = s[qb][rr];
+            float x = s[rr];
             float gcap = 1.0f;
             if constexpr (SOFTCAP) {
               x = transform_score<true>(x, p.softcap_pre, p.softcap);
@@ -364,52 +411,63 @@ bwd_dkdv_kernel(const BwdKernelParams p) {
             }
             if constexpr (ALIBI) x = fmaf(-slope, fabsf((float)(q + off - key)), x);
             if (!full) {
-              const bool vis = q < sq && key < sk && (wr < 0 || key <= q + off + wr) && (wl < 0 || key >= q + off - wl);
-              if (!vis) x = -INFINITY;
+              const bool vis = (q < sq) & (key < sk) & ((wr < 0) | (key <= q + off + wr)) &
+                               ((wl < 0) | (key >= q + off - wl));
+              x = vis ? x : -INFINITY;
             }
             const float pr = fast_exp2(fmaf(x, c2, -l4[i]));
             pv[i] = pr;
-            float d = pr * (dp[qb][rr] - d4[i]);
+            float d = pr * (dp[rr] - d4[i]);
             if constexpr (SOFTCAP) d *= gcap;
             dv[i] = d;
           }
-          pp[qb][2 * g4] = Ty::pack(pv[0], pv[1]);
-          pp[qb][2 * g4 + 1] = Ty::pack(pv[2], pv[3]);
-          ps[qb][2 * g4] = Ty::pack(dv[0], dv[1]);
-          ps[qb][2 * g4 + 1] = Ty::pack(dv[2], dv[3]);
+          pp[2 * g4] = Ty::pack(pv[0], pv[1]);
+          pp[2 * g4 + 1] = Ty::pack(pv[2], pv[3]);
+          ps[2 * g4] = Ty::pack(dv[0], dv[1]);
+          ps[2 * g4 + 1] = Ty::pack(dv[2], dv[3]);
         }
-      }
-      // dV^T += dO^T P and dK^T += Q^T dS, contracting over the step's queries
-      // in the order the score registers hold them.
+        // dV^T += dO^T P and dK^T += Q^T dS over the block's two 16-query
+        // slices, contracting in the order the score registers hold them.
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 bp = {pp[ks >> 1][4 * (ks & 1) + 0], pp[ks >> 1][4 * (ks & 1) + 1],
-                          pp[ks >> 1][4 * (ks & 1) + 2], pp[ks >> 1][4 * (ks & 1) + 3]};
-        const u32x4 bs = {ps[ks >> 1][4 * (ks & 1) + 0], ps[ks >> 1][4 * (ks & 1) + 1],
-                          ps[ks >> 1][4 * (ks & 1) + 2], ps[ks >> 1][4 * (ks & 1) + 3]};
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const u32x4 bp = {pp[4 * k2 + 0], pp[4 * k2 + 1], pp[4 * k2 + 2], pp[4 * k2 + 3]};
+          const u32x4 bs = {ps[4 * k2 + 0], ps[4 * k2 + 1], ps[4 * k2 + 2], ps[4 * k2 + 3]};
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          acc_dv[dt] = Ty::mfma(tr_operand<D>(g_cur, oo, ks, dt), bp, acc_dv[dt]);
-          acc_dk[dt] = Ty::mfma(tr_operand<D>(q_cur, oo, ks, dt), bs, acc_dk[dt]);
+          for (int dt = 0; dt < DT; ++dt) {
+            acc_dv[dt] = Ty::mfma(tg[k2][dt], bp, acc_dv[dt]);
+            acc_dk[dt] = Ty::mfma(tq[k2][dt], bs, acc_dk[dt]);
+          }
         }
       }
     }
-    wait_vmem();
-    if (r + 1 < n) stage_rows(ST ^ 1);
+    if (r + 2 < n) wait_vmem_le<2 * Copier::LOADS>();
+    else wait_vmem();
+    if (r + 1 < n) stage_rows((r + 1) & 1);
     __syncthreads();
+    h = h1;
+    q0 = q1;
   };
 
   if (n > 0) {
-    issue(0, lds_q0, lds_g0);
-    wait_vmem();
+    issue_rows(h, q0);
+    issue(h, q0, lds_q0, lds_g0);
+    if (n > 1) {
+      int h1 = h, q1 = q0;
+      advance(h1, q1);
+      issue(h1, q1, lds_q1, lds_g1);
+    }
+    if (n > 1) wait_vmem_le<2 * Copier::LOADS>();
+    else wait_vmem();
     stage_rows(0);
     __syncthreads();
     int r = 0;
-    for (; r + 2 <= n; r += 2) {
+    for (; r + 3 <= n; r += 3) {
       step(std::integral_constant<int, 0>{}, r);
       step(std::integral_constant<int, 1>{}, r + 1);
+      step(std::integral_constant<int, 2>{}, r + 2);
     }
     if (r < n) step(std::integral_constant<int, 0>{}, r);
+    if (r + 1 < n) step(std::integral_constant<int, 1>{}, r + 1);
   }
 
   if (key_valid) {
@@ -436,6 +494,7 @@ bwd_dq_kernel(const BwdKernelParams p) {
   constexpr int DS = D / 16;
   constexpr int DT = D / 32;
   constexpr int KS = BK / 16;
+  constexpr int LEAD = 4;
   using Copier = TileCopier<BK, D, NT>;
 
   __shared__ __attribute__((aligned(16))) char lds_k0[TILEB];
@@ -540,6 +599,11 @@ bwd_dq_kernel(const BwdKernelParams p) {
           dp[kt] = Ty::mfma(a2, gf[t], dp[kt]);
         }
       }
+      __builtin_amdgcn_sched_group_barrier(0x100, LEAD, 0);
+      for (int i = 0; i < 2 * DS * KT; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
       const bool full = j0 >= full_lo && j0 + BK - 1 <= full_hi;
       uint32_t ps[KT][8];
 #pragma unroll
@@ -559,7 +623,7 @@ bwd_dq_kernel(const BwdKernelParams p) {
               gcap = fmaf(-th, th, 1.0f);
             }
             if constexpr (ALIBI) x = fmaf(-slope, fabsf((float)(row + off - kk)), x);
-            if (!full && (kk < kmin || kk > kmax)) x = -INFINITY;
+            if (!full) x = ((kk >= kmin) & (kk <= kmax)) ? x : -INFINITY;
             const float pr = fast_exp2(fmaf(x, c2, -lse2));
             float d = pr * (dp[kt][rr] - dd);
             if constexpr (SOFTCAP) d *= gcap;
@@ -575,6 +639,11 @@ bwd_dq_kernel(const BwdKernelParams p) {
                           ps[ks >> 1][4 * (ks & 1) + 2], ps[ks >> 1][4 * (ks & 1) + 3]};
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) acc[dt] = Ty::mfma(tr_operand<D>(k_cur, oo, ks, dt), bs, acc[dt]);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * LEAD, 0);
+      for (int i = 0; i < KS * DT; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
     }
     wait_vmem();
