@@ -32,6 +32,7 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include <type_traits>
 
@@ -205,10 +206,15 @@ __device__ __forceinline__ void store_rows(uint16_t* dst, const f32x16 (&acc)[D 
 }
 
 // ---------------------------------------------------------------- dK, dV
-template <class Ty, int D, bool SOFTCAP, bool ALIBI>
-__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+// NW waves per workgroup (32 keys each), WPE waves per SIMD.  PASSES = 1:
+// one walk over the queries accumulates dV and dK together (~440 registers:
+// one wave per SIMD).  PASSES = 2: a first walk accumulates dV (S, P), a
+// second dK (S, dP, dS) -- S is formed twice, but each walk fits two waves
+// per SIMD.
+template <class Ty, int D, bool SOFTCAP, bool ALIBI, int NW, int WPE, int PASSES>
+__global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(WPE, WPE)))
 bwd_dkdv_kernel(const BwdKernelParams p) {
-  constexpr int NW = 4;
+  static_assert(PASSES == 1 || PASSES == 2, "one or two passes");
   constexpr int NT = NW * 64;
   constexpr int BQ = 64;            // queries per step
   constexpr int QB = BQ / 32;       // 32-query MFMA blocks per step
@@ -265,19 +271,10 @@ bwd_dkdv_kernel(const BwdKernelParams p) {
   const bool wave_live = wk_lo < sk;
   const int wk_hi = min(sk - 1, wk_lo + 31);
 
-  // K and V rows of this lane's key: B operands (8 consecutive dims per k-step).
-  u32x4 kf[DS], vf[DS];
-  {
-    const uint16_t* kp = reinterpret_cast<const uint16_t*>(p.k) + b * p.k_batch +
-                         (int64_t)(sr.k_start + keyc) * p.k_row + kvh * p.k_head;
-    const uint16_t* vp = reinterpret_cast<const uint16_t*>(p.v) + b * p.v_batch +
-                         (int64_t)(sr.k_start + keyc) * p.v_row + kvh * p.v_head;
-#pragma unroll
-    for (int t = 0; t < DS; ++t) {
-      kf[t] = *reinterpret_cast<const u32x4*>(kp + 16 * t + 8 * hl);
-      vf[t] = *reinterpret_cast<const u32x4*>(vp + 16 * t + 8 * hl);
-    }
-  }
+  const uint16_t* kp = reinterpret_cast<const uint16_t*>(p.k) + b * p.k_batch +
+                       (int64_t)(sr.k_start + keyc) * p.k_row + kvh * p.k_head;
+  const uint16_t* vp = reinterpret_cast<const uint16_t*>(p.v) + b * p.v_batch +
+                       (int64_t)(sr.k_start + keyc) * p.v_row + kvh * p.v_head;
 
   // Queries that see some key of this workgroup.
   const int wg_hi = min(sk - 1, n0 + BN - 1);
@@ -291,13 +288,6 @@ bwd_dkdv_kernel(const BwdKernelParams p) {
   oo.init(lane);
   Copier cp;
   cp.init(wave, lane, NW);
-
-  f32x16 acc_dk[DT], acc_dv[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    acc_dk[dt] = f32x16{};
-    acc_dv[dt] = f32x16{};
-  }
 
   const float c2 = p.scale_log2;
   const float icap = p.inv_softcap;
@@ -338,6 +328,25 @@ bwd_dkdv_kernel(const BwdKernelParams p) {
     }
   };
 
+  // One walk over the steps; DO_DV / DO_DK select the gradients it forms.
+  auto run_pass = [&](auto pass_c) __attribute__((always_inline)) {
+  constexpr int PASS = decltype(pass_c)::value;
+  constexpr bool DO_DV = PASSES == 1 || PASS == 0;
+  constexpr bool DO_DK = PASSES == 1 || PASS == 1;
+  // K (and, for dK, V) rows of this lane's key: B operands (8 consecutive
+  // dims per k-step), loaded per walk.
+  u32x4 kf[DS], vf[DS];
+#pragma unroll
+  for (int t = 0; t < DS; ++t) {
+    kf[t] = *reinterpret_cast<const u32x4*>(kp + 16 * t + 8 * hl);
+    if constexpr (DO_DK) vf[t] = *reinterpret_cast<const u32x4*>(vp + 16 * t + 8 * hl);
+  }
+  f32x16 acc_dk[DT], acc_dv[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    acc_dk[dt] = f32x16{};
+    acc_dv[dt] = f32x16{};
+  }
   // Step r computes on stage ST = r % 3.  Its row loads (for r + 1) are
   // issued before its copies (for r + 2), so waiting until only the newest
   // 2 LOADS copies are outstanding retires everything step r + 1 needs.
@@ -366,28 +375,38 @@ bwd_dkdv_kernel(const BwdKernelParams p) {
       for (int qb = 0; qb < QB; ++qb) {
         // One wave per SIMD hides no LDS latency behind another wave: all of
         // the block's operand reads are issued before its MFMAs.
-        u32x4 aq[DS], ag[DS];
-#pragma unroll
-        for (int t = 0; t < DS; ++t) {
-          aq[t] = *reinterpret_cast<const u32x4*>(q_cur + qb * 32 * ROWB + oo.row_off[t]);
-          ag[t] = *reinterpret_cast<const u32x4*>(g_cur + qb * 32 * ROWB + oo.row_off[t]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+        // In batches of RB k-steps (all of them at one wave per SIMD).
+        constexpr int RB = WPE == 1 ? DS : (DS >= 4 ? 2 : DS);
         f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-        for (int t = 0; t < DS; ++t) {
-          s = Ty::mfma(aq[t], kf[t], s);
-          dp = Ty::mfma(ag[t], vf[t], dp);
+        for (int t0 = 0; t0 < DS; t0 += RB) {
+          u32x4 aq[RB], ag[RB];
+#pragma unroll
+          for (int t = 0; t < RB; ++t) {
+            aq[t] = *reinterpret_cast<const u32x4*>(q_cur + qb * 32 * ROWB + oo.row_off[t0 + t]);
+            if constexpr (DO_DK) ag[t] = *reinterpret_cast<const u32x4*>(g_cur + qb * 32 * ROWB + oo.row_off[t0 + t]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int t = 0; t < RB; ++t) {
+            s = Ty::mfma(aq[t], kf[t0 + t], s);
+            if constexpr (DO_DK) dp = Ty::mfma(ag[t], vf[t0 + t], dp);
+          }
         }
-        // The transposed operands of the block's two 16-query slices, read
-        // while the elementwise work below runs.
+        // At one wave per SIMD the transposed operands of the block's two
+        // 16-query slices are read while the elementwise work below runs; at
+        // two, the other wave covers their latency and the registers are
+        // needed elsewhere.
+        constexpr bool TR_AHEAD = WPE == 1;
         u32x4 tg[2][DT], tq[2][DT];
+        if constexpr (TR_AHEAD) {
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
+          for (int k2 = 0; k2 < 2; ++k2) {
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
-            tg[k2][dt] = tr_operand<D>(g_cur, oo, 2 * qb + k2, dt);
-            tq[k2][dt] = tr_operand<D>(q_cur, oo, 2 * qb + k2, dt);
+            for (int dt = 0; dt < DT; ++dt) {
+              if constexpr (DO_DV) tg[k2][dt] = tr_operand<D>(g_cur, oo, 2 * qb + k2, dt);
+              if constexpr (DO_DK) tq[k2][dt] = tr_operand<D>(q_cur, oo, 2 * qb + k2, dt);
+            }
           }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -396,7 +415,8 @@ bwd_dkdv_kernel(const BwdKernelParams p) {
         for (int g4 = 0; g4 < 4; ++g4) {
           const int qo = 32 * qb + 8 * g4 + 4 * hl;  // first of this lane's 4 consecutive queries
           const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lds_lse[r & 1][qo]);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&lds_dd[r & 1][qo]);
+          f32x4 d4 = f32x4{};
+          if constexpr (DO_DK) d4 = *reinterpret_cast<const f32x4*>(&lds_dd[r & 1][qo]);
           float pv[4], dv[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -417,25 +437,37 @@ bwd_dkdv_kernel(const BwdKernelParams p) {
             }
             const float pr = fast_exp2(fmaf(x, c2, -l4[i]));
             pv[i] = pr;
-            float d = pr * (dp[rr] - d4[i]);
-            if constexpr (SOFTCAP) d *= gcap;
-            dv[i] = d;
+            if constexpr (DO_DK) {
+              float d = pr * (dp[rr] - d4[i]);
+              if constexpr (SOFTCAP) d *= gcap;
+              dv[i] = d;
+            }
           }
-          pp[2 * g4] = Ty::pack(pv[0], pv[1]);
-          pp[2 * g4 + 1] = Ty::pack(pv[2], pv[3]);
-          ps[2 * g4] = Ty::pack(dv[0], dv[1]);
-          ps[2 * g4 + 1] = Ty::pack(dv[2], dv[3]);
+          if constexpr (DO_DV) {
+            pp[2 * g4] = Ty::pack(pv[0], pv[1]);
+            pp[2 * g4 + 1] = Ty::pack(pv[2], pv[3]);
+          }
+          if constexpr (DO_DK) {
+            ps[2 * g4] = Ty::pack(dv[0], dv[1]);
+            ps[2 * g4 + 1] = Ty::pack(dv[2], dv[3]);
+          }
         }
         // dV^T += dO^T P and dK^T += Q^T dS over the block's two 16-query
         // slices, contracting in the order the score registers hold them.
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
-          const u32x4 bp = {pp[4 * k2 + 0], pp[4 * k2 + 1], pp[4 * k2 + 2], pp[4 * k2 + 3]};
-          const u32x4 bs = {ps[4 * k2 + 0], ps[4 * k2 + 1], ps[4 * k2 + 2], ps[4 * k2 + 3]};
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) {
-            acc_dv[dt] = Ty::mfma(tg[k2][dt], bp, acc_dv[dt]);
-            acc_dk[dt] = Ty::mfma(tq[k2][dt], bs, acc_dk[dt]);
+            if constexpr (DO_DV) {
+              const u32x4 bp = {pp[4 * k2 + 0], pp[4 * k2 + 1], pp[4 * k2 + 2], pp[4 * k2 + 3]};
+              const u32x4 a = TR_AHEAD ? tg[k2][dt] : tr_operand<D>(g_cur, oo, 2 * qb + k2, dt);
+              acc_dv[dt] = Ty::mfma(a, bp, acc_dv[dt]);
+            }
+            if constexpr (DO_DK) {
+              const u32x4 bs = {ps[4 * k2 + 0], ps[4 * k2 + 1], ps[4 * k2 + 2], ps[4 * k2 + 3]};
+              const u32x4 a = TR_AHEAD ? tq[k2][dt] : tr_operand<D>(q_cur, oo, 2 * qb + k2, dt);
+              acc_dk[dt] = Ty::mfma(a, bs, acc_dk[dt]);
+            }
           }
         }
       }
@@ -471,13 +503,21 @@ bwd_dkdv_kernel(const BwdKernelParams p) {
   }
 
   if (key_valid) {
-    uint16_t* dkp = reinterpret_cast<uint16_t*>(p.dk) + b * p.dk_batch + (int64_t)(sr.k_start + key) * p.dk_row +
-                    kvh * p.dk_head;
-    uint16_t* dvp = reinterpret_cast<uint16_t*>(p.dv) + b * p.dv_batch + (int64_t)(sr.k_start + key) * p.dv_row +
-                    kvh * p.dv_head;
-    store_rows<Ty, D>(dkp, acc_dk, p.scale, hl);
-    store_rows<Ty, D>(dvp, acc_dv, 1.0f, hl);
+    if constexpr (DO_DK) {
+      uint16_t* dkp = reinterpret_cast<uint16_t*>(p.dk) + b * p.dk_batch +
+                      (int64_t)(sr.k_start + key) * p.dk_row + kvh * p.dk_head;
+      store_rows<Ty, D>(dkp, acc_dk, p.scale, hl);
+    }
+    if constexpr (DO_DV) {
+      uint16_t* dvp = reinterpret_cast<uint16_t*>(p.dv) + b * p.dv_batch +
+                      (int64_t)(sr.k_start + key) * p.dv_row + kvh * p.dv_head;
+      store_rows<Ty, D>(dvp, acc_dv, 1.0f, hl);
+    }
   }
+  };  // run_pass
+
+  run_pass(std::integral_constant<int, 0>{});
+  if constexpr (PASSES == 2) run_pass(std::integral_constant<int, 1>{});
 }
 
 // ---------------------------------------------------------------- dQ
@@ -669,6 +709,16 @@ bwd_dq_kernel(const BwdKernelParams p) {
   }
 }
 
+// dK/dV kernel variant for sweeps (environment ATTN_MI355X_BWD_VARIANT):
+// 0 = one pass at 4 waves (default, measured faster), 1 = two passes at 8 waves.
+int bwd_variant() {
+  static const int v = [] {
+    const char* e = getenv("ATTN_MI355X_BWD_VARIANT");
+    return e ? atoi(e) : 0;
+  }();
+  return v;
+}
+
 // D first (both gradient kernels read it), then dK/dV, then dQ; a kernel
 // whose grid would be empty (no queries, or no keys) is not launched.
 template <class Ty, int D, bool SOFTCAP, bool ALIBI>
@@ -680,8 +730,13 @@ hipError_t launch_bwd_t(const BwdKernelParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((bwd_dot_kernel<Ty, D>), grid, dim3(256), 0, stream, p);
   }
   if (p.seqlen_k > 0) {
-    const dim3 grid((unsigned)((p.seqlen_k + 127) / 128), p.heads_kv, p.batch);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<Ty, D, SOFTCAP, ALIBI>), grid, dim3(256), 0, stream, p);
+    if (bwd_variant() == 1) {
+      const dim3 grid((unsigned)((p.seqlen_k + 255) / 256), p.heads_kv, p.batch);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<Ty, D, SOFTCAP, ALIBI, 8, 2, 2>), grid, dim3(512), 0, stream, p);
+    } else {
+      const dim3 grid((unsigned)((p.seqlen_k + 127) / 128), p.heads_kv, p.batch);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<Ty, D, SOFTCAP, ALIBI, 4, 1, 1>), grid, dim3(256), 0, stream, p);
+    }
   }
   if (p.seqlen_q > 0) {
     const dim3 grid((unsigned)((p.seqlen_q + 127) / 128), p.heads_q, p.batch);
