@@ -143,8 +143,28 @@ __device__ __forceinline__ bool tile_work(const FwdKernelParams& p, TileWork& w)
 // NSTAGE K/V tile buffers (copies run NSTAGE - 1 steps ahead of compute);
 // PAGED: K/V rows come from a paged cache through p.block_table.  ALIBI: the
 // linear distance bias of p.alibi is added to the scores.
+// 2^x without the transcendental unit (the exp2-on-FMA-pipe idea the pages
+// name for FA4, release notes of the project survey page): Cody-Waite range
+// reduction x = n + f with n = rint(x), |f| <= 1/2, a degree-4 polynomial for
+// 2^f (coefficients fitted for least relative error on [-1/2, 1/2]: max
+// relative error 2.6e-6, far below the 16-bit rounding of P), then 2^n by
+// ldexp.  Inputs below -126, the -inf of a masked score included, give 0.
+__device__ __forceinline__ float exp2_fma(float x) {
+  const bool live = x >= -126.0f;
+  const float xc = live ? x : 0.0f;
+  const float n = __builtin_rintf(xc);
+  const float f = xc - n;
+  float p = 0.009571806527674198f;
+  p = fmaf(p, f, 0.05591800436377525f);
+  p = fmaf(p, f, 0.24024702608585358f);
+  p = fmaf(p, f, 0.6931217908859253f);
+  p = fmaf(p, f, 0.9999992847442627f);
+  const float r = __builtin_amdgcn_ldexpf(p, (int)n);
+  return live ? r : 0.0f;
+}
+
 template <class Ty, int D, int BK, int NW, int QG, bool SOFTCAP, int LEAD, int WPE, int NSTAGE = 2,
-          bool PAGED = false, bool ALIBI = false>
+          bool PAGED = false, bool ALIBI = false, bool EXPP = false>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(WPE, WPE)))
 fwd_tile_kernel(const FwdKernelParams p) {
   constexpr int NT = NW * 64;           // threads per workgroup
@@ -380,7 +400,12 @@ fwd_tile_kernel(const FwdKernelParams p) {
         for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
           for (int r2 = 0; r2 < 16; ++r2)
-            sc[g][kt][r2] = transform_score<SOFTCAP>(sc[g][kt][r2], p.softcap_pre, p.softcap);
+            if constexpr (EXPP) {
+              const float e = exp2_fma(sc[g][kt][r2] * p.softcap_pre * (2.0f * kLog2e));
+              sc[g][kt][r2] = p.softcap * (1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f));
+            } else {
+              sc[g][kt][r2] = transform_score<SOFTCAP>(sc[g][kt][r2], p.softcap_pre, p.softcap);
+            }
       }
       // ALiBi bias -slope |d| with d = i + off - key = d0 - c, where key =
       // j0 + 4 hl + c and c is fixed per register.  When the whole step lies
@@ -451,8 +476,9 @@ fwd_tile_kernel(const FwdKernelParams p) {
       for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
         for (int r2 = 0; r2 < 16; r2 += 2) {
-          const float p0 = fast_exp2(fmaf(sc[g][kt][r2], c2, nb));
-          const float p1 = fast_exp2(fmaf(sc[g][kt][r2 + 1], c2, nb));
+          const float p0 = EXPP ? exp2_fma(fmaf(sc[g][kt][r2], c2, nb)) : fast_exp2(fmaf(sc[g][kt][r2], c2, nb));
+          const float p1 = EXPP ? exp2_fma(fmaf(sc[g][kt][r2 + 1], c2, nb))
+                                : fast_exp2(fmaf(sc[g][kt][r2 + 1], c2, nb));
           l_run[g] += p0 + p1;
           pk[g][kt][r2 >> 1] = Ty::pack(p0, p1);
         }
@@ -695,7 +721,7 @@ int col_group_for(const FwdKernelParams& p, int heads_grid, int nz, int head_dim
 }
 
 template <class Ty, int D, int BK, int NW, int QG, bool SOFTCAP, int LEAD, int WPE, int NSTAGE = 2,
-          bool PAGED = false, bool ALIBI = false>
+          bool PAGED = false, bool ALIBI = false, bool EXPP = false>
 hipError_t launch_fwd_t(FwdKernelParams p, hipStream_t stream) {
   constexpr int BQ = 32 * NW * QG;
   const int64_t rows = (int64_t)p.seqlen_q * (p.pack_gqa ? p.group : 1);
@@ -709,17 +735,17 @@ hipError_t launch_fwd_t(FwdKernelParams p, hipStream_t stream) {
     p.xcd_chunk = (p.cu_seqlens_q == nullptr && per_xcd > 0) ? per_xcd : 1;
   }
   dim3 grid(p.num_m_tiles, heads_grid, p.batch * p.num_splits);
-  hipLaunchKernelGGL((fwd_tile_kernel<Ty, D, BK, NW, QG, SOFTCAP, LEAD, WPE, NSTAGE, PAGED, ALIBI>), grid, dim3(NW * 64), 0, stream, p);
+  hipLaunchKernelGGL((fwd_tile_kernel<Ty, D, BK, NW, QG, SOFTCAP, LEAD, WPE, NSTAGE, PAGED, ALIBI, EXPP>), grid,
+                     dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 
-// Tile-shape variant for tuning sweeps (environment ATTN_MI355X_FWD_VARIANT); 0 = default.
+// Tile-shape variant for tuning sweeps (environment ATTN_MI355X_FWD_VARIANT,
+// read at every launch); 0 = default, 4 = P (and softcap's tanh) with exp2 on
+// the FMA pipe.
 int fwd_variant() {
-  static const int v = [] {
-    const char* e = getenv("ATTN_MI355X_FWD_VARIANT");
-    return e ? atoi(e) : 0;
-  }();
-  return v;
+  const char* e = getenv("ATTN_MI355X_FWD_VARIANT");
+  return e ? atoi(e) : 0;
 }
 
 // Decode tile variant for tuning sweeps (environment ATTN_MI355X_DEC_VARIANT); 0 = default.
@@ -758,6 +784,9 @@ hipError_t launch_fwd_shape(const FwdKernelParams& p, int head_dim, hipStream_t 
           case 1: return launch_fwd_t<Ty, 128, 64, 4, 1, CAP, 4, 2>(p, stream);
           case 2: return launch_fwd_t<Ty, 128, 64, 8, 1, CAP, 6, 2>(p, stream);
           case 3: return launch_fwd_t<Ty, 128, 32, 4, 1, CAP, 4, 2, 4>(p, stream);
+          case 4:
+            if (!CAP) return launch_fwd_t<Ty, 128, 64, 8, 1, CAP, 6, 2, 2, false, false, true>(p, stream);
+            return launch_fwd_t<Ty, 128, 64, 4, 1, CAP, 4, 2, 2, false, false, true>(p, stream);
           default: break;
         }
       }

@@ -376,3 +376,28 @@ def test_full_cfg5a_decode(name):
         lrefs.append(rl[0, 0])
     gate_check(np.concatenate(outs), np.concatenate(refs), np.concatenate(lses), np.concatenate(lrefs),
                "bf16", "cfg5a")
+
+
+# ------------------------------------------------------------------ exp2 on the FMA pipe (variant 4)
+
+@pytest.mark.parametrize("name", ["cfg2_bf16_causal_2k", "cfg4_bf16_gqa_window_softcap"])
+def test_exp2_fma_variant_full(name, monkeypatch):
+    """P (and softcap's tanh) from the polynomial exp2: the oracle's answer on the full-size
+    workload (sampled rows)."""
+    monkeypatch.setenv("ATTN_MI355X_FWD_VARIANT", "4")
+    _sampled_dense(name)
+
+
+@pytest.mark.parametrize("case", [(93, 1, 300, 100, 2, 2, 128, "bf16", dict(causal=True)),
+                                  (94, 2, 333, 333, 4, 1, 128, "fp16", dict(causal=True, softcap=20.0)),
+                                  (95, 1, 257, 400, 8, 8, 128, "bf16", dict(causal=False))],
+                         ids=["s93", "s94", "s95"])
+def test_exp2_fma_variant_small(case, monkeypatch):
+    """Ragged tails, rows with no visible key (O = 0 and LSE = -inf exactly), softcap."""
+    monkeypatch.setenv("ATTN_MI355X_FWD_VARIANT", "4")
+    seed, b, sq, sk, hq, hkv, d, dtype, kw = case
+    print(f"[case] exp2-fma seed={seed} b={b} sq={sq} sk={sk} hq={hq} hkv={hkv} d={d} {dtype} {kw}", flush=True)
+    o, lse, ro, rl = _dense_case(seed, b, sq, sk, hq, hkv, d, dtype, **kw)
+    gate_check(np64(o), ro, np64(lse), rl, dtype, f"exp2-fma {seed}")
+    if sq > sk and kw.get("causal"):
+        assert torch.all(o[:, : sq - sk] == 0) and torch.all(torch.isneginf(lse[:, :, : sq - sk]))
