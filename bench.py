@@ -247,6 +247,34 @@ def bench_bwd(name, steps, warmup, torch, eng, W):
                     "(five tile products); the kernels run seven (S and dP formed twice, no atomics)"}
 
 
+# Forward latency table of the release page "v1.7 / flash_attn 2.9.2.post1", section 4.5
+# (fp16, causal, one NVIDIA consumer GPU; batch and heads not stated): (S, D) -> ms per call.
+PAGES_LATENCY_MS = {(1024, 64): 0.079, (1024, 128): 0.151, (4096, 64): 0.839, (4096, 128): 1.725,
+                    (8192, 64): 3.162, (8192, 128): 6.504}
+
+
+def run_pages_latency(steps, warmup, torch, eng, W):
+    """The pages' latency shapes timed here (B = 2, H = 8 assumed: the page does not state them).
+    Context only -- another machine, unknown batch and heads."""
+    for (s, d), theirs in PAGES_LATENCY_MS.items():
+        q, k, v = W.make_dense(2000 + s + d, 2, s, s, 8, 8, d, "fp16", device="cuda")
+        o = torch.empty_like(q)
+        lse = torch.empty((2, 8, s), dtype=torch.float32, device="cuda")
+
+        def step():
+            eng.attn_fwd(q, k, v, causal=True, out=o, lse=lse)
+
+        ms = time_region(step, steps, warmup, torch)
+        flops = 4.0 * d * visible_pairs(s, s, True, (-1, -1)) * 2 * 8
+        print(json.dumps({"mode": "pages-latency", "seqlen": s, "head_dim": d, "batch": 2, "heads": 8,
+                          "dtype": "fp16", "causal": True, "ms": round(ms, 4),
+                          "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+                          "pages_ms": theirs, "note": "pages: another GPU, batch/heads not stated"}),
+              flush=True)
+        del q, k, v, o, lse
+        torch.cuda.empty_cache()
+
+
 def run_copy(steps, warmup, torch):
     n = 1 << 30  # bytes per buffer
     a = torch.ones(n // 4, dtype=torch.float32, device="cuda")
@@ -264,7 +292,7 @@ def main():
     ap.add_argument("--workload", default="cfg2_bf16_causal_2k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--mode", default="attn", choices=["attn", "copy"])
+    ap.add_argument("--mode", default="attn", choices=["attn", "copy", "pages-latency"])
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -284,6 +312,9 @@ def main():
     eng.lib()
     if args.mode == "copy":
         run_copy(args.steps, args.warmup, torch)
+        return
+    if args.mode == "pages-latency":
+        run_pages_latency(args.steps, args.warmup, torch, eng, W)
         return
 
     c = W.WORKLOADS[args.workload]

@@ -748,6 +748,18 @@ int fwd_variant() {
   return e ? atoi(e) : 0;
 }
 
+// Compute units of the current device (queried once per device).
+int compute_units() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    cus[dev] = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) ? n : 256;
+  }
+  return cus[dev];
+}
+
 // Decode tile variant for tuning sweeps (environment ATTN_MI355X_DEC_VARIANT); 0 = default.
 int dec_variant() {
   static const int v = [] {
@@ -792,9 +804,15 @@ hipError_t launch_fwd_shape(const FwdKernelParams& p, int head_dim, hipStream_t 
       }
       // 256 query rows per workgroup (8 waves, one workgroup per CU) halve
       // the K/V re-reads from L2 per FLOP and win on dense and varlen
-      // launches; the VALU-heavy softcap path runs faster with 128 rows
-      // and two workgroups per CU.
-      if (!CAP) return launch_fwd_t<Ty, 128, 64, 8, 1, CAP, 6, 2, 2, false, AL>(p, stream);
+      // launches that give every CU at least two such workgroups; smaller
+      // grids run faster with 128-row tiles (twice the workgroups), and so
+      // does the VALU-heavy softcap path (two workgroups per CU).
+      if (!CAP) {
+        const int64_t heads_grid = p.pack_gqa ? p.heads_kv : p.heads_q;
+        const int64_t wgs256 = (packed + 255) / 256 * heads_grid * p.batch * p.num_splits;
+        if (wgs256 >= 2 * (int64_t)compute_units())
+          return launch_fwd_t<Ty, 128, 64, 8, 1, CAP, 6, 2, 2, false, AL>(p, stream);
+      }
       return launch_fwd_t<Ty, 128, 64, 4, 1, CAP, 4, 2, 2, false, AL>(p, stream);
     }
     case 256:
