@@ -410,7 +410,11 @@ bwd_dkdv_kernel(const BwdKernelParams p) {
           }
         }
         __builtin_amdgcn_sched_barrier(0);
+        // P and dS, with the mask only on steps that an edge crosses for the
+        // wave (two copies of the loop, so that full steps carry no mask work).
         uint32_t pp[8], ps[8];
+        auto elementwise = [&](auto masked_c) __attribute__((always_inline)) {
+        constexpr bool MASKED = decltype(masked_c)::value;
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int qo = 32 * qb + 8 * g4 + 4 * hl;  // first of this lane's 4 consecutive queries
@@ -430,7 +434,7 @@ bwd_dkdv_kernel(const BwdKernelParams p) {
               gcap = fmaf(-th, th, 1.0f);
             }
             if constexpr (ALIBI) x = fmaf(-slope, fabsf((float)(q + off - key)), x);
-            if (!full) {
+            if constexpr (MASKED) {
               const bool vis = (q < sq) & (key < sk) & ((wr < 0) | (key <= q + off + wr)) &
                                ((wl < 0) | (key >= q + off - wl));
               x = vis ? x : -INFINITY;
@@ -452,6 +456,9 @@ bwd_dkdv_kernel(const BwdKernelParams p) {
             ps[2 * g4 + 1] = Ty::pack(dv[2], dv[3]);
           }
         }
+        };
+        if (full) elementwise(std::false_type{});
+        else elementwise(std::true_type{});
         // dV^T += dO^T P and dK^T += Q^T dS over the block's two 16-query
         // slices, contracting in the order the score registers hold them.
 #pragma unroll
@@ -644,34 +651,47 @@ bwd_dq_kernel(const BwdKernelParams p) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
-      const bool full = j0 >= full_lo && j0 + BK - 1 <= full_hi;
-      uint32_t ps[KT][8];
+      // dS^T in place of the scores, then (only on steps that an edge crosses
+      // for the wave) zero where the key is not visible: P = 0 there, and a
+      // select drops whatever the unmasked formula gave (inf or NaN included).
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
-        for (int r2 = 0; r2 < 16; r2 += 2) {
-          float dv[2];
-#pragma unroll
-          for (int i = 0; i < 2; ++i) {
-            const int rr = r2 + i;
-            const int kk = j0 + 32 * kt + 8 * (rr >> 2) + 4 * hl + (rr & 3);
-            float x = s[kt][rr];
-            float gcap = 1.0f;
-            if constexpr (SOFTCAP) {
-              x = transform_score<true>(x, p.softcap_pre, p.softcap);
-              const float th = x * icap;
-              gcap = fmaf(-th, th, 1.0f);
-            }
-            if constexpr (ALIBI) x = fmaf(-slope, fabsf((float)(row + off - kk)), x);
-            if (!full) x = ((kk >= kmin) & (kk <= kmax)) ? x : -INFINITY;
-            const float pr = fast_exp2(fmaf(x, c2, -lse2));
-            float d = pr * (dp[kt][rr] - dd);
-            if constexpr (SOFTCAP) d *= gcap;
-            dv[i] = d;
+        for (int rr = 0; rr < 16; ++rr) {
+          float x = s[kt][rr];
+          float gcap = 1.0f;
+          if constexpr (SOFTCAP) {
+            x = transform_score<true>(x, p.softcap_pre, p.softcap);
+            const float th = x * icap;
+            gcap = fmaf(-th, th, 1.0f);
           }
-          ps[kt][r2 >> 1] = Ty::pack(dv[0], dv[1]);
+          if constexpr (ALIBI) {
+            const int kk = j0 + 32 * kt + 8 * (rr >> 2) + 4 * hl + (rr & 3);
+            x = fmaf(-slope, fabsf((float)(row + off - kk)), x);
+          }
+          const float pr = fast_exp2(fmaf(x, c2, -lse2));
+          float d = pr * (dp[kt][rr] - dd);
+          if constexpr (SOFTCAP) d *= gcap;
+          s[kt][rr] = d;
         }
       }
+      if (!(j0 >= full_lo && j0 + BK - 1 <= full_hi)) {
+        // key - kmin in [0, kmax - kmin] as one unsigned compare
+        const uint32_t span = (uint32_t)(kmax - kmin);
+        const int base = j0 + 4 * hl - kmin;
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) {
+            const uint32_t rel = (uint32_t)(base + 32 * kt + 8 * (rr >> 2) + (rr & 3));
+            s[kt][rr] = rel <= span ? s[kt][rr] : 0.0f;
+          }
+      }
+      uint32_t ps[KT][8];
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int r2 = 0; r2 < 16; r2 += 2) ps[kt][r2 >> 1] = Ty::pack(s[kt][r2], s[kt][r2 + 1]);
       // dQ^T += K^T dS^T, contracting over the step's keys in register order.
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
