@@ -71,6 +71,23 @@ __device__ __forceinline__ SeqRange seq_range(const BwdKernelParams& p, int b) {
 // so that every recomputed P of that row is exp2(-inf) = 0.
 __device__ __forceinline__ float lse_to_exp2(float l) { return l == -INFINITY ? INFINITY : l * kLog2e; }
 
+// Work item of a backward workgroup from its linear index.  The grid is
+// (tiles, heads, batch); items are dealt tile-rank-major -- every (head,
+// batch) column's rank-0 tile first, then rank 1, .. -- so the dispatcher
+// starts the heaviest causal tiles first and fills the tail with light ones
+// (in grid order the first wave of workgroups mixes all sizes and the
+// makespan grows by ~30% on a causal square).  Workgroup i runs on XCD i % 8,
+// so all tiles of a column share one XCD and its L2.
+struct TileRank {
+  int rank, head, b;
+};
+__device__ __forceinline__ TileRank tile_rank() {
+  const int cols = (int)gridDim.y * (int)gridDim.z;
+  const int lin = (int)blockIdx.x + (int)gridDim.x * ((int)blockIdx.y + (int)gridDim.y * (int)blockIdx.z);
+  const int c = lin % cols;
+  return TileRank{lin / cols, c % (int)gridDim.y, c / (int)gridDim.y};
+}
+
 // ---------------------------------------------------------------- D = rowsum(dO * O)
 // D/8 consecutive lanes cover one (token, head) row, 8 elements each.
 template <class Ty, int D>
@@ -255,10 +272,11 @@ bwd_dkdv_kernel(const BwdKernelParams p) {
   const int l32 = lane & 31;
   const int hl = lane >> 5;
 
-  const int kvh = blockIdx.y, b = blockIdx.z;
+  const TileRank tr = tile_rank();  // rank = key tile: the first tiles see the most queries
+  const int kvh = tr.head, b = tr.b;
   const SeqRange sr = seq_range(p, b);
   const int sq = sr.sq, sk = sr.sk, off = sk - sq;
-  const int n0 = blockIdx.x * BN;
+  const int n0 = tr.rank * BN;
   if (n0 >= sk) return;
   const int wl = p.window_left, wr = p.window_right;
   const int G = p.group;
@@ -555,10 +573,11 @@ bwd_dq_kernel(const BwdKernelParams p) {
   const int l32 = lane & 31;
   const int hl = lane >> 5;
 
-  const int head = blockIdx.y, b = blockIdx.z;
+  const TileRank tr = tile_rank();
+  const int head = tr.head, b = tr.b;
   const SeqRange sr = seq_range(p, b);
   const int sq = sr.sq, sk = sr.sk, off = sk - sq;
-  const int m0 = ((int)gridDim.x - 1 - (int)blockIdx.x) * BQ;  // longest (causal) tiles first
+  const int m0 = ((int)gridDim.x - 1 - tr.rank) * BQ;  // the last query tiles see the most keys
   if (m0 >= sq) return;
   const int kvh = head / p.group;
   const int wl = p.window_left, wr = p.window_right;
