@@ -8,8 +8,8 @@
 // step, the exp2-domain probabilities with the -inf guard, the first KV step
 // that never skips, and the split-KV variant of the row-block kernel).
 //
-// Layout of one workgroup (NW wave64s: 8 for the dense D = 128 tiles, 4 for
-// softcap, D = 64/256 and decode; 32 query rows per wave):
+// Layout of one workgroup (NW wave64s: 8 for large grids of D = 128 without
+// softcap and of D = 256 without ALiBi, 4 otherwise; 32 query rows per wave):
 //  * Each wave owns 32 query rows.  Scores are computed transposed,
 //    S^T = K Q^T, with v_mfma_f32_32x32x16: A = a 32-key slice of K read
 //    from LDS, B = the wave's Q fragment held in VGPRs for the whole loop.
@@ -282,13 +282,19 @@ fwd_tile_kernel(const FwdKernelParams p) {
   // prologue's wait (all vector memory) retires both together.
 
   // Per-lane LDS byte offsets of the MFMA operands (constant over the loop).
-  int k_off[DS];
+  // The swizzle changes only the low 4 bits of a chunk index, so with more
+  // than 16 chunks per row (D = 256) chunks 16.. repeat the offsets of 0..
+  // plus 256 bytes: only the first 16 chunks' offsets are kept in registers.
+  constexpr int KOFF = CH > 16 ? 8 : DS;  // distinct K offsets (k-steps cover 2 chunks)
+  constexpr int VOFF = CH > 16 ? 4 : DT;  // distinct V offsets (4 chunks per 32 dims)
+  int k_off[KOFF];
   {
     const int sw = chunk_swizzle(lane & 15) & SWZ_MASK;
 #pragma unroll
-    for (int t = 0; t < DS; ++t) k_off[t] = l32 * ROWB + (((2 * t + hl) ^ sw) << 4);
+    for (int t = 0; t < KOFF; ++t) k_off[t] = l32 * ROWB + (((2 * t + hl) ^ sw) << 4);
   }
-  int v_off[2][DT];
+  auto koff = [&](int t) __attribute__((always_inline)) { return k_off[t % KOFF] + (t / KOFF) * 256; };
+  int v_off[2][VOFF];
   {
     const int cl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
 #pragma unroll
@@ -296,7 +302,7 @@ fwd_tile_kernel(const FwdKernelParams p) {
       const int vrow = 4 * hl + 8 * r2 + ((lane & 15) >> 2);
       const int x = cl ^ (chunk_swizzle(vrow) & SWZ_MASK);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) v_off[r2][dt] = vrow * ROWB + (((4 * dt) ^ x) << 4) + ((lane & 1) << 3);
+      for (int dt = 0; dt < VOFF; ++dt) v_off[r2][dt] = vrow * ROWB + (((4 * dt) ^ x) << 4) + ((lane & 1) << 3);
     }
   }
 
@@ -383,7 +389,7 @@ fwd_tile_kernel(const FwdKernelParams p) {
     for (int t = 0; t < DS; ++t) {
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(k_cur + kt * 32 * ROWB + k_off[t]);
+        const u32x4 a = *reinterpret_cast<const u32x4*>(k_cur + kt * 32 * ROWB + koff(t));
 #pragma unroll
         for (int g = 0; g < QG; ++g) sc[g][kt] = Ty::mfma(a, qf[g][t], sc[g][kt]);
       }
@@ -491,8 +497,9 @@ fwd_tile_kernel(const FwdKernelParams p) {
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(v_cur + ks * 16 * ROWB + v_off[0][dt]));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(v_cur + ks * 16 * ROWB + v_off[1][dt]));
+        const int vo = ks * 16 * ROWB + (dt / VOFF) * 256;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(v_cur + vo + v_off[0][dt % VOFF]));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(v_cur + vo + v_off[1][dt % VOFF]));
         const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
         const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
         const u32x4 aop = {lo2[0], lo2[1], hi2[0], hi2[1]};
@@ -815,8 +822,22 @@ hipError_t launch_fwd_shape(const FwdKernelParams& p, int head_dim, hipStream_t 
       }
       return launch_fwd_t<Ty, 128, 64, 4, 1, CAP, 4, 2, 2, false, AL>(p, stream);
     }
-    case 256:
+    case 256: {
+      // 256 query rows at two waves per SIMD (8 waves of 256 registers: the
+      // 32-key step keeps the O accumulators, Q fragments and scores within
+      // 256) when the grid gives every CU two such workgroups; otherwise, for
+      // decode-shaped launches and with ALiBi (whose slopes would spill), 128
+      // rows at one wave per SIMD.  Variants 1 / 2 force 128 / 256 rows.
+      if constexpr (!AL) {
+        const int64_t packed = (int64_t)p.seqlen_q * (p.pack_gqa ? p.group : 1);
+        const int64_t heads_grid = p.pack_gqa ? p.heads_kv : p.heads_q;
+        const int64_t wgs256 = (packed + 255) / 256 * heads_grid * p.batch * p.num_splits;
+        const int v = fwd_variant();
+        if (v == 2 || (v != 1 && packed > 64 && wgs256 >= 2 * (int64_t)compute_units()))
+          return launch_fwd_t<Ty, 256, 32, 8, 1, CAP, 2, 2, 2, false, AL>(p, stream);
+      }
       return launch_fwd_t<Ty, 256, 32, 4, 1, CAP, 4, 1, 2, false, AL>(p, stream);
+    }
     default:
       return hipErrorInvalidValue;
   }

@@ -401,3 +401,19 @@ def test_exp2_fma_variant_small(case, monkeypatch):
     gate_check(np64(o), ro, np64(lse), rl, dtype, f"exp2-fma {seed}")
     if sq > sk and kw.get("causal"):
         assert torch.all(o[:, : sq - sk] == 0) and torch.all(torch.isneginf(lse[:, :, : sq - sk]))
+
+
+# ------------------------------------------------------------------ D = 256 with 256-row tiles
+
+@pytest.mark.parametrize("case", [(96, 1, 300, 300, 4, 2, 256, "fp16", dict(causal=True)),
+                                  (97, 2, 257, 190, 4, 4, 256, "bf16", dict(causal=False, softcap=5.0)),
+                                  (98, 1, 100, 300, 2, 1, 256, "bf16", dict(causal=True, window=(64, 0)))],
+                         ids=["s96", "s97", "s98"])
+def test_d256_256row_tile_small(case, monkeypatch):
+    """The 256-row D = 256 tile (eight waves, two per SIMD), forced on small ragged grids: causal
+    with GQA, softcap with Sq > Sk, and a window with Sq < Sk."""
+    monkeypatch.setenv("ATTN_MI355X_FWD_VARIANT", "2")
+    seed, b, sq, sk, hq, hkv, d, dtype, kw = case
+    print(f"[case] d256-256row seed={seed} b={b} sq={sq} sk={sk} hq={hq} hkv={hkv} d={d} {dtype} {kw}", flush=True)
+    o, lse, ro, rl = _dense_case(seed, b, sq, sk, hq, hkv, d, dtype, **kw)
+    gate_check(np64(o), ro, np64(lse), rl, dtype, f"d256-256row {seed}")
