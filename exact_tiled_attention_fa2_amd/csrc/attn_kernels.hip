@@ -748,8 +748,10 @@ hipError_t launch_fwd_t(FwdKernelParams p, hipStream_t stream) {
 }
 
 // Tile-shape variant for tuning sweeps (environment ATTN_MI355X_FWD_VARIANT,
-// read at every launch); 0 = default, 4 = P (and softcap's tanh) with exp2 on
-// the FMA pipe.
+// read at every launch); 0 = default; D = 128: 1 = 128 rows, 2 = 256 rows,
+// 3 = 32-key steps with four stages, 4 = P (and softcap's tanh) with exp2 on
+// the FMA pipe, 5 = 128 rows of 32-key steps at three waves per SIMD;
+// D = 256: 1 = 128 rows, 2 = 256 rows.
 int fwd_variant() {
   const char* e = getenv("ATTN_MI355X_FWD_VARIANT");
   return e ? atoi(e) : 0;
@@ -806,8 +808,14 @@ hipError_t launch_fwd_shape(const FwdKernelParams& p, int head_dim, hipStream_t 
           case 4:
             if (!CAP) return launch_fwd_t<Ty, 128, 64, 8, 1, CAP, 6, 2, 2, false, false, true>(p, stream);
             return launch_fwd_t<Ty, 128, 64, 4, 1, CAP, 4, 2, 2, false, false, true>(p, stream);
+          case 5: return launch_fwd_t<Ty, 128, 32, 4, 1, CAP, 2, 3, 2>(p, stream);
           default: break;
         }
+        // Softcap and varlen launches: 128-row tiles of 32-key steps at three
+        // waves per SIMD (166 registers; three workgroups per CU, each SIMD
+        // interleaving waves of three tiles) -- the VALU-heavier softcap step
+        // and the uneven varlen tiles hide better behind the third wave.
+        if (CAP || p.cu_seqlens_q != nullptr) return launch_fwd_t<Ty, 128, 32, 4, 1, CAP, 2, 3, 2>(p, stream);
       }
       // 256 query rows per workgroup (8 waves, one workgroup per CU) halve
       // the K/V re-reads from L2 per FLOP and win on dense and varlen
