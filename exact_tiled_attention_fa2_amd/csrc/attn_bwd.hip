@@ -546,10 +546,9 @@ bwd_dkdv_kernel(const BwdKernelParams p) {
 }
 
 // ---------------------------------------------------------------- dQ
-template <class Ty, int D, bool SOFTCAP, bool ALIBI>
-__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+template <class Ty, int D, bool SOFTCAP, bool ALIBI, int NW = 4>
+__global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(2, 2)))
 bwd_dq_kernel(const BwdKernelParams p) {
-  constexpr int NW = 4;
   constexpr int NT = NW * 64;
   constexpr int BK = 64;            // keys per step
   constexpr int BQ = 32 * NW;       // queries per workgroup
@@ -748,8 +747,9 @@ bwd_dq_kernel(const BwdKernelParams p) {
   }
 }
 
-// dK/dV kernel variant for sweeps (environment ATTN_MI355X_BWD_VARIANT):
-// 0 = one pass at 4 waves (default, measured faster), 1 = two passes at 8 waves.
+// Backward variant for sweeps (environment ATTN_MI355X_BWD_VARIANT): 0 = the
+// default; 1 = dK/dV in two passes at 8 waves; 2 / 3 = dQ with 8 / 4 waves
+// (256 / 128 queries per workgroup).
 int bwd_variant() {
   static const int v = [] {
     const char* e = getenv("ATTN_MI355X_BWD_VARIANT");
@@ -778,8 +778,18 @@ hipError_t launch_bwd_t(const BwdKernelParams& p, hipStream_t stream) {
     }
   }
   if (p.seqlen_q > 0) {
-    const dim3 grid((unsigned)((p.seqlen_q + 127) / 128), p.heads_q, p.batch);
-    hipLaunchKernelGGL((bwd_dq_kernel<Ty, D, SOFTCAP, ALIBI>), grid, dim3(256), 0, stream, p);
+    // 256 queries per workgroup (8 waves, two per SIMD; half the K/V re-reads
+    // from L2) when that grid gives every CU two workgroups, else 128
+    // (twice the workgroups); variant 2 forces 256, 3 forces 128.
+    const int64_t wgs256 = (int64_t)((p.seqlen_q + 255) / 256) * p.heads_q * p.batch;
+    const int v = bwd_variant();
+    if (v == 2 || (v != 3 && wgs256 >= 2 * (int64_t)compute_units())) {
+      const dim3 grid((unsigned)((p.seqlen_q + 255) / 256), p.heads_q, p.batch);
+      hipLaunchKernelGGL((bwd_dq_kernel<Ty, D, SOFTCAP, ALIBI, 8>), grid, dim3(512), 0, stream, p);
+    } else {
+      const dim3 grid((unsigned)((p.seqlen_q + 127) / 128), p.heads_q, p.batch);
+      hipLaunchKernelGGL((bwd_dq_kernel<Ty, D, SOFTCAP, ALIBI>), grid, dim3(256), 0, stream, p);
+    }
   }
   return hipGetLastError();
 }

@@ -94,6 +94,10 @@ struct BwdKernelParams {
 
 constexpr int kBlockM = 128;  // nominal query rows per workgroup (split-count heuristic)
 
+// Compute units of the current device (queried once per device; 256 if the
+// query fails).
+int compute_units();
+
 // Host-side launchers (return a hipError_t).
 hipError_t launch_fwd(const FwdKernelParams& p, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, int dtype, int head_dim, hipStream_t stream);

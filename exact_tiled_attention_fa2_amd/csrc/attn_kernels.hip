@@ -757,17 +757,6 @@ int fwd_variant() {
   return e ? atoi(e) : 0;
 }
 
-// Compute units of the current device (queried once per device).
-int compute_units() {
-  static int cus[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
-    cus[dev] = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) ? n : 256;
-  }
-  return cus[dev];
-}
 
 // Decode tile variant for tuning sweeps (environment ATTN_MI355X_DEC_VARIANT); 0 = default.
 int dec_variant() {
@@ -882,6 +871,18 @@ hipError_t launch_combine_dtype(const CombineParams& p, int head_dim, hipStream_
 }
 
 }  // namespace
+
+// Compute units of the current device (queried once per device).
+int compute_units() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    cus[dev] = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) ? n : 256;
+  }
+  return cus[dev];
+}
 
 hipError_t launch_fwd(const FwdKernelParams& p, int dtype, int head_dim, hipStream_t stream) {
   return dtype == 1 ? launch_fwd_dtype<TypeBF16>(p, head_dim, stream)
