@@ -750,12 +750,10 @@ bwd_dq_kernel(const BwdKernelParams p) {
 // Backward variant for sweeps (environment ATTN_MI355X_BWD_VARIANT): 0 = the
 // default; 1 = dK/dV in two passes at 8 waves; 2 / 3 = dQ with 8 / 4 waves
 // (256 / 128 queries per workgroup).
+// Read at every launch.
 int bwd_variant() {
-  static const int v = [] {
-    const char* e = getenv("ATTN_MI355X_BWD_VARIANT");
-    return e ? atoi(e) : 0;
-  }();
-  return v;
+  const char* e = getenv("ATTN_MI355X_BWD_VARIANT");
+  return e ? atoi(e) : 0;
 }
 
 // D first (both gradient kernels read it), then dK/dV, then dQ; a kernel

@@ -157,3 +157,43 @@ def test_bwd_finite_2k(dtype):
     o, lse = eng.attn_fwd(q, k, v, causal=True)
     for g in eng.attn_bwd(q, k, v, o, lse, do, causal=True):
         assert torch.isfinite(g).all()
+
+
+@pytest.mark.parametrize("variant", ["1", "2", "3"])
+def test_bwd_variants(variant, monkeypatch):
+    """The selectable kernel shapes (two-pass dK/dV; dQ with 256 / 128 queries per workgroup) on a
+    ragged GQA causal case with a window and softcap."""
+    monkeypatch.setenv("ATTN_MI355X_BWD_VARIANT", variant)
+    print(f"[case] bwd variant {variant}", flush=True)
+    eng = _eng()
+    kw = dict(causal=True, window=(100, 0), softcap=20.0)
+    q, k, v = W.make_dense(93, 2, 333, 333, 4, 2, 128, "bf16", device="cuda")
+    do = _dout(93, tuple(q.shape), "bf16")
+    o, lse = eng.attn_fwd(q, k, v, **kw)
+    dq, dk, dv = eng.attn_bwd(q, k, v, o, lse, do, **kw)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.attention_bwd_ref(np64(q), np64(k), np64(v), np64(do), **kw)
+    grad_check(np64(dq), rq, "bf16", f"variant {variant} dQ")
+    grad_check(np64(dk), rk, "bf16", f"variant {variant} dK")
+    grad_check(np64(dv), rv, "bf16", f"variant {variant} dV")
+
+
+def test_bwd_headline_sampled():
+    """The benchmarked backward shape (bf16, B=4, Sq=Sk=2048, 16 heads, D=128, causal) in its default
+    launch configuration (256-query dQ tiles), against the oracle on three sampled (batch, head)
+    pairs in full."""
+    print("[case] bwd headline sampled", flush=True)
+    eng = _eng()
+    c = W.WORKLOADS["bwd_cfg2_bf16_causal_2k"]
+    b, s, h, d = c["batch"], c["seqlen_q"], c["heads_q"], c["head_dim"]
+    q, k, v = W.make_dense(c["seed"], b, s, s, h, h, d, c["dtype"], device="cuda")
+    do = _dout(c["seed"], tuple(q.shape), c["dtype"])
+    o, lse = eng.attn_fwd(q, k, v, causal=True)
+    dq, dk, dv = eng.attn_bwd(q, k, v, o, lse, do, causal=True)
+    torch.cuda.synchronize()
+    for bi, hi in ((0, 0), (1, 7), (3, 15)):
+        sl = (slice(bi, bi + 1), slice(None), slice(hi, hi + 1))
+        rq, rk, rv = oracle.attention_bwd_ref(np64(q[sl]), np64(k[sl]), np64(v[sl]), np64(do[sl]), causal=True)
+        grad_check(np64(dq[sl]), rq, c["dtype"], f"headline ({bi},{hi}) dQ")
+        grad_check(np64(dk[sl]), rk, c["dtype"], f"headline ({bi},{hi}) dK")
+        grad_check(np64(dv[sl]), rv, c["dtype"], f"headline ({bi},{hi}) dV")
