@@ -412,9 +412,11 @@ bwd_dkdv_kernel(const BwdKernelParams p) {
           }
         }
         // At one wave per SIMD the transposed operands of the block's two
-        // 16-query slices are read while the elementwise work below runs; at
-        // two, the other wave covers their latency and the registers are
-        // needed elsewhere.
+        // 16-query slices are read under the S / dP MFMAs (two reads after
+        // each MFMA: a wave keeps at most 15 LDS reads in flight, so issued
+        // in one batch they would stall it), ahead of the elementwise work;
+        // at two waves per SIMD the other wave covers their latency and the
+        // registers are needed elsewhere.
         constexpr bool TR_AHEAD = WPE == 1;
         u32x4 tg[2][DT], tq[2][DT];
         if constexpr (TR_AHEAD) {
@@ -424,6 +426,16 @@ bwd_dkdv_kernel(const BwdKernelParams p) {
             for (int dt = 0; dt < DT; ++dt) {
               if constexpr (DO_DV) tg[k2][dt] = tr_operand<D>(g_cur, oo, 2 * qb + k2, dt);
               if constexpr (DO_DK) tq[k2][dt] = tr_operand<D>(q_cur, oo, 2 * qb + k2, dt);
+            }
+          }
+          if constexpr (RB == DS) {
+            constexpr int NM = DS * (DO_DK ? 2 : 1);                          // S (and dP) MFMAs
+            constexpr int NR = 4 * DT * ((DO_DV ? 1 : 0) + (DO_DK ? 1 : 0));  // transposing reads
+            static_assert(NR % NM == 0, "reads spread evenly over the MFMAs");
+#pragma unroll
+            for (int i = 0; i < NM; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x100, NR / NM, 0);
             }
           }
         }
