@@ -296,7 +296,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the forward shards over batch x KV-head groups with no exchange; see the design notes). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)

@@ -214,7 +214,7 @@ def gather_pages(pool, table_row, n):
     pool [num_pages, page_size, Hkv, D]; table_row[i] is the page holding keys
     i*page_size .. (i+1)*page_size - 1 (the paged KV cache of the Python API,
     "flash-attention" project survey page, csrc/flash_attn entry; the layout
-    is this build's reading).  Only the pages covering the first n keys are
+    is the reading taken here).  Only the pages covering the first n keys are
     read.
     """
     page = pool.shape[1]
