@@ -77,7 +77,8 @@ __device__ __forceinline__ float lse_to_exp2(float l) { return l == -INFINITY ? 
 // starts the heaviest causal tiles first and fills the tail with light ones
 // (in grid order the first wave of workgroups mixes all sizes and the
 // makespan grows by ~30% on a causal square).  Workgroup i runs on XCD i % 8,
-// so all tiles of a column share one XCD and its L2.
+// so when the column count is a multiple of 8 all tiles of a column share
+// one XCD and its L2.
 struct TileRank {
   int rank, head, b;
 };
