@@ -13,7 +13,7 @@ def np64(t):
 
 
 def gate_check(out, ref, lse=None, lse_ref=None, dtype="bf16", what=""):
-    """Assert the spec gates: rel_Linf (dtype), cosine >= 0.9995, LSE abs <= 1e-3."""
+    """Assert the parity gates: rel_Linf (per dtype), cosine >= 0.9995, LSE abs error <= 1e-3."""
     res = oracle.compare(out, ref, lse, lse_ref, dtype=dtype)
     print(f"[parity] {what}: {res}", flush=True)
     assert res["finite"], f"{what}: non-finite output"
