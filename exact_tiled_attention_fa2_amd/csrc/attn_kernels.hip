@@ -9,7 +9,8 @@
 // that never skips, and the split-KV variant of the row-block kernel).
 //
 // Layout of one workgroup (NW wave64s: 8 for large grids of D = 128 without
-// softcap and of D = 256 without ALiBi, 4 otherwise; 32 query rows per wave):
+// softcap and of D = 256 without ALiBi, 4 otherwise, at two or three waves
+// per SIMD; 32 query rows per wave):
 //  * Each wave owns 32 query rows.  Scores are computed transposed,
 //    S^T = K Q^T, with v_mfma_f32_32x32x16: A = a 32-key slice of K read
 //    from LDS, B = the wave's Q fragment held in VGPRs for the whole loop.
@@ -751,7 +752,7 @@ hipError_t launch_fwd_t(FwdKernelParams p, hipStream_t stream) {
 // read at every launch); 0 = default; D = 128: 1 = 128 rows, 2 = 256 rows,
 // 3 = 32-key steps with four stages, 4 = P (and softcap's tanh) with exp2 on
 // the FMA pipe, 5 = 128 rows of 32-key steps at three waves per SIMD;
-// D = 256: 1 = 128 rows, 2 = 256 rows.
+// D = 256: 1 = 128 rows, 2 = 256 rows; D = 64: 1 = two waves per SIMD.
 int fwd_variant() {
   const char* e = getenv("ATTN_MI355X_FWD_VARIANT");
   return e ? atoi(e) : 0;
@@ -778,8 +779,16 @@ hipError_t launch_fwd_shape(const FwdKernelParams& p, int head_dim, hipStream_t 
     }
   }
   switch (head_dim) {
-    case 64:
+    case 64: {
+      // 128-row tiles at three waves per SIMD (129 registers at D = 64;
+      // three workgroups per CU) except for decode-shaped launches and ALiBi;
+      // variant 1 forces the two-wave tile.
+      if constexpr (!AL) {
+        const int64_t packed = (int64_t)p.seqlen_q * (p.pack_gqa ? p.group : 1);
+        if (packed > 64 && fwd_variant() != 1) return launch_fwd_t<Ty, 64, 64, 4, 1, CAP, 2, 3, 2>(p, stream);
+      }
       return launch_fwd_t<Ty, 64, 64, 4, 1, CAP, 4, 2, 2, false, AL>(p, stream);
+    }
     case 128: {
       const int64_t packed = (int64_t)p.seqlen_q * (p.pack_gqa ? p.group : 1);
       if (packed <= 64) {
