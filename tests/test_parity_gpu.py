@@ -417,3 +417,24 @@ def test_d256_256row_tile_small(case, monkeypatch):
     print(f"[case] d256-256row seed={seed} b={b} sq={sq} sk={sk} hq={hq} hkv={hkv} d={d} {dtype} {kw}", flush=True)
     o, lse, ro, rl = _dense_case(seed, b, sq, sk, hq, hkv, d, dtype, **kw)
     gate_check(np64(o), ro, np64(lse), rl, dtype, f"d256-256row {seed}")
+
+
+# ------------------------------------------------------------------ chunked prefill into a cache
+
+@pytest.mark.parametrize("case", [(58, 64, "fp16", 1), (59, 64, "bf16", 3), (60, 128, "bf16", 4),
+                                  (61, 128, "fp16", 7)], ids=["s58", "s59", "s60", "s61"])
+def test_kvcache_chunked_prefill(case):
+    """A 200-query chunk against caches of random valid length (NaN past it), causal and aligned to
+    the end of each sequence, in split mode: the prefill tiles writing fp32 partials for the combine."""
+    seed, d, dtype, splits = case
+    print(f"[case] chunked prefill seed={seed} d={d} {dtype} splits={splits}", flush=True)
+    q, kc, vc, lens = W.make_kvcache(seed, 2, 200, 900, 8, 2, d, dtype, device="cuda", random_lengths=True)
+    lens = torch.clamp(lens, min=200)  # every sequence holds at least the chunk
+    for b in range(2):
+        kc[b, int(lens[b]):] = float("nan")
+        vc[b, int(lens[b]):] = float("nan")
+    o, lse = _eng().attn_fwd_kvcache(q, kc, vc, cache_seqlens=lens, num_splits=splits, causal=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_kvcache_ref(np64(q), np64(kc), np64(vc), cache_seqlens=lens.cpu().numpy(),
+                                          causal=True)
+    gate_check(np64(o), ro, np64(lse), rl, dtype, f"chunked prefill {seed}")
