@@ -510,10 +510,9 @@ bwd_dkdv_kernel(const BwdKernelParams p) {
         }
       }
     }
-    if (r + 2 < n) wait_vmem_le<2 * Copier::LOADS>();
-    else wait_vmem();
     if (r + 1 < n) stage_rows((r + 1) & 1);
-    __syncthreads();
+    if (r + 2 < n) barrier_vmem_le<2 * Copier::LOADS>();
+    else barrier_vmem_le<0>();
     h = h1;
     q0 = q1;
   };
@@ -526,10 +525,9 @@ bwd_dkdv_kernel(const BwdKernelParams p) {
       advance(h1, q1);
       issue(h1, q1, lds_q1, lds_g1);
     }
-    if (n > 1) wait_vmem_le<2 * Copier::LOADS>();
-    else wait_vmem();
     stage_rows(0);
-    __syncthreads();
+    if (n > 1) barrier_vmem_le<2 * Copier::LOADS>();
+    else barrier_vmem_le<0>();
     int r = 0;
     for (; r + 3 <= n; r += 3) {
       step(std::integral_constant<int, 0>{}, r);

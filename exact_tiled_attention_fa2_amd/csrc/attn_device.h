@@ -85,5 +85,22 @@ __device__ __forceinline__ void wait_vmem_le() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Workgroup barrier of a tile pipeline: this wave's LDS reads and writes have
+// retired (lgkmcnt(0)) and at most N vector-memory operations -- the newest,
+// i.e. HBM -> LDS copies for later steps -- are still in flight.
+// __syncthreads() would also drain those (its release fence waits for
+// vmcnt(0)), so a copy issued two steps ahead would have to land within the
+// current step.  The empty asm statements keep the compiler from moving
+// memory accesses across the barrier; the explicit wait gives the ordering
+// the hardware needs.
+template <int N>
+__device__ __forceinline__ void barrier_vmem_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 }  // namespace
 }  // namespace attn

@@ -329,8 +329,14 @@ fwd_tile_kernel(const FwdKernelParams p) {
   }
   // Page holding KV step blk of a paged cache (clamped into the pool); a
   // tile never straddles pages (the page size is a multiple of 64).
+  // The lookup is wave-uniform and the table read-only, so it goes through
+  // the scalar cache: a scalar load is counted by lgkmcnt, and waiting for its
+  // result never drains the HBM -> LDS copies of later steps (a vector load
+  // issued after them would).
+  typedef const __attribute__((address_space(4))) int* ConstIntPtr;
+  const ConstIntPtr btab = (ConstIntPtr)(uintptr_t)p.block_table;
   auto page_of = [&](int blk) __attribute__((always_inline)) -> int {
-    return min(max(p.block_table[(int64_t)b * p.bt_stride + blk * BK / p.page_size], 0), p.num_pages - 1);
+    return min(max(btab[(int64_t)b * p.bt_stride + blk * BK / p.page_size], 0), p.num_pages - 1);
   };
   auto copy_tile = [&](const char* gbase, int64_t rowb, int64_t pageb, char* tile, int blk, int pg)
       __attribute__((always_inline)) {
@@ -559,16 +565,15 @@ fwd_tile_kernel(const FwdKernelParams p) {
     // Copies are issued in step order, 2 LOADS per step per lane.
     const int later = min(NSTAGE - 2, n - 2 - r);  // steps r+2.. with copies in flight
     if constexpr (NSTAGE >= 4) {
-      if (later >= 2) wait_vmem_le<4 * LOADS>();
-      else if (later == 1) wait_vmem_le<2 * LOADS>();
-      else wait_vmem();
+      if (later >= 2) barrier_vmem_le<4 * LOADS>();
+      else if (later == 1) barrier_vmem_le<2 * LOADS>();
+      else barrier_vmem_le<0>();
     } else if constexpr (NSTAGE == 3) {
-      if (later >= 1) wait_vmem_le<2 * LOADS>();
-      else wait_vmem();
+      if (later >= 1) barrier_vmem_le<2 * LOADS>();
+      else barrier_vmem_le<0>();
     } else {
-      wait_vmem();
+      barrier_vmem_le<0>();
     }
-    __syncthreads();
   };
 
   if (n > 0) {
@@ -596,13 +601,12 @@ fwd_tile_kernel(const FwdKernelParams p) {
     if constexpr (NSTAGE > 2) {
       // step 0's tiles must have landed; later prologue copies may still fly
       const int later = min(NSTAGE - 2, n - 1);
-      if (NSTAGE >= 4 && later >= 2) wait_vmem_le<4 * LOADS>();
-      else if (later >= 1) wait_vmem_le<2 * LOADS>();
-      else wait_vmem();
+      if (NSTAGE >= 4 && later >= 2) barrier_vmem_le<4 * LOADS>();
+      else if (later >= 1) barrier_vmem_le<2 * LOADS>();
+      else barrier_vmem_le<0>();
     } else {
-      wait_vmem();
+      barrier_vmem_le<0>();
     }
-    __syncthreads();
     int r = 0;
     for (; r + NSTAGE <= n; r += NSTAGE) {
       step(std::integral_constant<int, 0>{}, r);
@@ -794,6 +798,7 @@ hipError_t launch_fwd_shape(const FwdKernelParams& p, int head_dim, hipStream_t 
       if (packed <= 64) {
         // Decode-shaped launches (few live rows; the KV stream dominates).
         if constexpr (!AL) {
+          // Variant 1: 32-key steps, four stages (three steps' copies in flight).
           if (dec_variant() == 1) return launch_fwd_t<Ty, 128, 32, 4, 1, CAP, 4, 2, 4>(p, stream);
         }
         return launch_fwd_t<Ty, 128, 64, 4, 1, CAP, 4, 2, 2, false, AL>(p, stream);
