@@ -764,12 +764,10 @@ int fwd_variant() {
 
 
 // Decode tile variant for tuning sweeps (environment ATTN_MI355X_DEC_VARIANT); 0 = default.
+// Read at every launch.
 int dec_variant() {
-  static const int v = [] {
-    const char* e = getenv("ATTN_MI355X_DEC_VARIANT");
-    return e ? atoi(e) : 0;
-  }();
-  return v;
+  const char* e = getenv("ATTN_MI355X_DEC_VARIANT");
+  return e ? atoi(e) : 0;
 }
 
 template <class Ty, bool CAP, bool AL>

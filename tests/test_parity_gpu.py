@@ -217,6 +217,21 @@ def test_kvcache_small_nan_tail(case):
     gate_check(np64(o), ro, np64(lse), rl, dtype, f"kvcache {seed}")
 
 
+@pytest.mark.parametrize("case", DECODE_SMALL[:4], ids=[f"s{c[0]}" for c in DECODE_SMALL[:4]])
+def test_kvcache_four_stage_tile(case, monkeypatch):
+    """The selectable decode tile of 32-key steps with four copy stages (three steps' K/V copies in
+    flight at each step end) on the D = 128 decode cases: the oracle's answer at every split count."""
+    monkeypatch.setenv("ATTN_MI355X_DEC_VARIANT", "1")
+    seed, b, sq, sk, hq, hkv, d, dtype, splits = case
+    print(f"[case] kvcache four-stage seed={seed} splits={splits}", flush=True)
+    q, kc, vc, lens = W.make_kvcache(seed, b, sq, sk, hq, hkv, d, dtype, device="cuda",
+                                     random_lengths=True, nan_tail=True)
+    o, lse = _eng().attn_fwd_kvcache(q, kc, vc, cache_seqlens=lens, num_splits=splits, causal=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_kvcache_ref(np64(q), np64(kc), np64(vc), lens.cpu().numpy(), causal=True)
+    gate_check(np64(o), ro, np64(lse), rl, dtype, f"kvcache four-stage {seed}")
+
+
 PAGED_SMALL = [
     (61, 3, 1, 1000, 8, 2, 128, "bf16", 0, 64),
     (62, 2, 3, 777, 8, 8, 64, "fp16", 5, 128),
@@ -417,6 +432,22 @@ def test_d256_256row_tile_small(case, monkeypatch):
     print(f"[case] d256-256row seed={seed} b={b} sq={sq} sk={sk} hq={hq} hkv={hkv} d={d} {dtype} {kw}", flush=True)
     o, lse, ro, rl = _dense_case(seed, b, sq, sk, hq, hkv, d, dtype, **kw)
     gate_check(np64(o), ro, np64(lse), rl, dtype, f"d256-256row {seed}")
+
+
+# ------------------------------------------------------------------ four copy stages (D = 128)
+
+@pytest.mark.parametrize("case", [(99, 2, 333, 333, 8, 2, 128, "bf16", dict(causal=True)),
+                                  (100, 1, 130, 517, 4, 4, 128, "fp16", dict(causal=False, softcap=30.0)),
+                                  (101, 1, 300, 300, 4, 1, 128, "bf16", dict(causal=True, window=(100, 0)))],
+                         ids=["s99", "s100", "s101"])
+def test_four_stage_tile_small(case, monkeypatch):
+    """The 32-key tile with four copy stages (each step end keeps the next two steps' K/V copies in
+    flight), forced on small ragged grids: causal GQA, softcap with Sq < Sk, and a sliding window."""
+    monkeypatch.setenv("ATTN_MI355X_FWD_VARIANT", "3")
+    seed, b, sq, sk, hq, hkv, d, dtype, kw = case
+    print(f"[case] four-stage seed={seed} b={b} sq={sq} sk={sk} hq={hq} hkv={hkv} d={d} {dtype} {kw}", flush=True)
+    o, lse, ro, rl = _dense_case(seed, b, sq, sk, hq, hkv, d, dtype, **kw)
+    gate_check(np64(o), ro, np64(lse), rl, dtype, f"four-stage {seed}")
 
 
 # ------------------------------------------------------------------ chunked prefill into a cache
