@@ -75,6 +75,14 @@ __device__ __forceinline__ void dma16(const void* g, const char* lds) {
   __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(g),
                                    (__attribute__((address_space(3))) void*)(lds), 16, 0, 0);
 }
+// The same copy with a cache-policy operand (gfx950 CPOL bits: 1 = sc0,
+// 2 = nt, 16 = sc1).  CPOL_NT marks data that is streamed once.
+constexpr int CPOL_NT = 2;
+template <int CPOL>
+__device__ __forceinline__ void dma16_pol(const void* g, const char* lds) {
+  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(g),
+                                   (__attribute__((address_space(3))) void*)(lds), 16, 0, CPOL);
+}
 
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
