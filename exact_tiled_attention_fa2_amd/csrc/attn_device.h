@@ -86,13 +86,6 @@ __device__ __forceinline__ void dma16_pol(const void* g, const char* lds) {
 
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
-// s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt in bits 3:0 and 15:14), other counters untouched.
-template <int N>
-__device__ __forceinline__ void wait_vmem_le() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 // Workgroup barrier of a tile pipeline: this wave's LDS reads and writes have
 // retired (lgkmcnt(0)) and at most N vector-memory operations -- the newest,
 // i.e. HBM -> LDS copies for later steps -- are still in flight.
@@ -101,6 +94,7 @@ __device__ __forceinline__ void wait_vmem_le() {
 // current step.  The empty asm statements keep the compiler from moving
 // memory accesses across the barrier; the explicit wait gives the ordering
 // the hardware needs.
+// (s_waitcnt gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8.)
 template <int N>
 __device__ __forceinline__ void barrier_vmem_le() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
