@@ -165,7 +165,7 @@ __device__ __forceinline__ float exp2_fma(float x) {
 }
 
 template <class Ty, int D, int BK, int NW, int QG, bool SOFTCAP, int LEAD, int WPE, int NSTAGE = 2,
-          bool PAGED = false, bool ALIBI = false, bool EXPP = false, int CPOL = 0>
+          bool PAGED = false, bool ALIBI = false, bool EXPP = false, int CPOL = 0, bool EPI_STAGE = true>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(WPE, WPE)))
 fwd_tile_kernel(const FwdKernelParams p) {
   constexpr int NT = NW * 64;           // threads per workgroup
@@ -622,6 +622,74 @@ fwd_tile_kernel(const FwdKernelParams p) {
   }
 
   // ---------------------------------------------------------------- epilogue
+  // Staged store of O: a lane holds one query row, so direct 8-byte stores
+  // scatter over 32 rows per instruction.  The wave instead writes its
+  // 32 x D block into LDS (the K/V stage buffers are idle once the last
+  // step's barrier has passed: every wave's reads of them have retired) and
+  // reads it back row-contiguous, so that 64 / (D / 8) whole rows leave per
+  // 16-byte-per-lane store.  Needs 16-byte aligned O rows.
+  constexpr int REGB = 32 * ROWB;                        // one wave's 32-row block
+  constexpr int RPBUF = TILEB / REGB;                    // blocks per stage buffer
+  constexpr bool STAGED_O = EPI_STAGE && QG == 1 && RPBUF >= 1 && NW <= 2 * NSTAGE * RPBUF;
+  if constexpr (STAGED_O) {
+    const bool aligned = ((reinterpret_cast<uintptr_t>(p.o) & 15) | ((p.o_batch | p.o_row | p.o_head) & 7)) == 0;
+    if (p.o_part == nullptr && aligned && n > 0) {
+      char* reg;
+      {
+        const int bi = wave / RPBUF;                      // stage buffer: k0, k1, .., v0, v1, ..
+        char* base;
+        if (bi == 0) base = kbuf(std::integral_constant<int, 0>{});
+        else if (bi == 1) base = kbuf(std::integral_constant<int, 1>{});
+        else if (bi == NSTAGE) base = vbuf(std::integral_constant<int, 0>{});
+        else base = vbuf(std::integral_constant<int, 1>{});
+        if constexpr (NSTAGE > 2) {
+          if (bi == 2) base = kbuf(std::integral_constant<int, 2>{});
+          if (bi == NSTAGE + 2) base = vbuf(std::integral_constant<int, 2>{});
+        }
+        if constexpr (NSTAGE > 3) {
+          if (bi == 3) base = kbuf(std::integral_constant<int, 3>{});
+          if (bi == NSTAGE + 3) base = vbuf(std::integral_constant<int, 3>{});
+        }
+        reg = base + (wave % RPBUF) * REGB;
+      }
+      const float l_tot = l_run[0] + __shfl_xor(l_run[0], 32);
+      const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+      const float mgf = (m_run[0] == -INFINITY) ? 0.0f : m_run[0];
+      const float lse_val = l_tot > 0.0f ? mgf * p.scale_ln + logf(l_tot) : -INFINITY;
+      constexpr int SW = CH < 16 ? CH - 1 : 15;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int c = 4 * dt + g4;  // 16-byte chunk of dims 32 dt + 8 g4 .. + 7
+          u32x2 w;
+          w[0] = Ty::pack(acc[0][dt][4 * g4 + 0] * inv, acc[0][dt][4 * g4 + 1] * inv);
+          w[1] = Ty::pack(acc[0][dt][4 * g4 + 2] * inv, acc[0][dt][4 * g4 + 3] * inv);
+          *reinterpret_cast<u32x2*>(reg + l32 * ROWB + ((c ^ (l32 & SW)) << 4) + 8 * hl) = w;
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes done
+      asm volatile("" ::: "memory");
+      constexpr int RPI = 64 / CH;  // rows per store instruction
+#pragma unroll
+      for (int it = 0; it < 32 / RPI; ++it) {
+        const int rr = it * RPI + lane / CH;
+        const int cc = lane % CH;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(reg + rr * ROWB + ((cc ^ (rr & SW)) << 4));
+        const int rrow = __shfl(row[0], rr);
+        const int rhq = __shfl(hq[0], rr);
+        const int rvalid = __shfl((int)q_valid[0], rr);
+        if (rvalid) {
+          uint16_t* dst = reinterpret_cast<uint16_t*>(p.o) + (int64_t)b * p.o_batch +
+                          (int64_t)(q_start + rrow) * p.o_row + (int64_t)rhq * p.o_head + 8 * cc;
+          *reinterpret_cast<u32x4*>(dst) = v;
+        }
+      }
+      if (q_valid[0] && hl == 0 && p.lse != nullptr)
+        p.lse[(int64_t)b * p.lse_batch + (int64_t)hq[0] * p.lse_head + q_start + row[0]] = lse_val;
+      return;
+    }
+  }
 #pragma unroll
   for (int g = 0; g < QG; ++g) {
     const float l_tot = l_run[g] + __shfl_xor(l_run[g], 32);
@@ -733,7 +801,7 @@ int col_group_for(const FwdKernelParams& p, int heads_grid, int nz, int head_dim
 }
 
 template <class Ty, int D, int BK, int NW, int QG, bool SOFTCAP, int LEAD, int WPE, int NSTAGE = 2,
-          bool PAGED = false, bool ALIBI = false, bool EXPP = false, int CPOL = 0>
+          bool PAGED = false, bool ALIBI = false, bool EXPP = false, int CPOL = 0, bool EPI_STAGE = true>
 hipError_t launch_fwd_t(FwdKernelParams p, hipStream_t stream) {
   constexpr int BQ = 32 * NW * QG;
   const int64_t rows = (int64_t)p.seqlen_q * (p.pack_gqa ? p.group : 1);
@@ -747,7 +815,7 @@ hipError_t launch_fwd_t(FwdKernelParams p, hipStream_t stream) {
     p.xcd_chunk = (p.cu_seqlens_q == nullptr && per_xcd > 0) ? per_xcd : 1;
   }
   dim3 grid(p.num_m_tiles, heads_grid, p.batch * p.num_splits);
-  hipLaunchKernelGGL((fwd_tile_kernel<Ty, D, BK, NW, QG, SOFTCAP, LEAD, WPE, NSTAGE, PAGED, ALIBI, EXPP, CPOL>), grid,
+  hipLaunchKernelGGL((fwd_tile_kernel<Ty, D, BK, NW, QG, SOFTCAP, LEAD, WPE, NSTAGE, PAGED, ALIBI, EXPP, CPOL, EPI_STAGE>), grid,
                      dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
 }
@@ -755,7 +823,8 @@ hipError_t launch_fwd_t(FwdKernelParams p, hipStream_t stream) {
 // Tile-shape variant for tuning sweeps (environment ATTN_MI355X_FWD_VARIANT,
 // read at every launch); 0 = default; D = 128: 1 = 128 rows, 2 = 256 rows,
 // 3 = 32-key steps with four stages, 4 = P (and softcap's tanh) with exp2 on
-// the FMA pipe, 5 = 128 rows of 32-key steps at three waves per SIMD;
+// the FMA pipe, 5 = 128 rows of 32-key steps at three waves per SIMD, 6 = 256
+// rows with O stored directly from the accumulator layout (no LDS staging);
 // D = 256: 1 = 128 rows, 2 = 256 rows; D = 64: 1 = two waves per SIMD.
 int fwd_variant() {
   const char* e = getenv("ATTN_MI355X_FWD_VARIANT");
@@ -824,6 +893,7 @@ hipError_t launch_fwd_shape(const FwdKernelParams& p, int head_dim, hipStream_t 
             if (!CAP) return launch_fwd_t<Ty, 128, 64, 8, 1, CAP, 6, 2, 2, false, false, true>(p, stream);
             return launch_fwd_t<Ty, 128, 64, 4, 1, CAP, 4, 2, 2, false, false, true>(p, stream);
           case 5: return launch_fwd_t<Ty, 128, 32, 4, 1, CAP, 2, 3, 2>(p, stream);
+          case 6: return launch_fwd_t<Ty, 128, 64, 8, 1, CAP, 6, 2, 2, false, false, false, 0, false>(p, stream);
           default: break;
         }
         // Softcap and varlen launches: 128-row tiles of 32-key steps at three
