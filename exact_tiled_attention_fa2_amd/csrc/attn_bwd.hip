@@ -223,6 +223,48 @@ __device__ __forceinline__ void store_rows(uint16_t* dst, const f32x16 (&acc)[D 
   }
 }
 
+// The same [D x 32] accumulator stored through LDS: the wave writes its
+// 32 x D block into `region` (32 * 2D bytes, private to the wave and idle;
+// 16-byte chunks XOR-swizzled by row) and reads it back row-contiguous, so
+// that each 16-byte-per-lane store covers 64 / (D / 8) whole rows instead of
+// scattering 8-byte pieces over 32 rows.  row_ptr(r) gives the destination
+// of row r, or nullptr for a row that is not stored.
+template <class Ty, int D, class RowPtr>
+__device__ __forceinline__ void store_rows_staged(char* region, const f32x16 (&acc)[D / 32], float mul, int lane,
+                                                  RowPtr row_ptr) {
+  constexpr int CH = D / 8;
+  constexpr int ROWB = 2 * D;
+  constexpr int SW = CH < 16 ? CH - 1 : 15;
+  constexpr int RPI = 64 / CH;  // rows per store instruction
+  const int l32 = lane & 31, hl = lane >> 5;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int c = 4 * dt + g4;
+      u32x2 w;
+      w[0] = Ty::pack(acc[dt][4 * g4 + 0] * mul, acc[dt][4 * g4 + 1] * mul);
+      w[1] = Ty::pack(acc[dt][4 * g4 + 2] * mul, acc[dt][4 * g4 + 3] * mul);
+      *reinterpret_cast<u32x2*>(region + l32 * ROWB + ((c ^ (l32 & SW)) << 4) + 8 * hl) = w;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes done
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int it = 0; it < 32 / RPI; ++it) {
+    const int rr = it * RPI + lane / CH;
+    const int cc = lane % CH;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(region + rr * ROWB + ((cc ^ (rr & SW)) << 4));
+    uint16_t* d = row_ptr(rr);
+    if (d != nullptr) *reinterpret_cast<u32x4*>(d + 8 * cc) = v;
+  }
+}
+
+// 16-byte aligned rows (base pointer and every stride a multiple of 8 elements).
+__device__ __forceinline__ bool rows_aligned16(const void* base, int64_t s0, int64_t s1, int64_t s2) {
+  return ((reinterpret_cast<uintptr_t>(base) & 15) | ((s0 | s1 | s2) & 7)) == 0;
+}
+
 // ---------------------------------------------------------------- dK, dV
 // NW waves per workgroup (32 keys each), WPE waves per SIMD.  PASSES = 1:
 // one walk over the queries accumulates dV and dK together (~440 registers:
@@ -538,6 +580,26 @@ bwd_dkdv_kernel(const BwdKernelParams p) {
     if (r + 1 < n) step(std::integral_constant<int, 1>{}, r + 1);
   }
 
+  // One pass: the gradients leave through the idle Q stage buffers (the last
+  // step's barrier has retired every wave's reads of them); wave w takes
+  // stage buffer w, dK in its first half and dV in its second.
+  if constexpr (PASSES == 1 && NW <= 4) {
+    if (n > 0 && rows_aligned16(p.dk, p.dk_batch, p.dk_row, p.dk_head) &&
+        rows_aligned16(p.dv, p.dv_batch, p.dv_row, p.dv_head)) {
+      char* region = wave == 0 ? lds_q0 : wave == 1 ? lds_q1 : wave == 2 ? lds_q2 : lds_g0;
+      uint16_t* dk0 = reinterpret_cast<uint16_t*>(p.dk) + b * p.dk_batch + (int64_t)(sr.k_start + wk_lo) * p.dk_row +
+                      kvh * p.dk_head;
+      uint16_t* dv0 = reinterpret_cast<uint16_t*>(p.dv) + b * p.dv_batch + (int64_t)(sr.k_start + wk_lo) * p.dv_row +
+                      kvh * p.dv_head;
+      store_rows_staged<Ty, D>(region, acc_dk, p.scale, lane, [&](int rr) -> uint16_t* {
+        return wk_lo + rr < sk ? dk0 + (int64_t)rr * p.dk_row : nullptr;
+      });
+      store_rows_staged<Ty, D>(region + TILEB / 2, acc_dv, 1.0f, lane, [&](int rr) -> uint16_t* {
+        return wk_lo + rr < sk ? dv0 + (int64_t)rr * p.dv_row : nullptr;
+      });
+      return;
+    }
+  }
   if (key_valid) {
     if constexpr (DO_DK) {
       uint16_t* dkp = reinterpret_cast<uint16_t*>(p.dk) + b * p.dk_batch +
@@ -751,6 +813,20 @@ bwd_dq_kernel(const BwdKernelParams p) {
     if (r < n) step(std::integral_constant<int, 0>{}, r);
   }
 
+  // dQ leaves through the idle K/V stage buffers (the last step's barrier has
+  // retired every wave's reads of them): two 32-row blocks per buffer.
+  if (n > 0 && rows_aligned16(p.dq, p.dq_batch, p.dq_row, p.dq_head)) {
+    constexpr int REGB = 32 * ROWB;
+    static_assert(TILEB == 2 * REGB && NW <= 8, "two wave blocks per stage buffer");
+    const int bi = wave >> 1;
+    char* region = (bi == 0 ? lds_k0 : bi == 1 ? lds_k1 : bi == 2 ? lds_v0 : lds_v1) + (wave & 1) * REGB;
+    uint16_t* dq0 = reinterpret_cast<uint16_t*>(p.dq) + b * p.dq_batch + (int64_t)(sr.q_start + wrow_lo) * p.dq_row +
+                    head * p.dq_head;
+    store_rows_staged<Ty, D>(region, acc, p.scale, lane, [&](int rr) -> uint16_t* {
+      return wrow_lo + rr < sq ? dq0 + (int64_t)rr * p.dq_row : nullptr;
+    });
+    return;
+  }
   if (q_valid) {
     uint16_t* dqp = reinterpret_cast<uint16_t*>(p.dq) + b * p.dq_batch + (int64_t)(sr.q_start + row) * p.dq_row +
                     head * p.dq_head;
