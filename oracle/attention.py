@@ -47,6 +47,7 @@ __all__ = [
     "attention_ref",
     "attention_varlen_ref",
     "attention_kvcache_ref",
+    "sequence_slopes",
 ]
 
 
@@ -173,13 +174,25 @@ def attention_ref(q, k, v, scale=None, causal=False, window=(-1, -1), softcap=0.
     return out, lse
 
 
+def sequence_slopes(alibi_slopes, b):
+    """ALiBi slopes for the one-sequence call of batch entry (or packed sequence) b.
+
+    ``alibi_slopes`` is None, [Hq] (one slope per query head, shared by every
+    sequence) or [B, Hq] (row b belongs to sequence b).  Returns None, the
+    [Hq] array unchanged, or row b as a [1, Hq] array for a batch-1 call.
+    """
+    if alibi_slopes is None:
+        return None
+    a = np.asarray(alibi_slopes, dtype=np.float64)
+    return a if a.ndim == 1 else a[b:b + 1]
+
+
 def _batch_entry(kw, b):
     """Keyword arguments for the one-sequence call of batch entry b (per-batch ALiBi slopes)."""
-    a = kw.get("alibi_slopes")
-    if a is None or np.asarray(a).ndim == 1:
+    if kw.get("alibi_slopes") is None:
         return kw
     kw = dict(kw)
-    kw["alibi_slopes"] = np.asarray(a)[b:b + 1]
+    kw["alibi_slopes"] = sequence_slopes(kw["alibi_slopes"], b)
     return kw
 
 

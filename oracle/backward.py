@@ -31,6 +31,7 @@ Masks, alignment, window and softcap follow the forward's readings.
 
 import numpy as np
 
+from . import attention as _attention
 from .attention import allowed_mask, alibi_bias, kv_head_of, _slope
 
 __all__ = [
@@ -137,10 +138,7 @@ def attention_bwd_varlen_ref(q, k, v, do, cu_seqlens_q, cu_seqlens_k, **kw):
     slopes = kw.pop("alibi_slopes", None)
     for b in range(cu_q.shape[0] - 1):
         q0, q1, k0, k1 = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
-        sl = None
-        if slopes is not None:
-            a = np.asarray(slopes, dtype=np.float64)
-            sl = a if a.ndim == 1 else a[b]
+        sl = _attention.sequence_slopes(slopes, b)
         dq_b, dk_b, dv_b = attention_bwd_ref(q[None, q0:q1], k[None, k0:k1], v[None, k0:k1],
                                              do[None, q0:q1], alibi_slopes=sl, **kw)
         dq[q0:q1] = dq_b[0]

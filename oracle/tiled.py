@@ -25,6 +25,13 @@ scores of the tile:
 Finally O /= l and LSE = m~ + ln(l); a row with l = 0 gives O = 0 and
 LSE = -inf.  ``lagging=False`` is the superseded v1.2 rule (on a skip keep
 the new max); it is kept only to show that it is wrong at tau = 8.
+
+Per-row statistics (``return_row_stats``).  A tile is *live* for a row when
+the row sees at least one key of it.  On a row's first live tile the running
+max leaves -inf ("first"); on every later live tile step 3 either skips
+(the max lags) or rescales.  So first + skips + rescales = the number of
+live tiles of the row, and max_p is the largest P the row ever forms.
+Tiles with no visible key change nothing and are not counted.
 """
 
 import numpy as np
@@ -52,7 +59,7 @@ def round_to_16bit(x, kind):
 
 
 def _tiled_one_head(q_h, k_g, v_g, scale, causal, window, softcap, tau, block_k, lagging,
-                    order, p_round, stats):
+                    order, p_round, stats, row_stats=None):
     seqlen_q, seqlen_k = q_h.shape[0], k_g.shape[0]
     rows = np.arange(seqlen_q)
     m = np.full(seqlen_q, -np.inf)
@@ -66,7 +73,10 @@ def _tiled_one_head(q_h, k_g, v_g, scale, causal, window, softcap, tau, block_k,
         t = transformed_scores(q_h, k_g[j0:j1], scale, softcap)
         ok = allowed_mask(seqlen_q, seqlen_k, rows, causal, window[0], window[1])[:, j0:j1]
         t = np.where(ok, t, -np.inf)
+        live = ok.any(axis=1)
+        first = live & np.isneginf(m)
         m_cur = np.maximum(m, t.max(axis=1))
+        skip = np.zeros(seqlen_q, dtype=bool)
         if step == 0:
             m = m_cur
         else:
@@ -86,6 +96,12 @@ def _tiled_one_head(q_h, k_g, v_g, scale, causal, window, softcap, tau, block_k,
         m_guard = np.where(np.isneginf(m), 0.0, m)
         p = np.exp2(t * LOG2E - (m_guard * LOG2E)[:, None])
         stats["max_p"] = max(stats["max_p"], float(p.max(initial=0.0)))
+        if row_stats is not None:
+            later = live & ~first
+            row_stats["first"] += first
+            row_stats["skips"] += later & skip
+            row_stats["rescales"] += later & ~skip
+            row_stats["max_p"] = np.maximum(row_stats["max_p"], p.max(axis=1, initial=0.0))
         l = l + p.sum(axis=1)
         acc = acc + round_to_16bit(p, p_round) @ v_g[j0:j1]
     live = l > 0
@@ -96,11 +112,15 @@ def _tiled_one_head(q_h, k_g, v_g, scale, causal, window, softcap, tau, block_k,
 
 
 def tiled_ref(q, k, v, scale=None, causal=False, window=(-1, -1), softcap=0.0, tau=8.0,
-              block_k=64, lagging=True, order="ascending", p_round=None, return_stats=False):
+              block_k=64, lagging=True, order="ascending", p_round=None, return_stats=False,
+              return_row_stats=False):
     """The tiled algorithm above, fp64, for q [B, Sq, Hq, D], k/v [B, Sk, Hkv, D].
 
     Returns (O [B, Sq, Hq, D], LSE [B, Hq, Sq]) and, with ``return_stats``, a
     dict with the number of skipped and applied rescales and the largest P.
+    With ``return_row_stats`` one more dict follows: int arrays "first",
+    "skips", "rescales" and float array "max_p", each [B, Hq, Sq] (see the
+    module docstring for what is counted).
     ``p_round`` in {None, "fp16", "bf16"} rounds P before the P V product
     (the row sum keeps the unrounded P), to model a 16-bit P operand.
     """
@@ -114,14 +134,30 @@ def tiled_ref(q, k, v, scale=None, causal=False, window=(-1, -1), softcap=0.0, t
     out = np.zeros((batch, seqlen_q, heads_q, v.shape[3]))
     lse = np.full((batch, heads_q, seqlen_q), -np.inf)
     stats = {"skips": 0, "rescales": 0, "max_p": 0.0}
+    rows = {"first": np.zeros((batch, heads_q, seqlen_q), dtype=np.int64),
+            "skips": np.zeros((batch, heads_q, seqlen_q), dtype=np.int64),
+            "rescales": np.zeros((batch, heads_q, seqlen_q), dtype=np.int64),
+            "max_p": np.zeros((batch, heads_q, seqlen_q))}
     for b in range(batch):
         for h in range(heads_q):
             g = kv_head_of(h, heads_q, heads_kv)
+            rs = None
+            if return_row_stats:
+                rs = {"first": np.zeros(seqlen_q, dtype=np.int64),
+                      "skips": np.zeros(seqlen_q, dtype=np.int64),
+                      "rescales": np.zeros(seqlen_q, dtype=np.int64),
+                      "max_p": np.zeros(seqlen_q)}
             o_bh, lse_bh = _tiled_one_head(q[b, :, h], k[b, :, g], v[b, :, g], scale, causal,
                                            window, softcap, tau, block_k, lagging, order,
-                                           p_round, stats)
+                                           p_round, stats, rs)
             out[b, :, h] = o_bh
             lse[b, h] = lse_bh
+            if rs is not None:
+                for key in rows:
+                    rows[key][b, h] = rs[key]
+    res = (out, lse)
     if return_stats:
-        return out, lse, stats
-    return out, lse
+        res = res + (stats,)
+    if return_row_stats:
+        res = res + (rows,)
+    return res

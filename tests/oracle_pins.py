@@ -20,6 +20,7 @@ import torch
 
 import oracle
 from oracle import attention as oatt
+from oracle import metrics as ometrics
 from oracle import tiled as otiled
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -691,6 +692,174 @@ def pin_metrics():
     assert oracle.lse_max_abs_err(np.array([0.0, 1.0]), np.array([-np.inf, 1.0])) == float("inf")
 
 
+def pin_gates_are_the_pages():
+    """[v1.7] section 4: fp16 rel_Linf <= 2e-2, bf16 rel_Linf <= 1e-2, cosine >= 0.9995 (read
+    from the golden file of the page's numbers); the LSE gate, 1e-3 absolute, is the stated
+    target beside them (the page prints no LSE gate)."""
+    g = _golden("page_v17_probes.json")["gates"]
+    gates = ometrics.GATES
+    assert set(gates) == {"fp16", "bf16"}
+    assert gates["fp16"]["rel_linf"] == g["fp16_rel_linf"]
+    assert gates["bf16"]["rel_linf"] == g["bf16_rel_linf"]
+    for dt in ("fp16", "bf16"):
+        assert gates[dt]["cosine"] == g["cosine"]
+        assert gates[dt]["lse_abs"] == 1e-3
+
+
+def pin_cosine_hand_values():
+    """Cosine of hand-picked pairs: [1,0].[1,1] = 1/sqrt(2), [3,4].[4,3] = 24/25, opposite
+    vectors -1, orthogonal 0; independent of either vector's length."""
+    sq2 = 1.0 / math.sqrt(2.0)
+    assert abs(ometrics.cosine(np.array([1.0, 0.0]), np.array([1.0, 1.0])) - sq2) < 1e-15
+    assert abs(ometrics.cosine(np.array([3.0, 4.0]), np.array([4.0, 3.0])) - 0.96) < 1e-15
+    assert abs(ometrics.cosine(np.array([1.0, 2.0, 3.0]), np.array([-1.0, -2.0, -3.0])) + 1.0) < 1e-15
+    assert ometrics.cosine(np.array([0.0, 2.0]), np.array([5.0, 0.0])) == 0.0
+    a = np.array([[0.3, -1.2], [2.0, 0.7]])
+    b = np.array([[1.1, 0.4], [-0.2, 0.9]])
+    c0 = ometrics.cosine(a, b)
+    assert abs(ometrics.cosine(7.5 * a, b) - c0) < 1e-15 and abs(ometrics.cosine(a, 0.01 * b) - c0) < 1e-15
+    dot = 0.3 * 1.1 - 1.2 * 0.4 - 2.0 * 0.2 + 0.7 * 0.9
+    na = math.sqrt(0.09 + 1.44 + 4.0 + 0.49)
+    nb = math.sqrt(1.21 + 0.16 + 0.04 + 0.81)
+    assert abs(c0 - dot / (na * nb)) < 1e-15
+
+
+def pin_compare_each_gate():
+    """compare() passes a case that meets every gate, and fails each hand-built case that
+    breaks exactly one of them: non-finite output, rel_Linf (per dtype), cosine, LSE error,
+    and the -inf pattern of LSE."""
+    ref = np.full(4000, 0.5)
+    lref = np.array([0.25, -np.inf, 3.0])
+    ok = ometrics.compare(ref.copy(), ref, lref.copy(), lref, dtype="bf16")
+    assert ok["pass"] and ok["finite"] and ok["rel_linf"] == 0.0 and ok["lse_abs"] == 0.0
+    # a rel_Linf exactly at the gate passes (the gates are inclusive)
+    edge = np.array([1.0, 0.0]), np.array([1.0, 0.01])
+    assert ometrics.compare(edge[1], edge[0], dtype="bf16")["pass"]
+    # non-finite output only
+    bad = ref.copy(); bad[17] = np.nan
+    assert not ometrics.compare(bad, ref, dtype="fp16")["pass"]
+    bad = ref.copy(); bad[3] = np.inf
+    r = ometrics.compare(bad, ref, dtype="fp16")
+    assert not r["finite"] and not r["pass"]
+    # rel_Linf 1.5e-2 with cosine ~ 1: fails the bf16 gate, passes the fp16 gate
+    out = ref.copy(); out[0] += 0.0075
+    rb, rf = ometrics.compare(out, ref, dtype="bf16"), ometrics.compare(out, ref, dtype="fp16")
+    assert abs(rb["rel_linf"] - 0.015) < 1e-12 and rb["cosine"] > 0.99999
+    assert not rb["pass"] and rf["pass"]
+    # cosine 1/sqrt(1 + 1000 * 0.009^2) = 0.962 with rel_Linf 9e-3: fails on cosine alone
+    ref2 = np.zeros(1001); ref2[0] = 1.0
+    out2 = np.full(1001, 0.009); out2[0] = 1.0
+    r = ometrics.compare(out2, ref2, dtype="bf16")
+    assert r["rel_linf"] <= 1e-2 and abs(r["cosine"] - 1.0 / math.sqrt(1.081)) < 1e-12
+    assert not r["pass"]
+    # LSE off by 2e-3 on one finite row
+    l2 = lref.copy(); l2[2] += 2e-3
+    r = ometrics.compare(ref.copy(), ref, l2, lref, dtype="fp16")
+    assert abs(r["lse_abs"] - 2e-3) < 1e-12 and not r["pass"]
+    # -inf pattern: a finite LSE where the reference is -inf, and the reverse
+    l3 = lref.copy(); l3[1] = -50.0
+    assert not ometrics.compare(ref.copy(), ref, l3, lref, dtype="fp16")["pass"]
+    l4 = lref.copy(); l4[0] = -np.inf
+    assert not ometrics.compare(ref.copy(), ref, l4, lref, dtype="fp16")["pass"]
+    # without an LSE only the output gates apply
+    assert ometrics.compare(ref.copy(), ref, dtype="fp16")["pass"]
+
+
+def pin_alibi_per_sequence_slopes():
+    """[B, Hq] ALiBi slopes: packed sequence (or cache entry) b uses row b of the table, in the
+    forward (varlen, kv-cache) and in the varlen backward -- each checked against batch-1
+    calls of the dense functions written out with that row as [Hq] slopes."""
+    rng = _rng(41)
+    hq, hkv, d = 4, 2, 8
+    table = np.array([[0.5, 0.25, 0.125, 0.0625], [2.0, 0.0, 1.0, 3.0], [0.3, 0.9, 0.05, 1.7]])
+    lens = [6, 9, 4]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    q = rng.standard_normal((cu[-1], hq, d))
+    k = rng.standard_normal((cu[-1], hkv, d))
+    v = rng.standard_normal((cu[-1], hkv, d))
+    do = rng.standard_normal((cu[-1], hq, d))
+    o, l = oracle.attention_varlen_ref(q, k, v, cu, cu, causal=True, alibi_slopes=table)
+    dq, dk, dv = oracle.attention_bwd_varlen_ref(q, k, v, do, cu, cu, causal=True, alibi_slopes=table)
+    for s_ in range(len(lens)):
+        a, z = cu[s_], cu[s_ + 1]
+        ro, rl = oracle.attention_ref(q[None, a:z], k[None, a:z], v[None, a:z], causal=True,
+                                      alibi_slopes=list(table[s_]))
+        assert np.array_equal(o[a:z], ro[0]) and np.array_equal(l[:, a:z], rl[0])
+        gq, gk, gv = oracle.attention_bwd_ref(q[None, a:z], k[None, a:z], v[None, a:z],
+                                              do[None, a:z], causal=True, alibi_slopes=list(table[s_]))
+        assert np.array_equal(dq[a:z], gq[0]) and np.array_equal(dk[a:z], gk[0])
+        assert np.array_equal(dv[a:z], gv[0])
+    # the rows differ enough that a wrong row is visible
+    o_wrong, _ = oracle.attention_ref(q[None, cu[1]:cu[2]], k[None, cu[1]:cu[2]], v[None, cu[1]:cu[2]],
+                                      causal=True, alibi_slopes=list(table[0]))
+    assert np.max(np.abs(o_wrong[0] - o[cu[1]:cu[2]])) > 1e-3
+    # kv-cache: cache entry b, valid length n_b, row b of the table
+    sk, nq = 11, 3
+    kc = rng.standard_normal((3, sk, hkv, d))
+    vc = rng.standard_normal((3, sk, hkv, d))
+    qc = rng.standard_normal((3, nq, hq, d))
+    n_valid = [11, 5, 8]
+    oc, lc = oracle.attention_kvcache_ref(qc, kc, vc, cache_seqlens=n_valid, causal=True,
+                                          alibi_slopes=table)
+    for b in range(3):
+        n = n_valid[b]
+        ro, rl = oracle.attention_ref(qc[b:b + 1], kc[b:b + 1, :n], vc[b:b + 1, :n], causal=True,
+                                      alibi_slopes=list(table[b]))
+        assert np.array_equal(oc[b], ro[0]) and np.array_equal(lc[b], rl[0])
+
+
+def _stats_case(rises_log2, block_k=2):
+    """One query row and one key per tile position: tile i holds a key of score u_i (natural
+    units, scale 1) and a key 40 nats lower, with u_i the running sum of rises_log2 times ln 2."""
+    ln2 = math.log(2.0)
+    u = np.cumsum([0.0] + list(rises_log2)) * ln2
+    n = len(u)
+    q = np.zeros((1, 1, 1, 2)); q[0, 0, 0, 0] = 1.0
+    k = np.zeros((1, n * block_k, 1, 2))
+    for i, ui in enumerate(u):
+        k[0, i * block_k, 0, 0] = ui
+        for j in range(1, block_k):
+            k[0, i * block_k + j, 0, 0] = ui - 40.0
+    v = np.ones((1, n * block_k, 1, 2))
+    return q, k, v
+
+
+def pin_tiled_row_stats():
+    """Per-row counts of the threshold rule on tiles whose maxima rise by known amounts (log2
+    units): rises 3, 6, 0.5, 11, -1 from a first tile at 0 give, at tau = 8, first, skip (3 <= 8,
+    max stays at 0), rescale (cumulative 9 > 8, max 9), skip (0.5), rescale (11), skip (-1);
+    the largest P is 2^3 = 8, formed on the second tile while the max lags at 0.  A rise of
+    exactly 8 is skipped and gives P = 256 ([v1.7] section 1.2).  At tau = 0 every rise
+    rescales.  first + skips + rescales = live tiles, counted from the mask in closed form."""
+    q, k, v = _stats_case([3, 6, 0.5, 11, -1])
+    *_, rs = oracle.tiled_ref(q, k, v, scale=1.0, tau=8.0, block_k=2, return_row_stats=True)
+    assert (rs["first"][0, 0, 0], rs["skips"][0, 0, 0], rs["rescales"][0, 0, 0]) == (1, 3, 2)
+    assert abs(rs["max_p"][0, 0, 0] - 8.0) < 1e-12
+    *_, rs = oracle.tiled_ref(q, k, v, scale=1.0, tau=0.0, block_k=2, return_row_stats=True)
+    assert (rs["first"][0, 0, 0], rs["skips"][0, 0, 0], rs["rescales"][0, 0, 0]) == (1, 1, 4)
+    assert abs(rs["max_p"][0, 0, 0] - 1.0) < 1e-12
+    q, k, v = _stats_case([8.0])
+    *_, rs = oracle.tiled_ref(q, k, v, scale=1.0, tau=8.0, block_k=2, return_row_stats=True)
+    assert (rs["first"][0, 0, 0], rs["skips"][0, 0, 0], rs["rescales"][0, 0, 0]) == (1, 1, 0)
+    assert abs(rs["max_p"][0, 0, 0] - 256.0) < 1e-9
+    # live-tile identity on a causal window problem with Sq != Sk and empty rows
+    rng = _rng(42)
+    sq, sk, bk, wl = 37, 53, 8, 5
+    qq = rng.standard_normal((1, sq, 2, 8))
+    kk = rng.standard_normal((1, sk, 1, 8)) * (1.0 + np.arange(sk) / 10.0)[None, :, None, None]
+    vv = rng.standard_normal((1, sk, 1, 8))
+    for kw in (dict(causal=True, window=(wl, -1)), dict(causal=False, window=(3, 0)),
+               dict(causal=True, window=(-1, -1))):
+        *_, rs = oracle.tiled_ref(qq, kk, vv, tau=8.0, block_k=bk, return_row_stats=True, **kw)
+        for i in range(sq):
+            n, lo, hi = _visible_count(i, sq, sk, kw["causal"], *kw["window"])
+            tiles = 0 if n == 0 else hi // bk - lo // bk + 1
+            tot = rs["first"][0, :, i] + rs["skips"][0, :, i] + rs["rescales"][0, :, i]
+            assert np.all(tot == tiles), (kw, i)
+            assert np.all(rs["first"][0, :, i] == (1 if n else 0))
+            assert np.all(rs["max_p"][0, :, i] <= 256.0 + 1e-9)
+
+
 ALL_PINS = [
     pin_uniform_scores,
     pin_one_hot_scores,
@@ -720,4 +889,9 @@ ALL_PINS = [
     pin_p_bound,
     pin_bf16_rounding_helper,
     pin_metrics,
+    pin_gates_are_the_pages,
+    pin_cosine_hand_values,
+    pin_compare_each_gate,
+    pin_alibi_per_sequence_slopes,
+    pin_tiled_row_stats,
 ]

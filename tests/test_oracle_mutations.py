@@ -6,7 +6,9 @@ transposed operand, softcap on the unscaled score, log2 instead of natural
 log, a missing max shift, a window bound read as unbounded, the superseded
 keep-new-max skip rule, or a backward without the softmax row term, the
 softcap derivative, the scale or the GQA sum must each make at least one pin
-fail.
+fail.  So must a slip in the gate code every GPU verdict passes through (an
+"or" for an "and", a dropped cosine or LSE gate, a loosened bf16
+gate, a wrong cosine normaliser) and a wrong per-sequence ALiBi slope row.
 """
 
 import contextlib
@@ -99,12 +101,12 @@ def _tiled_no_lagging(*a, **kw):
 
 
 def _tiled_natural_exp(q_h, k_g, v_g, scale, causal, window, softcap, tau, block_k, lagging,
-                       order, p_round, stats):
+                       order, p_round, stats, row_stats=None):
     saved = otiled.LOG2E
     otiled.LOG2E = 1.0                    # exp2 of the raw score: wrong base
     try:
         return _orig_tiled_one(q_h, k_g, v_g, scale, causal, window, softcap, tau, block_k,
-                               lagging, order, p_round, stats)
+                               lagging, order, p_round, stats, row_stats)
     finally:
         otiled.LOG2E = saved
 
@@ -163,7 +165,57 @@ def _bwd_gqa_overwrite(dk, dv, dk_h, dv_h):
     dv[...] = dv_h
 
 
+from oracle import metrics as omet
+
+_orig_compare = omet.compare
+_orig_cosine = omet.cosine
+
+
+def _compare_variant(use_or=False, cosine_gate=True, finite_gate=True, lse_gate=True):
+    def compare(out, ref, lse=None, lse_ref=None, dtype="bf16"):
+        out = np.asarray(out, dtype=np.float64)
+        res = {"finite": bool(np.all(np.isfinite(out))), "rel_linf": omet.rel_linf(out, ref),
+               "cosine": omet.cosine(out, ref)}
+        gate = omet.GATES[dtype]
+        r_ok = res["rel_linf"] <= gate["rel_linf"]
+        c_ok = res["cosine"] >= gate["cosine"] if cosine_gate else True
+        f_ok = res["finite"] if finite_gate else True
+        ok = (r_ok or c_ok) if use_or else (r_ok and c_ok)
+        ok = ok and f_ok
+        if lse is not None:
+            res["lse_abs"] = omet.lse_max_abs_err(lse, lse_ref)
+            if lse_gate:
+                ok = ok and res["lse_abs"] <= gate["lse_abs"]
+        res["pass"] = bool(ok)
+        return res
+    return compare
+
+
+def _cosine_sq_norm(out, ref):
+    a = np.asarray(out, dtype=np.float64).ravel()
+    b = np.asarray(ref, dtype=np.float64).ravel()
+    na = np.linalg.norm(a)
+    return float(np.dot(a, b) / (na * na)) if na else 0.0     # |a|^2 instead of |a||b|
+
+
+_LOOSE_GATES = {"fp16": {"rel_linf": 2e-2, "cosine": 0.9995, "lse_abs": 1e-3},
+                "bf16": {"rel_linf": 2e-2, "cosine": 0.9995, "lse_abs": 1e-3}}
+
+
+def _slopes_first_sequence(alibi_slopes, b):
+    if alibi_slopes is None:
+        return None
+    a = np.asarray(alibi_slopes, dtype=np.float64)
+    return a if a.ndim == 1 else a[0:1]                          # row 0 for every sequence
+
+
 MUTATIONS = {
+    "compare_or_for_and": (omet, "compare", _compare_variant(use_or=True)),
+    "compare_no_cosine_gate": (omet, "compare", _compare_variant(cosine_gate=False)),
+    "compare_lse_ignored": (omet, "compare", _compare_variant(lse_gate=False)),
+    "gates_bf16_loosened": (omet, "GATES", _LOOSE_GATES),
+    "cosine_sq_norm": (omet, "cosine", _cosine_sq_norm),
+    "alibi_first_sequence_slopes": (oatt, "sequence_slopes", _slopes_first_sequence),
     "causal_strict_lt": (oatt, "allowed_mask", _mask_causal_strict),
     "top_left_alignment": (oatt, "allowed_mask", _mask_top_left),
     "window_zero_as_unbounded": (oatt, "allowed_mask", _mask_window_zero_unbounded),
