@@ -7,7 +7,6 @@ built, loading fails with an error that says how to build it.
 """
 
 import ctypes
-import math
 import os
 
 import torch
@@ -103,41 +102,50 @@ class BwdVarlenArgs(ctypes.Structure):
 
 
 _LIB = None
+_OVERRIDE = []  # libraries pushed by exact_tiled_attention_fa2_amd.debug (tests and sweeps only)
+
+
+def configure(h):
+    """Declare the argument and return types of every entry point of attn_mi355x.h on handle h."""
+    h.attn_fwd.argtypes = [ctypes.POINTER(FwdArgs), _vp]
+    h.attn_fwd.restype = ctypes.c_int
+    h.attn_fwd_varlen.argtypes = [ctypes.POINTER(VarlenArgs), _vp, ctypes.c_size_t, _vp]
+    h.attn_fwd_varlen.restype = ctypes.c_int
+    h.attn_fwd_kvcache.argtypes = [ctypes.POINTER(KvcacheArgs), _vp, ctypes.c_size_t, _vp]
+    h.attn_fwd_kvcache.restype = ctypes.c_int
+    h.attn_varlen_workspace_bytes.argtypes = [_i32] * 5
+    h.attn_varlen_workspace_bytes.restype = ctypes.c_size_t
+    h.attn_kvcache_workspace_bytes.argtypes = [_i32] * 5
+    h.attn_kvcache_workspace_bytes.restype = ctypes.c_size_t
+    h.attn_kvcache_num_splits.argtypes = [_i32] * 6
+    h.attn_kvcache_num_splits.restype = _i32
+    h.attn_bwd.argtypes = [ctypes.POINTER(BwdArgs), _vp, ctypes.c_size_t, _vp]
+    h.attn_bwd.restype = ctypes.c_int
+    h.attn_bwd_workspace_bytes.argtypes = [_i32] * 3
+    h.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+    h.attn_bwd_varlen.argtypes = [ctypes.POINTER(BwdVarlenArgs), _vp, ctypes.c_size_t, _vp]
+    h.attn_bwd_varlen.restype = ctypes.c_int
+    h.attn_bwd_varlen_workspace_bytes.argtypes = [_i32] * 2
+    h.attn_bwd_varlen_workspace_bytes.restype = ctypes.c_size_t
+    h.attn_status_string.argtypes = [ctypes.c_int]
+    h.attn_status_string.restype = ctypes.c_char_p
+    h.attn_version.argtypes = []
+    h.attn_version.restype = ctypes.c_int
+    return h
 
 
 def lib():
-    """The loaded shared library (raises if it has not been built)."""
+    """The library the entry points below call: the release build (raises if it is not
+    built), or the debug build while a test holds exact_tiled_attention_fa2_amd.debug's
+    override."""
     global _LIB
+    if _OVERRIDE:
+        return _OVERRIDE[-1]
     if _LIB is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                                "`python -m exact_tiled_attention_fa2_amd.build_lib`")
-        h = ctypes.CDLL(LIB_PATH)
-        h.attn_fwd.argtypes = [ctypes.POINTER(FwdArgs), _vp]
-        h.attn_fwd.restype = ctypes.c_int
-        h.attn_fwd_varlen.argtypes = [ctypes.POINTER(VarlenArgs), _vp, ctypes.c_size_t, _vp]
-        h.attn_fwd_varlen.restype = ctypes.c_int
-        h.attn_fwd_kvcache.argtypes = [ctypes.POINTER(KvcacheArgs), _vp, ctypes.c_size_t, _vp]
-        h.attn_fwd_kvcache.restype = ctypes.c_int
-        h.attn_varlen_workspace_bytes.argtypes = [_i32] * 5
-        h.attn_varlen_workspace_bytes.restype = ctypes.c_size_t
-        h.attn_kvcache_workspace_bytes.argtypes = [_i32] * 5
-        h.attn_kvcache_workspace_bytes.restype = ctypes.c_size_t
-        h.attn_kvcache_num_splits.argtypes = [_i32] * 6
-        h.attn_kvcache_num_splits.restype = _i32
-        h.attn_bwd.argtypes = [ctypes.POINTER(BwdArgs), _vp, ctypes.c_size_t, _vp]
-        h.attn_bwd.restype = ctypes.c_int
-        h.attn_bwd_workspace_bytes.argtypes = [_i32] * 3
-        h.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
-        h.attn_bwd_varlen.argtypes = [ctypes.POINTER(BwdVarlenArgs), _vp, ctypes.c_size_t, _vp]
-        h.attn_bwd_varlen.restype = ctypes.c_int
-        h.attn_bwd_varlen_workspace_bytes.argtypes = [_i32] * 2
-        h.attn_bwd_varlen_workspace_bytes.restype = ctypes.c_size_t
-        h.attn_status_string.argtypes = [ctypes.c_int]
-        h.attn_status_string.restype = ctypes.c_char_p
-        h.attn_version.argtypes = []
-        h.attn_version.restype = ctypes.c_int
-        _LIB = h
+        _LIB = configure(ctypes.CDLL(LIB_PATH))
     return _LIB
 
 
@@ -361,7 +369,3 @@ def attn_bwd_varlen(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, max_seqle
     _check(lib().attn_bwd_varlen(ctypes.byref(a), _ptr(workspace), ws_bytes, _stream(stream, q.device)),
            "attn_bwd_varlen")
     return dq, dk, dv
-
-
-def default_scale(head_dim):
-    return 1.0 / math.sqrt(head_dim)

@@ -11,6 +11,32 @@
 
 #include "attn_internal.h"
 #include "attn_mi355x.h"
+#ifdef ATTN_DEBUG_BUILD
+#include "attn_mi355x_debug.h"
+#endif
+
+namespace attn {
+
+// Compute units of the current device (queried once per device).
+int compute_units() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    cus[dev] = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) ? n : 256;
+  }
+  return cus[dev];
+}
+
+#ifdef ATTN_DEBUG_BUILD
+DebugState& debug_state() {
+  static DebugState state = {0, 0, 0, 0};  // process-wide
+  return state;
+}
+#endif
+
+}  // namespace attn
 
 namespace {
 
@@ -89,8 +115,6 @@ void resolve_bwd_opts(const attn_softmax_opts& o, int head_dim, attn::BwdKernelP
 
 int launch_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH; }
 
-int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
-
 }  // namespace
 
 extern "C" {
@@ -113,12 +137,22 @@ const char* attn_status_string(int status) {
 
 int attn_version(void) { return ATTN_VERSION; }
 
-int attn_fwd(const attn_fwd_args* a, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and kernel parameters of attn_fwd.  Returns ATTN_OK with
+// `empty` set when there is nothing to launch.
+int prepare_fwd(const attn_fwd_args* a, FwdKernelParams& p, bool& empty) {
+  empty = false;
   if (a == nullptr) return ATTN_E_NULL;
   int st = check_common(a->dtype, a->head_dim, a->heads_q, a->heads_kv, a->opts);
   if (st != ATTN_OK) return st;
   if (a->batch < 0 || a->seqlen_q < 0 || a->seqlen_k < 0) return ATTN_E_SHAPE;
-  if (a->batch == 0 || a->seqlen_q == 0) return ATTN_OK;  // empty problem: nothing to do
+  if (a->batch == 0 || a->seqlen_q == 0) {  // empty problem: nothing to do
+    empty = true;
+    return ATTN_OK;
+  }
   if (a->q == nullptr || a->o == nullptr) return ATTN_E_NULL;
   if (a->seqlen_k > 0 && (a->k == nullptr || a->v == nullptr)) return ATTN_E_NULL;
   if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o) ||
@@ -129,7 +163,6 @@ int attn_fwd(const attn_fwd_args* a, void* stream) {
     return ATTN_E_ALIGN;
   if (a->lse != nullptr && (reinterpret_cast<uintptr_t>(a->lse) & 3u) != 0) return ATTN_E_ALIGN;
 
-  FwdKernelParams p;
   std::memset(&p, 0, sizeof(p));
   p.q = a->q; p.k = a->k; p.v = a->v; p.o = a->o; p.lse = a->lse;
   p.q_batch = a->q_batch_stride; p.q_row = a->q_row_stride; p.q_head = a->q_head_stride;
@@ -143,6 +176,18 @@ int attn_fwd(const attn_fwd_args* a, void* stream) {
   p.pack_gqa = p.group > 1 ? 1 : 0;
   p.num_splits = 1;
   resolve_opts(a->opts, a->head_dim, p);
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const attn_fwd_args* a, void* stream) {
+  FwdKernelParams p;
+  bool empty = false;
+  const int st = prepare_fwd(a, p, empty);
+  if (st != ATTN_OK || empty) return st;
   return launch_status(attn::launch_fwd(p, a->dtype, a->head_dim, (hipStream_t)stream));
 }
 
@@ -387,5 +432,27 @@ int attn_bwd_varlen(const attn_bwd_varlen_args* a, void* workspace, size_t works
   resolve_bwd_opts(a->opts, a->head_dim, p);
   return launch_status(attn::launch_bwd(p, a->dtype, a->head_dim, (hipStream_t)stream));
 }
+
+#ifdef ATTN_DEBUG_BUILD
+void attn_debug_set_variants(int32_t fwd, int32_t dec, int32_t bwd) {
+  attn::DebugState& d = attn::debug_state();
+  d.fwd_variant = fwd;
+  d.dec_variant = dec;
+  d.bwd_variant = bwd;
+}
+
+int32_t attn_debug_last_block_k(void) { return attn::debug_state().last_block_k; }
+
+int attn_fwd_stats(const attn_fwd_args* a, uint32_t* row_stats, void* stream) {
+  FwdKernelParams p;
+  bool empty = false;
+  const int st = prepare_fwd(a, p, empty);
+  if (st != ATTN_OK || empty) return st;
+  if (row_stats == nullptr) return ATTN_E_NULL;
+  if (!aligned16(row_stats)) return ATTN_E_ALIGN;
+  p.row_stats = row_stats;
+  return launch_status(attn::launch_fwd(p, a->dtype, a->head_dim, (hipStream_t)stream));
+}
+#endif
 
 }  // extern "C"

@@ -32,7 +32,6 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
-#include <stdlib.h>
 
 #include <type_traits>
 
@@ -283,7 +282,6 @@ bwd_dkdv_kernel(const BwdKernelParams p) {
   constexpr int TILEB = BQ * ROWB;
   constexpr int DS = D / 16;
   constexpr int DT = D / 32;
-  constexpr int LEAD = 4;           // LDS operand reads issued ahead of the MFMAs
   using Copier = TileCopier<BQ, D, NT>;
 
   // Three stages of Q and dO tiles (copies run two steps ahead of compute);
@@ -834,14 +832,9 @@ bwd_dq_kernel(const BwdKernelParams p) {
   }
 }
 
-// Backward variant for sweeps (environment ATTN_MI355X_BWD_VARIANT): 0 = the
-// default; 1 = dK/dV in two passes at 8 waves; 2 / 3 = dQ with 8 / 4 waves
-// (256 / 128 queries per workgroup).
-// Read at every launch.
-int bwd_variant() {
-  const char* e = getenv("ATTN_MI355X_BWD_VARIANT");
-  return e ? atoi(e) : 0;
-}
+// Kernel-shape overrides of the debug build (attn_debug_set_variants; the
+// release library compiles none of them): 1 = dK/dV in two passes at 8
+// waves; 2 / 3 = dQ with 8 / 4 waves (256 / 128 queries per workgroup).
 
 // D first (both gradient kernels read it), then dK/dV, then dQ; a kernel
 // whose grid would be empty (no queries, or no keys) is not launched.
@@ -854,10 +847,15 @@ hipError_t launch_bwd_t(const BwdKernelParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((bwd_dot_kernel<Ty, D>), grid, dim3(256), 0, stream, p);
   }
   if (p.seqlen_k > 0) {
-    if (bwd_variant() == 1) {
-      const dim3 grid((unsigned)((p.seqlen_k + 255) / 256), p.heads_kv, p.batch);
-      hipLaunchKernelGGL((bwd_dkdv_kernel<Ty, D, SOFTCAP, ALIBI, 8, 2, 2>), grid, dim3(512), 0, stream, p);
-    } else {
+    bool two_pass = false;
+    if constexpr (kDebugBuild) {
+      if (bwd_variant() == 1) {
+        const dim3 grid((unsigned)((p.seqlen_k + 255) / 256), p.heads_kv, p.batch);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<Ty, D, SOFTCAP, ALIBI, 8, 2, 2>), grid, dim3(512), 0, stream, p);
+        two_pass = true;
+      }
+    }
+    if (!two_pass) {
       const dim3 grid((unsigned)((p.seqlen_k + 127) / 128), p.heads_kv, p.batch);
       hipLaunchKernelGGL((bwd_dkdv_kernel<Ty, D, SOFTCAP, ALIBI, 4, 1, 1>), grid, dim3(256), 0, stream, p);
     }
@@ -865,9 +863,9 @@ hipError_t launch_bwd_t(const BwdKernelParams& p, hipStream_t stream) {
   if (p.seqlen_q > 0) {
     // 256 queries per workgroup (8 waves, two per SIMD; half the K/V re-reads
     // from L2) when that grid gives every CU two workgroups, else 128
-    // (twice the workgroups); variant 2 forces 256, 3 forces 128.
+    // (twice the workgroups); the debug build's variant 2 forces 256, 3 forces 128.
     const int64_t wgs256 = (int64_t)((p.seqlen_q + 255) / 256) * p.heads_q * p.batch;
-    const int v = bwd_variant();
+    const int v = kDebugBuild ? bwd_variant() : 0;
     if (v == 2 || (v != 3 && wgs256 >= 2 * (int64_t)compute_units())) {
       const dim3 grid((unsigned)((p.seqlen_q + 255) / 256), p.heads_q, p.batch);
       hipLaunchKernelGGL((bwd_dq_kernel<Ty, D, SOFTCAP, ALIBI, 8>), grid, dim3(512), 0, stream, p);
@@ -895,9 +893,15 @@ hipError_t launch_bwd_ty(const BwdKernelParams& p, int head_dim, hipStream_t str
 
 }  // namespace
 
-hipError_t launch_bwd(const BwdKernelParams& p, int dtype, int head_dim, hipStream_t stream) {
-  if (p.batch <= 0 || p.heads_q <= 0) return hipSuccess;
-  return dtype == 1 ? launch_bwd_ty<TypeBF16>(p, head_dim, stream) : launch_bwd_ty<TypeF16>(p, head_dim, stream);
+#if !defined(ATTN_TU_DTYPE) || ATTN_TU_DTYPE == 0
+hipError_t launch_bwd_f16(const BwdKernelParams& p, int head_dim, hipStream_t stream) {
+  return launch_bwd_ty<TypeF16>(p, head_dim, stream);
 }
+#endif
+#if !defined(ATTN_TU_DTYPE) || ATTN_TU_DTYPE == 1
+hipError_t launch_bwd_bf16(const BwdKernelParams& p, int head_dim, hipStream_t stream) {
+  return launch_bwd_ty<TypeBF16>(p, head_dim, stream);
+}
+#endif
 
 }  // namespace attn

@@ -43,6 +43,10 @@ struct FwdKernelParams {
   const float* alibi;   // ALiBi slopes (null: off), slope(b, h) = alibi[b * alibi_bstride + h]
   int64_t alibi_bstride;
   float alibi_inv_scale;  // 1 / scale_ln: bias in raw-score units
+  // Debug build only (null otherwise): per query row, 4 words at the LSE
+  // index: live KV steps that set the first max, steps that skipped the
+  // rescale, steps that rescaled, and the bits of the largest fp32 P formed.
+  uint32_t* row_stats;
 };
 
 struct CombineParams {
@@ -98,9 +102,50 @@ constexpr int kBlockM = 128;  // nominal query rows per workgroup (split-count h
 // query fails).
 int compute_units();
 
-// Host-side launchers (return a hipError_t).
-hipError_t launch_fwd(const FwdKernelParams& p, int dtype, int head_dim, hipStream_t stream);
-hipError_t launch_combine(const CombineParams& p, int dtype, int head_dim, hipStream_t stream);
-hipError_t launch_bwd(const BwdKernelParams& p, int dtype, int head_dim, hipStream_t stream);
+// The debug build (-DATTN_DEBUG_BUILD) adds tile-shape overrides for tests
+// and sweeps, set through an explicit call, and the per-row rescale
+// counters.  The release library has neither: the kernel a call runs
+// depends on its arguments alone.
+#ifdef ATTN_DEBUG_BUILD
+constexpr bool kDebugBuild = true;
+struct DebugState {
+  int fwd_variant;   // forward tile override (0: per-shape default)
+  int dec_variant;   // decode tile override
+  int bwd_variant;   // backward kernel-shape override
+  int last_block_k;  // KV step of the last forward tile launch on this thread
+};
+DebugState& debug_state();
+inline int fwd_variant() { return debug_state().fwd_variant; }
+inline int dec_variant() { return debug_state().dec_variant; }
+inline int bwd_variant() { return debug_state().bwd_variant; }
+inline void note_block_k(int bk) { debug_state().last_block_k = bk; }
+#else
+constexpr bool kDebugBuild = false;
+constexpr int fwd_variant() { return 0; }
+constexpr int dec_variant() { return 0; }
+constexpr int bwd_variant() { return 0; }
+inline void note_block_k(int) {}
+#endif
+
+// Host-side launchers (return a hipError_t).  Each kernel source is compiled
+// once per 16-bit type (ATTN_TU_DTYPE = 0: fp16, 1: bf16); the dispatchers
+// below pick the type.
+hipError_t launch_fwd_f16(const FwdKernelParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_fwd_bf16(const FwdKernelParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_combine_f16(const CombineParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_combine_bf16(const CombineParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_bwd_f16(const BwdKernelParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_bwd_bf16(const BwdKernelParams& p, int head_dim, hipStream_t stream);
+
+inline hipError_t launch_fwd(const FwdKernelParams& p, int dtype, int head_dim, hipStream_t stream) {
+  return dtype == 1 ? launch_fwd_bf16(p, head_dim, stream) : launch_fwd_f16(p, head_dim, stream);
+}
+inline hipError_t launch_combine(const CombineParams& p, int dtype, int head_dim, hipStream_t stream) {
+  return dtype == 1 ? launch_combine_bf16(p, head_dim, stream) : launch_combine_f16(p, head_dim, stream);
+}
+inline hipError_t launch_bwd(const BwdKernelParams& p, int dtype, int head_dim, hipStream_t stream) {
+  if (p.batch <= 0 || p.heads_q <= 0) return hipSuccess;
+  return dtype == 1 ? launch_bwd_bf16(p, head_dim, stream) : launch_bwd_f16(p, head_dim, stream);
+}
 
 }  // namespace attn

@@ -39,7 +39,6 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
-#include <stdlib.h>
 
 #include <algorithm>
 #include <type_traits>
@@ -375,6 +374,14 @@ fwd_tile_kernel(const FwdKernelParams p) {
     for (int dt = 0; dt < DT; ++dt) acc[g][dt] = f32x16{};
   }
 
+#ifdef ATTN_DEBUG_BUILD
+  // Per-row rescale counters (debug build): first max, skips, rescales, largest P.
+  uint32_t st_first[QG], st_skip[QG], st_resc[QG];
+  float st_pmax[QG];
+#pragma unroll
+  for (int g = 0; g < QG; ++g) st_first[g] = st_skip[g] = st_resc[g] = 0u, st_pmax[g] = 0.0f;
+#endif
+
   const float c2 = p.scale_log2;
   const float tau = p.tau;
   // Rescale threshold in units of the raw score: the running max may lag the
@@ -469,6 +476,8 @@ fwd_tile_kernel(const FwdKernelParams p) {
       // rises more than tau above its running max, the running max is kept
       // (no exchange between the two halves is needed for that).  Otherwise
       // the halves agree on the row max and rows that rose too far rescale.
+      [[maybe_unused]] const float m_before = m_run[g];
+      [[maybe_unused]] bool rescaled = false;
       if (__any(mx > m_run[g] + tau_raw)) {
         const float mx_row = fmaxf(mx, __shfl_xor(mx, 32));
         const float m_new = fmaxf(m_run[g], mx_row);
@@ -480,8 +489,19 @@ fwd_tile_kernel(const FwdKernelParams p) {
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) acc[g][dt] *= alpha;
           m_run[g] = m_new;
+          rescaled = true;
         }
       }
+#ifdef ATTN_DEBUG_BUILD
+      if (p.row_stats != nullptr) {  // wave-uniform
+        const float mrow = fmaxf(mx, __shfl_xor(mx, 32));
+        if (mrow > -INFINITY) {  // the row sees a key of this step
+          if (m_before == -INFINITY) ++st_first[g];
+          else if (rescaled) ++st_resc[g];
+          else ++st_skip[g];
+        }
+      }
+#endif
       // ---- P = exp2((s - m) c2) <= exp2(tau), row sum, 16-bit pack
       const float mg = (m_run[g] == -INFINITY) ? 0.0f : m_run[g];
       const float nb = ALIBI ? (kb - mg) * c2 : -mg * c2;
@@ -494,6 +514,9 @@ fwd_tile_kernel(const FwdKernelParams p) {
                                 : fast_exp2(fmaf(sc[g][kt][r2 + 1], c2, nb));
           l_run[g] += p0 + p1;
           pk[g][kt][r2 >> 1] = Ty::pack(p0, p1);
+#ifdef ATTN_DEBUG_BUILD
+          st_pmax[g] = fmaxf(st_pmax[g], fmaxf(p0, p1));
+#endif
         }
       }
     }
@@ -620,6 +643,20 @@ fwd_tile_kernel(const FwdKernelParams p) {
       if (r + 2 < n) step(std::integral_constant<int, 2>{}, r + 2);
     }
   }
+
+#ifdef ATTN_DEBUG_BUILD
+  if (p.row_stats != nullptr && p.o_part == nullptr) {  // one 16-byte record per valid row
+#pragma unroll
+    for (int g = 0; g < QG; ++g) {
+      const float pm = fmaxf(st_pmax[g], __shfl_xor(st_pmax[g], 32));
+      if (q_valid[g] && hl == 0) {
+        const int64_t idx = (int64_t)b * p.lse_batch + (int64_t)hq[g] * p.lse_head + q_start + row[g];
+        const u32x4 rec = {st_first[g], st_skip[g], st_resc[g], __builtin_bit_cast(uint32_t, pm)};
+        *reinterpret_cast<u32x4*>(p.row_stats + 4 * idx) = rec;
+      }
+    }
+  }
+#endif
 
   // ---------------------------------------------------------------- epilogue
   // Staged store of O: a lane holds one query row, so direct 8-byte stores
@@ -815,30 +852,20 @@ hipError_t launch_fwd_t(FwdKernelParams p, hipStream_t stream) {
     p.xcd_chunk = (p.cu_seqlens_q == nullptr && per_xcd > 0) ? per_xcd : 1;
   }
   dim3 grid(p.num_m_tiles, heads_grid, p.batch * p.num_splits);
+  note_block_k(BK);
   hipLaunchKernelGGL((fwd_tile_kernel<Ty, D, BK, NW, QG, SOFTCAP, LEAD, WPE, NSTAGE, PAGED, ALIBI, EXPP, CPOL, EPI_STAGE>), grid,
                      dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 
-// Tile-shape variant for tuning sweeps (environment ATTN_MI355X_FWD_VARIANT,
-// read at every launch); 0 = default; D = 128: 1 = 128 rows, 2 = 256 rows,
-// 3 = 32-key steps with four stages, 4 = P (and softcap's tanh) with exp2 on
-// the FMA pipe, 5 = 128 rows of 32-key steps at three waves per SIMD, 6 = 256
-// rows with O stored directly from the accumulator layout (no LDS staging);
-// D = 256: 1 = 128 rows, 2 = 256 rows; D = 64: 1 = two waves per SIMD.
-int fwd_variant() {
-  const char* e = getenv("ATTN_MI355X_FWD_VARIANT");
-  return e ? atoi(e) : 0;
-}
-
-
-// Decode tile variant for tuning sweeps (environment ATTN_MI355X_DEC_VARIANT); 0 = default;
-// 1 = 32-key steps with four stages; 2 = K/V copies without the non-temporal
-// policy.  Read at every launch.
-int dec_variant() {
-  const char* e = getenv("ATTN_MI355X_DEC_VARIANT");
-  return e ? atoi(e) : 0;
-}
+// Tile-shape overrides of the debug build (set through attn_debug_set_variants;
+// the release library compiles none of them): forward, D = 128: 1 = 128
+// rows, 2 = 256 rows, 3 = 32-key steps with four stages, 4 = P (and
+// softcap's tanh) with exp2 on the FMA pipe, 5 = 128 rows of 32-key steps at
+// three waves per SIMD, 6 = 256 rows with O stored directly from the
+// accumulator layout; D = 256: 1 = 128 rows, 2 = 256 rows; D = 64: 1 = two
+// waves per SIMD.  Decode: 1 = 32-key steps with four stages, 2 = K/V copies
+// without the non-temporal policy.
 
 template <class Ty, bool CAP, bool AL>
 hipError_t launch_fwd_shape(const FwdKernelParams& p, int head_dim, hipStream_t stream) {
@@ -848,7 +875,7 @@ hipError_t launch_fwd_shape(const FwdKernelParams& p, int head_dim, hipStream_t 
   // with the default policy).  Prefill tiles re-read each K/V tile from L2
   // (every query tile of a column needs it) and keep the default policy.
   const int64_t packed = (int64_t)p.seqlen_q * (p.pack_gqa ? p.group : 1);
-  const bool stream_kv = packed <= 64 && dec_variant() != 2;
+  const bool stream_kv = packed <= 64 && !(kDebugBuild && dec_variant() == 2);
   if (p.block_table != nullptr) {  // paged cache: one tile shape per head dim
     switch (head_dim) {
       case 64:
@@ -869,7 +896,8 @@ hipError_t launch_fwd_shape(const FwdKernelParams& p, int head_dim, hipStream_t 
       // three workgroups per CU) except for decode-shaped launches and ALiBi;
       // variant 1 forces the two-wave tile.
       if constexpr (!AL) {
-        if (packed > 64 && fwd_variant() != 1) return launch_fwd_t<Ty, 64, 64, 4, 1, CAP, 2, 3, 2>(p, stream);
+        if (packed > 64 && !(kDebugBuild && fwd_variant() == 1))
+          return launch_fwd_t<Ty, 64, 64, 4, 1, CAP, 2, 3, 2>(p, stream);
       }
       if (stream_kv) return launch_fwd_t<Ty, 64, 64, 4, 1, CAP, 4, 2, 2, false, AL, false, CPOL_NT>(p, stream);
       return launch_fwd_t<Ty, 64, 64, 4, 1, CAP, 4, 2, 2, false, AL>(p, stream);
@@ -877,14 +905,14 @@ hipError_t launch_fwd_shape(const FwdKernelParams& p, int head_dim, hipStream_t 
     case 128: {
       if (packed <= 64) {
         // Decode-shaped launches (few live rows; the KV stream dominates).
-        if constexpr (!AL) {
+        if constexpr (!AL && kDebugBuild) {
           // Variant 1: 32-key steps, four stages (three steps' copies in flight).
           if (dec_variant() == 1) return launch_fwd_t<Ty, 128, 32, 4, 1, CAP, 4, 2, 4, false, false, false, CPOL_NT>(p, stream);
         }
         if (stream_kv) return launch_fwd_t<Ty, 128, 64, 4, 1, CAP, 4, 2, 2, false, AL, false, CPOL_NT>(p, stream);
         return launch_fwd_t<Ty, 128, 64, 4, 1, CAP, 4, 2, 2, false, AL>(p, stream);
       }
-      if constexpr (!AL) {  // tile variants for tuning sweeps
+      if constexpr (!AL && kDebugBuild) {  // tile overrides of the debug build
         switch (fwd_variant()) {
           case 1: return launch_fwd_t<Ty, 128, 64, 4, 1, CAP, 4, 2>(p, stream);
           case 2: return launch_fwd_t<Ty, 128, 64, 8, 1, CAP, 6, 2>(p, stream);
@@ -896,6 +924,8 @@ hipError_t launch_fwd_shape(const FwdKernelParams& p, int head_dim, hipStream_t 
           case 6: return launch_fwd_t<Ty, 128, 64, 8, 1, CAP, 6, 2, 2, false, false, false, 0, false>(p, stream);
           default: break;
         }
+      }
+      if constexpr (!AL) {
         // Softcap and varlen launches: 128-row tiles of 32-key steps at three
         // waves per SIMD (166 registers; three workgroups per CU, each SIMD
         // interleaving waves of three tiles) -- the VALU-heavier softcap step
@@ -924,7 +954,7 @@ hipError_t launch_fwd_shape(const FwdKernelParams& p, int head_dim, hipStream_t 
       if constexpr (!AL) {
         const int64_t heads_grid = p.pack_gqa ? p.heads_kv : p.heads_q;
         const int64_t wgs256 = (packed + 255) / 256 * heads_grid * p.batch * p.num_splits;
-        const int v = fwd_variant();
+        const int v = kDebugBuild ? fwd_variant() : 0;
         if (v == 2 || (v != 1 && packed > 64 && wgs256 >= 2 * (int64_t)compute_units()))
           return launch_fwd_t<Ty, 256, 32, 8, 1, CAP, 2, 2, 2, false, AL>(p, stream);
       }
@@ -968,26 +998,21 @@ hipError_t launch_combine_dtype(const CombineParams& p, int head_dim, hipStream_
 
 }  // namespace
 
-// Compute units of the current device (queried once per device).
-int compute_units() {
-  static int cus[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
-    cus[dev] = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) ? n : 256;
-  }
-  return cus[dev];
+#if !defined(ATTN_TU_DTYPE) || ATTN_TU_DTYPE == 0
+hipError_t launch_fwd_f16(const FwdKernelParams& p, int head_dim, hipStream_t stream) {
+  return launch_fwd_dtype<TypeF16>(p, head_dim, stream);
 }
-
-hipError_t launch_fwd(const FwdKernelParams& p, int dtype, int head_dim, hipStream_t stream) {
-  return dtype == 1 ? launch_fwd_dtype<TypeBF16>(p, head_dim, stream)
-                    : launch_fwd_dtype<TypeF16>(p, head_dim, stream);
+hipError_t launch_combine_f16(const CombineParams& p, int head_dim, hipStream_t stream) {
+  return launch_combine_dtype<TypeF16>(p, head_dim, stream);
 }
-
-hipError_t launch_combine(const CombineParams& p, int dtype, int head_dim, hipStream_t stream) {
-  return dtype == 1 ? launch_combine_dtype<TypeBF16>(p, head_dim, stream)
-                    : launch_combine_dtype<TypeF16>(p, head_dim, stream);
+#endif
+#if !defined(ATTN_TU_DTYPE) || ATTN_TU_DTYPE == 1
+hipError_t launch_fwd_bf16(const FwdKernelParams& p, int head_dim, hipStream_t stream) {
+  return launch_fwd_dtype<TypeBF16>(p, head_dim, stream);
 }
+hipError_t launch_combine_bf16(const CombineParams& p, int head_dim, hipStream_t stream) {
+  return launch_combine_dtype<TypeBF16>(p, head_dim, stream);
+}
+#endif
 
 }  // namespace attn

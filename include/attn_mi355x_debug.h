@@ -1,0 +1,64 @@
+/*
+ * attn_mi355x_debug.h -- extra entry points of the debug build of the
+ * library, libattn_mi355x_debug.so (compiled from the same sources with
+ * ATTN_DEBUG_BUILD defined).  The release library libattn_mi355x.so exports
+ * none of these.  Everything in attn_mi355x.h is exported by both builds and
+ * behaves the same way.
+ *
+ * The debug build exists to observe what the release kernels cannot show in
+ * their outputs: which branch of the rescale-threshold rule each query row
+ * took on each KV step (release page "v1.7 / flash_attn 2.9.2.post1",
+ * section 1.2: the rescale of O and the row sum is skipped while the row max
+ * rises by at most the threshold, and the max then lags, so P stays at or
+ * below exp2(threshold) = 256; release page "FA2 2.9.0 Kernel Changes in
+ * v1.2", section 3: the first KV step never skips), and to run the tile
+ * shapes the release library's per-shape choice does not pick.
+ */
+#ifndef ATTN_MI355X_DEBUG_H
+#define ATTN_MI355X_DEBUG_H
+
+#include <stdint.h>
+
+#include "attn_mi355x.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * Tile-shape overrides for later forward / decode / backward launches of
+ * this process (0 = the per-shape default the release library uses).
+ * Forward, head_dim 128: 1 = 128 query rows per workgroup, 2 = 256 rows,
+ * 3 = 32-key steps with four LDS stages, 4 = exp2 (and softcap's tanh) on
+ * the FMA pipe, 5 = 128 rows of 32-key steps at three waves per SIMD,
+ * 6 = 256 rows storing O straight from the accumulators; head_dim 256:
+ * 1 = 128 rows, 2 = 256 rows; head_dim 64: 1 = two waves per SIMD.  Decode:
+ * 1 = 32-key steps with four stages, 2 = K/V copies with the default cache
+ * policy.  Backward: 1 = dK/dV in two passes, 2 / 3 = dQ with 256 / 128
+ * queries per workgroup.  Unknown values select the default.  Not
+ * thread-safe; the setting is process-wide.
+ */
+void attn_debug_set_variants(int32_t fwd, int32_t dec, int32_t bwd);
+
+/* KV step (keys per tile) of the last forward tile kernel launched. */
+int32_t attn_debug_last_block_k(void);
+
+/*
+ * attn_fwd plus per-row counters of the rescale-threshold rule.
+ *   args: as for attn_fwd (same validation, same outputs, same bits).
+ *   row_stats: device uint32 [batch, heads_q, seqlen_q, 4], 16-byte aligned,
+ *     written for every query row: [0] KV steps on which the row's running
+ *     max left -inf (1 if the row sees any key, else 0), [1] later steps
+ *     with a visible key that skipped the rescale (the max lagged), [2]
+ *     later steps that rescaled, [3] the bits of the largest fp32 P the row
+ *     formed before its 16-bit conversion (0.0f if none).  A step counts
+ *     only when the row sees at least one of its keys.
+ * Returns ATTN_E_NULL / ATTN_E_ALIGN for a bad row_stats, else as attn_fwd.
+ */
+int attn_fwd_stats(const attn_fwd_args* args, uint32_t* row_stats, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_MI355X_DEBUG_H */

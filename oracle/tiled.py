@@ -68,10 +68,11 @@ def _tiled_one_head(q_h, k_g, v_g, scale, causal, window, softcap, tau, block_k,
     starts = list(range(0, seqlen_k, block_k))
     if order == "descending":
         starts = starts[::-1]
+    ok_all = allowed_mask(seqlen_q, seqlen_k, rows, causal, window[0], window[1])
     for step, j0 in enumerate(starts):
         j1 = min(j0 + block_k, seqlen_k)
         t = transformed_scores(q_h, k_g[j0:j1], scale, softcap)
-        ok = allowed_mask(seqlen_q, seqlen_k, rows, causal, window[0], window[1])[:, j0:j1]
+        ok = ok_all[:, j0:j1]
         t = np.where(ok, t, -np.inf)
         live = ok.any(axis=1)
         first = live & np.isneginf(m)

@@ -1,5 +1,8 @@
 """Helpers shared by the GPU parity tests (comparison against the CPU oracle)."""
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
 
@@ -29,9 +32,29 @@ def gpu_required():
     binding.lib()  # fails loudly if the library is missing
 
 
-def sample_rows(n_rows, count, seed):
-    """Sorted unique query rows: the first, the last, and random ones in between."""
-    rng = np.random.default_rng(seed)
-    rows = set([0, n_rows - 1])
-    rows.update(rng.integers(0, n_rows, size=count).tolist())
-    return np.array(sorted(rows), dtype=np.int64)
+def force_variants(request, fwd=0, dec=0, bwd=0):
+    """Run this test's library calls on the debug build with the given tile overrides (undone at
+    the end of the test).  The release library has no overrides: its kernel choice depends on the
+    call's arguments alone."""
+    from exact_tiled_attention_fa2_amd import debug
+    cm = debug.forced_variants(fwd=fwd, dec=dec, bwd=bwd)
+    cm.__enter__()
+    request.addfinalizer(lambda: cm.__exit__(None, None, None))
+
+
+def run_jobs(fn, jobs, workers=None):
+    """fn over jobs on a thread pool (at most 16 threads, one BLAS thread each), in order.
+
+    The oracle is NumPy: its matrix products and elementwise passes release
+    the GIL, so whole-output references of the full-size workloads are
+    computed one (batch, head) at a time in parallel."""
+    from threadpoolctl import threadpool_limits
+    workers = workers or max(1, min(16, os.cpu_count() or 1))
+    with threadpool_limits(1), ThreadPoolExecutor(workers) as ex:
+        return list(ex.map(fn, jobs))
+
+
+def nan_like(t):
+    """A tensor shaped like t, filled with NaN: an output position the library never writes fails
+    the finiteness gate."""
+    return torch.full_like(t, float("nan"), memory_format=torch.contiguous_format)

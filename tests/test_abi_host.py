@@ -12,6 +12,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "attn_mi355x.h")
+DEBUG_HEADER = os.path.join(ROOT, "include", "attn_mi355x_debug.h")
 
 binding = pytest.importorskip("exact_tiled_attention_fa2_amd.binding")
 
@@ -23,12 +24,18 @@ def _lib():
         pytest.fail(str(e))
 
 
-def _declared_functions():
-    text = open(HEADER).read()
+def _declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(attn_[a-z0-9_]+)\s*\(", text,
                        flags=re.M)
     return sorted(set(names))
+
+
+def _exported(path):
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
+                         check=True).stdout
+    return set(re.findall(r" T (attn_[a-z0-9_]+)", out))
 
 
 def test_library_exports_every_declared_function():
@@ -37,10 +44,23 @@ def test_library_exports_every_declared_function():
     assert {"attn_fwd", "attn_fwd_varlen", "attn_fwd_kvcache", "attn_bwd", "attn_bwd_varlen"} <= set(names)
     for n in names:
         assert hasattr(h, n), f"{n} declared in the header but not exported"
-    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True,
-                         text=True, check=True).stdout
-    exported = set(re.findall(r" T (attn_[a-z0-9_]+)", out))
-    assert set(names) <= exported
+    assert set(names) <= _exported(binding.LIB_PATH)
+
+
+def test_debug_library_exports_both_headers():
+    """The debug build exports every entry point of both headers; the release build exports none
+    of the debug header's and reads no environment variable."""
+    from exact_tiled_attention_fa2_amd import debug
+    debug_names = set(_declared_functions(DEBUG_HEADER))
+    assert {"attn_debug_set_variants", "attn_debug_last_block_k", "attn_fwd_stats"} <= debug_names
+    h = debug.debug_lib()
+    for n in set(_declared_functions()) | debug_names:
+        assert hasattr(h, n), f"{n} not exported by the debug library"
+    assert debug_names <= _exported(debug.DEBUG_LIB_PATH)
+    assert not (debug_names & _exported(binding.LIB_PATH))
+    imports = subprocess.run(["nm", "-D", "--undefined-only", binding.LIB_PATH], capture_output=True,
+                             text=True, check=True).stdout
+    assert "getenv" not in imports
 
 
 def test_version_and_status_strings():

@@ -18,7 +18,7 @@ import torch
 
 import attn_workloads as W
 import oracle
-from gpu_common import gpu_required, np64
+from gpu_common import force_variants, gpu_required, nan_like, np64, run_jobs
 
 pytestmark = pytest.mark.gpu
 
@@ -160,10 +160,10 @@ def test_bwd_finite_2k(dtype):
 
 
 @pytest.mark.parametrize("variant", ["1", "2", "3"])
-def test_bwd_variants(variant, monkeypatch):
+def test_bwd_variants(variant, request):
     """The selectable kernel shapes (two-pass dK/dV; dQ with 256 / 128 queries per workgroup) on a
     ragged GQA causal case with a window and softcap."""
-    monkeypatch.setenv("ATTN_MI355X_BWD_VARIANT", variant)
+    force_variants(request, bwd=int(variant))
     print(f"[case] bwd variant {variant}", flush=True)
     eng = _eng()
     kw = dict(causal=True, window=(100, 0), softcap=20.0)
@@ -178,22 +178,33 @@ def test_bwd_variants(variant, monkeypatch):
     grad_check(np64(dv), rv, "bf16", f"variant {variant} dV")
 
 
-def test_bwd_headline_sampled():
+def test_bwd_headline_whole():
     """The benchmarked backward shape (bf16, B=4, Sq=Sk=2048, 16 heads, D=128, causal) in its default
-    launch configuration (256-query dQ tiles), against the oracle on three sampled (batch, head)
-    pairs in full."""
-    print("[case] bwd headline sampled", flush=True)
+    launch configuration (256-query dQ tiles), against the oracle on the whole dQ, dK and dV; the
+    gradients start as NaN so an unwritten tile fails."""
+    print("[case] bwd headline whole", flush=True)
     eng = _eng()
     c = W.WORKLOADS["bwd_cfg2_bf16_causal_2k"]
-    b, s, h, d = c["batch"], c["seqlen_q"], c["heads_q"], c["head_dim"]
-    q, k, v = W.make_dense(c["seed"], b, s, s, h, h, d, c["dtype"], device="cuda")
+    b_, s, h_, d = c["batch"], c["seqlen_q"], c["heads_q"], c["head_dim"]
+    q, k, v = W.make_dense(c["seed"], b_, s, s, h_, h_, d, c["dtype"], device="cuda")
     do = _dout(c["seed"], tuple(q.shape), c["dtype"])
     o, lse = eng.attn_fwd(q, k, v, causal=True)
-    dq, dk, dv = eng.attn_bwd(q, k, v, o, lse, do, causal=True)
+    dq, dk, dv = nan_like(q), nan_like(k), nan_like(v)
+    eng.attn_bwd(q, k, v, o, lse, do, causal=True, dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
-    for bi, hi in ((0, 0), (1, 7), (3, 15)):
+    qn, kn, vn, don = np64(q), np64(k), np64(v), np64(do)
+
+    def ref(job):
+        bi, hi = job
         sl = (slice(bi, bi + 1), slice(None), slice(hi, hi + 1))
-        rq, rk, rv = oracle.attention_bwd_ref(np64(q[sl]), np64(k[sl]), np64(v[sl]), np64(do[sl]), causal=True)
-        grad_check(np64(dq[sl]), rq, c["dtype"], f"headline ({bi},{hi}) dQ")
-        grad_check(np64(dk[sl]), rk, c["dtype"], f"headline ({bi},{hi}) dK")
-        grad_check(np64(dv[sl]), rv, c["dtype"], f"headline ({bi},{hi}) dV")
+        return oracle.attention_bwd_ref(np.ascontiguousarray(qn[sl]), np.ascontiguousarray(kn[sl]),
+                                        np.ascontiguousarray(vn[sl]), np.ascontiguousarray(don[sl]),
+                                        causal=True)
+
+    jobs = [(bi, hi) for bi in range(b_) for hi in range(h_)]
+    rq, rk, rv = np.empty(qn.shape), np.empty(kn.shape), np.empty(vn.shape)
+    for (bi, hi), (gq, gk, gv) in zip(jobs, run_jobs(ref, jobs)):
+        rq[bi, :, hi], rk[bi, :, hi], rv[bi, :, hi] = gq[0, :, 0], gk[0, :, 0], gv[0, :, 0]
+    grad_check(np64(dq), rq, c["dtype"], "headline dQ")
+    grad_check(np64(dk), rk, c["dtype"], "headline dK")
+    grad_check(np64(dv), rv, c["dtype"], "headline dV")

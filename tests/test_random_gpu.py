@@ -10,7 +10,7 @@ import torch
 
 import attn_workloads as W
 import oracle
-from gpu_common import gate_check, gpu_required, np64
+from gpu_common import force_variants, gate_check, gpu_required, np64
 
 pytestmark = pytest.mark.gpu
 
@@ -53,9 +53,9 @@ BWD_SEEDS = list(range(6000, 6012))
 
 
 @pytest.mark.parametrize("seed", FWD_SEEDS)
-def test_random_forward(seed, monkeypatch):
+def test_random_forward(seed, request):
     c = _draw(seed, [64, 128, 256])
-    monkeypatch.setenv("ATTN_MI355X_FWD_VARIANT", c["variant"])
+    force_variants(request, fwd=int(c["variant"]))
     print(f"[case] random forward {c}", flush=True)
     kw = dict(c["kw"])
     if c["alibi"]:
@@ -84,10 +84,10 @@ def _grad_check(got, ref, dtype, what):
 
 
 @pytest.mark.parametrize("seed", BWD_SEEDS)
-def test_random_backward(seed, monkeypatch):
+def test_random_backward(seed, request):
     c = _draw(seed, [64, 128])
     bwd_variant = str(np.random.default_rng(seed + 1).choice(["0", "1", "2", "3"]))
-    monkeypatch.setenv("ATTN_MI355X_BWD_VARIANT", bwd_variant)
+    force_variants(request, bwd=int(bwd_variant))
     print(f"[case] random backward {c} bwd_variant={bwd_variant}", flush=True)
     kw = dict(c["kw"])
     if c["alibi"]:
