@@ -2,18 +2,24 @@
 """Benchmark of the exact tiled attention forward on one MI355X.
 
 A step is one pass of the hot path over one batch of synthetic input resident
-in HBM.  Default workload: bf16, B=4, H=16, Sq=Sk=2048, D=128, causal (the
-headline prefill configuration).  Prints ONE JSON line with throughput in
-TFLOP/s of algorithmic work (4*D per visible query/key pair, i.e. causal
-pairs only), the roofline of the dominant kernel against the published dense
-bf16 MFMA peak, the same workload's fp64 CPU-oracle rate on a bounded sample,
-and a secondary decode measurement (split-KV, HBM GB/s).
+in HBM.  Default workload: fp16, B=4, Sq=Sk=4096, 32 query / 8 KV heads,
+D=256, causal -- the configuration with the most algorithmic work that fits
+one GPU.  Prints ONE JSON line with its throughput in TFLOP/s of algorithmic
+work (4*D per visible query/key pair, i.e. causal pairs only), the roofline of
+the dominant kernel against the published dense fp16 MFMA peak, the same
+workload's fp64 CPU-oracle rate on a bounded sample, and every other
+workload as a secondary measurement with its own fraction of roofline
+(prefill TFLOP/s; decode HBM GB/s; the backward).
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                  [--no-cpu-baseline] [--no-secondary] [--mode copy]
+                  [--warmup-floor-ms F] [--no-cpu-baseline] [--no-secondary]
+                  [--mode copy]
 
-``--mode copy`` runs a plain device copy of known size instead; it is the
-calibration kernel for the HBM byte counters (FETCH_SIZE / WRITE_SIZE).
+Warm-up: W untimed steps, then more untimed steps until at least F ms
+(default 200) of wall time has gone into them -- the GPU clock settles only
+after ~20 ms of continuous work, so a fixed small W would time a ramping
+clock.  ``--mode copy`` runs a plain device copy of known size instead; it is
+the calibration kernel for the HBM byte counters (FETCH_SIZE / WRITE_SIZE).
 """
 
 import argparse
@@ -29,10 +35,13 @@ sys.path.insert(0, ROOT)
 METRIC = "attn fwd TFLOP/s (4·B·H·Sq·Sk·D) & % MFMA peak; decode HBM GB/s"
 PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0}  # MI355X dense MFMA, published
 PEAK_HBM_GBS = 8000.0                                  # MI355X HBM3E, published
-# Sources the forward tile kernel is compiled from (their hash keys the traffic record).
+HEADLINE = "cfg5b_fp16_d256_causal"
+# Sources the forward tile kernel is compiled from (their hash keys the traffic records).
 KERNEL_SRCS = [os.path.join(ROOT, "exact_tiled_attention_fa2_amd", "csrc", n)
                for n in ("attn_kernels.hip", "attn_device.h")]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_cfg2.json")
+# Per-workload HBM byte counts of the forward tile kernel (rocprofv3 FETCH_SIZE / WRITE_SIZE).
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_{}.json")
+WARMUP_FLOOR_MS = 200.0
 
 
 def log(msg):
@@ -64,10 +73,11 @@ def kernel_sha():
     return h.hexdigest()
 
 
-def load_traffic():
-    """HBM bytes per launch from the committed counter summary, if the kernel is unchanged."""
+def load_traffic(workload):
+    """HBM bytes per launch from the committed counter summary of this workload, if the kernel
+    sources are unchanged since the counters were taken (else None)."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(TRAFFIC_FILE.format(workload)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -76,12 +86,29 @@ def load_traffic():
     return (t["fetch_kib_per_dispatch"] * t["fetch_scale"] + t["write_kib_per_dispatch"] * t["write_scale"]) * 1024.0
 
 
-def time_region(fn, steps, warmup, torch):
-    """W untimed steps, then K timed steps between synchronisations, with HIP events on the
-    current stream (the stream the library launches on).  Returns ms per step."""
+WARMUP_RUN = {}  # workload -> untimed steps actually run (W plus the floor's extra steps)
+
+
+def time_region(fn, steps, warmup, torch, floor_ms=None, tag=None):
+    """W untimed steps (then more until floor_ms of wall time has gone into warm-up), then K
+    timed steps between synchronisations, with HIP events on the current stream (the stream the
+    library launches on).  Returns ms per step."""
+    floor_ms = WARMUP_FLOOR_MS if floor_ms is None else floor_ms
+    t0 = time.perf_counter()
+    ran = 0
     for _ in range(warmup):
         fn()
+        ran += 1
     torch.cuda.synchronize()
+    batch = 1
+    while (time.perf_counter() - t0) * 1e3 < floor_ms:
+        for _ in range(batch):
+            fn()
+        ran += batch
+        torch.cuda.synchronize()
+        batch = min(2 * batch, 64)
+    if tag is not None:
+        WARMUP_RUN[tag] = ran
     stream = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -151,7 +178,7 @@ def bench_dense(name, steps, warmup, torch, eng, W):
         eng.attn_fwd(q, k, v, causal=c["causal"], window=c["window"], softcap=c["softcap"],
                      softmax_scale=c.get("scale"), out=o, lse=lse, alibi_slopes=sl)
 
-    ms = time_region(step, steps, warmup, torch)
+    ms = time_region(step, steps, warmup, torch, tag=name)
     pairs = visible_pairs(c["seqlen_q"], c["seqlen_k"], c["causal"], c["window"])
     flops = 4.0 * c["head_dim"] * pairs * c["batch"] * c["heads_q"]
     literal = 4.0 * c["batch"] * c["heads_q"] * c["seqlen_q"] * c["seqlen_k"] * c["head_dim"]
@@ -176,7 +203,7 @@ def bench_varlen(name, steps, warmup, torch, eng, W):
         eng.attn_fwd_varlen(q, k, v, cu, cu, mx, mx, causal=c["causal"], window=c["window"],
                             softcap=c["softcap"], out=o, lse=lse)
 
-    ms = time_region(step, steps, warmup, torch)
+    ms = time_region(step, steps, warmup, torch, tag=name)
     pairs = sum(visible_pairs(n, n, c["causal"], c["window"]) for n in lens)
     flops = 4.0 * c["head_dim"] * pairs * c["heads_q"]
     literal = sum(4.0 * c["heads_q"] * n * n * c["head_dim"] for n in lens)
@@ -207,7 +234,7 @@ def bench_kvcache(name, steps, warmup, torch, eng, W):
         eng.attn_fwd_kvcache(q, kc, vc, cache_seqlens=lens, num_splits=c["num_splits"], out=o, lse=lse,
                              workspace=ws, block_table=table, alibi_slopes=sl)
 
-    ms = time_region(step, steps, warmup, torch)
+    ms = time_region(step, steps, warmup, torch, tag=name)
     el = 2  # 16-bit
     bytes_alg = (2 * c["batch"] * c["seqlen_k"] * c["heads_kv"] * c["head_dim"] * el
                  + 2 * q.numel() * el + lse.numel() * 4)
@@ -236,7 +263,7 @@ def bench_bwd(name, steps, warmup, torch, eng, W):
         eng.attn_bwd(q, k, v, o, lse, do, causal=c["causal"], window=c["window"], softcap=c["softcap"],
                      dq=dq, dk=dk, dv=dv, workspace=ws)
 
-    ms = time_region(step, steps, warmup, torch)
+    ms = time_region(step, steps, warmup, torch, tag=name)
     pairs = visible_pairs(c["seqlen_q"], c["seqlen_k"], c["causal"], c["window"])
     flops = 10.0 * c["head_dim"] * pairs * c["batch"] * c["heads_q"]
     tflops = flops / (ms * 1e-3) / 1e12
@@ -284,12 +311,31 @@ def run_copy(steps, warmup, torch):
                       "GBps_read_plus_write": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
+PREFILL_SECONDARY = ["cfg2_bf16_causal_2k", "cfg2r_bf16_causal_2k_kramp", "cfg3_bf16_varlen",
+                     "cfg4_bf16_gqa_window_softcap"]
+
+
+def prefill_entry(name, steps, warmup, torch, eng, W):
+    """One prefill workload as a secondary record with its own fraction of the MFMA peak."""
+    c = W.WORKLOADS[name]
+    fn = bench_varlen if c["kind"] == "varlen" else bench_dense
+    ms, flops, config, cfg = fn(name, steps, warmup, torch, eng, W)
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_MFMA_TFLOPS[cfg["dtype"]]
+    return {"workload": name, "ms_per_step": round(ms, 5), "value": round(tflops, 2), "unit": "TFLOP/s",
+            "frac_of_mfma_peak": round(tflops / peak, 4), "peak": peak, "dtype": cfg["dtype"],
+            "flops_per_step": flops, "literal_formula_tflops": config["literal_formula_tflops"],
+            "traffic": load_traffic(name), "warmup_steps_run": WARMUP_RUN.get(name),
+            "note": "one fwd_tile_kernel launch per step; algorithmic FLOPs = 4*D per visible pair"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=400)
-    ap.add_argument("--workload", default="cfg2_bf16_causal_2k")
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--warmup-floor-ms", type=float, default=WARMUP_FLOOR_MS)
+    ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--mode", default="attn", choices=["attn", "copy", "pages-latency"])
@@ -309,6 +355,8 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    global WARMUP_FLOOR_MS
+    WARMUP_FLOOR_MS = args.warmup_floor_ms
     eng.lib()
     if args.mode == "copy":
         run_copy(args.steps, args.warmup, torch)
@@ -318,7 +366,7 @@ def main():
         return
 
     c = W.WORKLOADS[args.workload]
-    log(f"workload {args.workload}: warmup {args.warmup}, steps {args.steps}")
+    log(f"workload {args.workload}: warmup {args.warmup} (floor {WARMUP_FLOOR_MS:g} ms), steps {args.steps}")
     if c["kind"] == "kvcache":
         sec = bench_kvcache(args.workload, args.steps, args.warmup, torch, eng, W)
         line = {"metric": METRIC, "value": sec["value"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -328,7 +376,8 @@ def main():
                                                                            "heads_q", "heads_kv", "head_dim",
                                                                            "num_splits")}},
                 "roofline": {"bound": "hbm", "achieved": sec["value"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                             "frac": sec["frac_of_hbm_peak"], "traffic": None}}
+                             "frac": sec["frac_of_hbm_peak"], "traffic": None},
+                "warmup_steps_run": WARMUP_RUN.get(args.workload)}
         print(json.dumps(line), flush=True)
         return
 
@@ -344,7 +393,7 @@ def main():
                 "roofline": {"bound": "mfma", "achieved": sec["value"], "peak": sec["peak"], "unit": "TFLOP/s",
                              "frac": sec["frac_of_mfma_peak"], "traffic": None,
                              "kernel": "bwd_dot + bwd_dkdv + bwd_dq (one attn_bwd call per step)"},
-                "note": sec["note"]}
+                "warmup_steps_run": WARMUP_RUN.get(args.workload), "note": sec["note"]}
         print(json.dumps(line), flush=True)
         return
 
@@ -355,23 +404,32 @@ def main():
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_MFMA_TFLOPS[cfg["dtype"]]
     log(f"{args.workload}: {ms:.4f} ms/step, {tflops:.1f} TFLOP/s")
-    traffic = load_traffic() if args.workload == "cfg2_bf16_causal_2k" else None
     line = {"metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg["dtype"],
             "data": "synthetic", "config": config,
             "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": peak, "unit": "TFLOP/s",
-                         "frac": round(tflops / peak, 4), "traffic": traffic,
-                         "kernel": "fwd_tile_kernel (one launch per step)"}}
+                         "frac": round(tflops / peak, 4), "traffic": load_traffic(args.workload),
+                         "kernel": "fwd_tile_kernel (one launch per step)"},
+            "warmup_steps_run": WARMUP_RUN.get(args.workload)}
     if not args.no_secondary:
+        line["secondary"] = []
+        for name in PREFILL_SECONDARY:
+            if name == args.workload:
+                continue
+            log(f"secondary: {name}")
+            torch.cuda.empty_cache()
+            line["secondary"].append(prefill_entry(name, args.steps, args.warmup, torch, eng, W))
+        torch.cuda.empty_cache()
         log("secondary: cfg5a decode")
+        dec = bench_kvcache("cfg5a_bf16_decode", args.steps, args.warmup, torch, eng, W)
+        dec["warmup_steps_run"] = WARMUP_RUN.get("cfg5a_bf16_decode")
+        line["secondary"].append(dec)
         torch.cuda.empty_cache()
-        line["secondary"] = [bench_kvcache("cfg5a_bf16_decode", max(5, args.steps // 5),
-                                           max(2, args.warmup // 10), torch, eng, W)]
-        torch.cuda.empty_cache()
-        log("secondary: backward of the headline workload")
-        line["secondary"].append(bench_bwd("bwd_cfg2_bf16_causal_2k", max(5, args.steps // 4),
-                                           max(20, args.warmup // 4), torch, eng, W))
+        log("secondary: backward, bf16 4x2048 16 heads D=128 causal")
+        bwd = bench_bwd("bwd_cfg2_bf16_causal_2k", args.steps, args.warmup, torch, eng, W)
+        bwd["warmup_steps_run"] = WARMUP_RUN.get("bwd_cfg2_bf16_causal_2k")
+        line["secondary"].append(bwd)
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline and c["kind"] == "dense":
         log("cpu baseline (oracle on a bounded sample)")
