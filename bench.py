@@ -330,6 +330,7 @@ def prefill_entry(name, steps, warmup, torch, eng, W):
 
 
 def main():
+    global WARMUP_FLOOR_MS
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
@@ -355,7 +356,6 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    global WARMUP_FLOOR_MS
     WARMUP_FLOOR_MS = args.warmup_floor_ms
     eng.lib()
     if args.mode == "copy":
