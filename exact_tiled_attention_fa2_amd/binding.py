@@ -113,6 +113,8 @@ def configure(h):
     h.attn_fwd_varlen.restype = ctypes.c_int
     h.attn_fwd_kvcache.argtypes = [ctypes.POINTER(KvcacheArgs), _vp, ctypes.c_size_t, _vp]
     h.attn_fwd_kvcache.restype = ctypes.c_int
+    h.attn_fwd_kvcache_noalloc.argtypes = [ctypes.POINTER(KvcacheArgs), _vp]
+    h.attn_fwd_kvcache_noalloc.restype = ctypes.c_int
     h.attn_varlen_workspace_bytes.argtypes = [_i32] * 5
     h.attn_varlen_workspace_bytes.restype = ctypes.c_size_t
     h.attn_kvcache_workspace_bytes.argtypes = [_i32] * 5
@@ -257,17 +259,9 @@ def attn_kvcache_workspace_bytes(batch, seqlen_q, heads_q, head_dim, num_splits)
     return int(lib().attn_kvcache_workspace_bytes(batch, seqlen_q, heads_q, head_dim, num_splits))
 
 
-def attn_fwd_kvcache(q, k_cache, v_cache, cache_seqlens=None, num_splits=0, causal=False,
-                     window=(-1, -1), softcap=0.0, softmax_scale=None, rescale_threshold=-1.0,
-                     out=None, lse=None, return_lse=True, workspace=None, stream=None,
-                     block_table=None, alibi_slopes=None):
-    """Split-KV attention against a cache: q [B, Sq, Hq, D], caches [B, Sk, Hkv, D].
-
-    Paged cache: with block_table (int32 [B, max_pages_per_seq]) the caches are
-    [num_pages, page_block_size, Hkv, D] and the capacity per sequence is
-    max_pages_per_seq * page_block_size.
-    """
-    _need_gpu(q, k_cache, v_cache, cache_seqlens, block_table)
+def _kvcache_args(q, k_cache, v_cache, cache_seqlens, num_splits, causal, window, softcap, softmax_scale,
+                  rescale_threshold, out, lse, block_table, alibi_slopes):
+    """The attn_kvcache_args struct of one call (num_splits passed through: 0 = the library's pick)."""
     b, sq, hq, d = q.shape
     hkv = k_cache.shape[2]
     if block_table is None:
@@ -281,6 +275,27 @@ def attn_fwd_kvcache(q, k_cache, v_cache, cache_seqlens=None, num_splits=0, caus
         paging = (block_table, block_table.stride(0), page, k_cache.shape[0])
     if cache_seqlens is not None and cache_seqlens.dtype != torch.int32:
         raise TypeError("cache_seqlens must be int32")
+    return KvcacheArgs(_dtype_code(q), b, sq, sk, hq, hkv, d, int(num_splits), _ptr(q), _ptr(k_cache),
+                       _ptr(v_cache), _ptr(cache_seqlens), _ptr(out), _ptr(lse),
+                       *q.stride()[:3], *k_cache.stride()[:3], *v_cache.stride()[:3], *out.stride()[:3],
+                       _opts(causal, window, softcap, softmax_scale, rescale_threshold, alibi_slopes),
+                       _ptr(paging[0]), paging[1], paging[2], paging[3], 0)
+
+
+def attn_fwd_kvcache(q, k_cache, v_cache, cache_seqlens=None, num_splits=0, causal=False,
+                     window=(-1, -1), softcap=0.0, softmax_scale=None, rescale_threshold=-1.0,
+                     out=None, lse=None, return_lse=True, workspace=None, stream=None,
+                     block_table=None, alibi_slopes=None):
+    """Split-KV attention against a cache: q [B, Sq, Hq, D], caches [B, Sk, Hkv, D].
+
+    Paged cache: with block_table (int32 [B, max_pages_per_seq]) the caches are
+    [num_pages, page_block_size, Hkv, D] and the capacity per sequence is
+    max_pages_per_seq * page_block_size.
+    """
+    _need_gpu(q, k_cache, v_cache, cache_seqlens, block_table)
+    b, sq, hq, d = q.shape
+    hkv = k_cache.shape[2]
+    sk = k_cache.shape[1] if block_table is None else block_table.shape[1] * k_cache.shape[1]
     if out is None:
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
     if lse is None and return_lse:
@@ -289,15 +304,29 @@ def attn_fwd_kvcache(q, k_cache, v_cache, cache_seqlens=None, num_splits=0, caus
     need = attn_kvcache_workspace_bytes(b, sq, hq, d, splits)
     if need > 0 and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    a = KvcacheArgs(_dtype_code(q), b, sq, sk, hq, hkv, d, splits, _ptr(q), _ptr(k_cache),
-                    _ptr(v_cache), _ptr(cache_seqlens), _ptr(out), _ptr(lse),
-                    *q.stride()[:3], *k_cache.stride()[:3], *v_cache.stride()[:3], *out.stride()[:3],
-                    _opts(causal, window, softcap, softmax_scale, rescale_threshold, alibi_slopes),
-                    _ptr(paging[0]), paging[1], paging[2], paging[3], 0)
+    a = _kvcache_args(q, k_cache, v_cache, cache_seqlens, splits, causal, window, softcap, softmax_scale,
+                      rescale_threshold, out, lse, block_table, alibi_slopes)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().attn_fwd_kvcache(ctypes.byref(a), _ptr(workspace), ws_bytes, _stream(stream, q.device)),
            "attn_fwd_kvcache")
     return out, lse
+
+
+def attn_fwd_kvcache_noalloc(q, k_cache, v_cache, out, lse=None, cache_seqlens=None, num_splits=0,
+                             causal=False, window=(-1, -1), softcap=0.0, softmax_scale=None,
+                             rescale_threshold=-1.0, stream=None, block_table=None, alibi_slopes=None):
+    """attn_fwd_kvcache through the entry point that allocates nothing: the caller passes the
+    output (and optionally the LSE) tensor, and the split partials live in the library's static
+    per-GPU scratch (at most ATTN_NOALLOC_SCRATCH_BYTES).  Nothing here allocates either."""
+    _need_gpu(q, k_cache, v_cache, out, lse, cache_seqlens, block_table)
+    a = _kvcache_args(q, k_cache, v_cache, cache_seqlens, num_splits, causal, window, softcap,
+                      softmax_scale, rescale_threshold, out, lse, block_table, alibi_slopes)
+    _check(lib().attn_fwd_kvcache_noalloc(ctypes.byref(a), _stream(stream, q.device)),
+           "attn_fwd_kvcache_noalloc")
+    return out, lse
+
+
+ATTN_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def attn_bwd_workspace_bytes(batch, seqlen_q, heads_q):

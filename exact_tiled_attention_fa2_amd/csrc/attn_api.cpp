@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "attn_internal.h"
 #include "attn_mi355x.h"
@@ -253,13 +254,25 @@ size_t attn_kvcache_workspace_bytes(int32_t batch, int32_t seqlen_q, int32_t hea
   return rows * (size_t)head_dim * sizeof(float) + rows * sizeof(float);
 }
 
-int attn_fwd_kvcache(const attn_kvcache_args* a, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and kernel parameters of attn_fwd_kvcache, everything but the
+// workspace.  Returns ATTN_OK with `empty` set when there is nothing to
+// launch; `need` is the workspace the call requires.
+int prepare_kvcache(const attn_kvcache_args* a, FwdKernelParams& p, size_t& need, bool& empty) {
+  empty = false;
+  need = 0;
   if (a == nullptr) return ATTN_E_NULL;
   int st = check_common(a->dtype, a->head_dim, a->heads_q, a->heads_kv, a->opts);
   if (st != ATTN_OK) return st;
   if (a->batch < 0 || a->seqlen_q < 0 || a->seqlen_k < 0) return ATTN_E_SHAPE;
   if (a->num_splits < 0 || a->num_splits > 256) return ATTN_E_ARG;
-  if (a->batch == 0 || a->seqlen_q == 0) return ATTN_OK;
+  if (a->batch == 0 || a->seqlen_q == 0) {
+    empty = true;
+    return ATTN_OK;
+  }
   if (a->q == nullptr || a->o == nullptr) return ATTN_E_NULL;
   if (a->seqlen_k > 0 && (a->k_cache == nullptr || a->v_cache == nullptr)) return ATTN_E_NULL;
   if (a->block_table != nullptr) {
@@ -280,11 +293,8 @@ int attn_fwd_kvcache(const attn_kvcache_args* a, void* workspace, size_t workspa
                              ? a->num_splits
                              : attn_kvcache_num_splits(a->batch, a->seqlen_q, a->heads_q, a->heads_kv,
                                                        a->seqlen_k, a->head_dim);
-  const size_t need = attn_kvcache_workspace_bytes(a->batch, a->seqlen_q, a->heads_q, a->head_dim, splits);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
-    return ATTN_E_WORKSPACE;
+  need = attn_kvcache_workspace_bytes(a->batch, a->seqlen_q, a->heads_q, a->head_dim, splits);
 
-  FwdKernelParams p;
   std::memset(&p, 0, sizeof(p));
   p.q = a->q; p.k = a->k_cache; p.v = a->v_cache; p.o = a->o; p.lse = a->lse;
   p.seqused_k = a->cache_seqlens;
@@ -305,18 +315,79 @@ int attn_fwd_kvcache(const attn_kvcache_args* a, void* workspace, size_t workspa
   p.pack_gqa = p.group > 1 ? 1 : 0;
   p.num_splits = splits;
   resolve_opts(a->opts, a->head_dim, p);
+  return ATTN_OK;
+}
+
+// Device scratch of attn_fwd_kvcache_noalloc: the fp32 split partials live
+// here instead of in a caller workspace.  Every GPU the library runs on holds
+// its own copy until the process ends.  In host code `scratch` names only a
+// host-side stand-in, so kernels are given the device address that
+// hipGetSymbolAddress returns for it, fetched once per device with that
+// device current and kept in scratch_ptr.
+static __device__ __align__(256) char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
+
+std::mutex scratch_mu;
+void* scratch_ptr[64] = {nullptr};
+
+// Device address of the current device's scratch (nullptr on failure).
+void* scratch_of_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    scratch_ptr[dev] = ptr;
+  }
+  return scratch_ptr[dev];
+}
+
+// Split kernel (fp32 partials in `workspace` when there is more than one
+// split) and the combine, on the caller's stream.
+int launch_kvcache(const attn_kvcache_args* a, FwdKernelParams& p, void* workspace, hipStream_t stream) {
+  const int32_t splits = p.num_splits;
   if (splits > 1) {
     const size_t rows = (size_t)splits * a->batch * a->heads_q * a->seqlen_q;
     p.o_part = static_cast<float*>(workspace);
     p.lse_part = p.o_part + rows * a->head_dim;
   }
-  hipError_t e = attn::launch_fwd(p, a->dtype, a->head_dim, (hipStream_t)stream);
+  hipError_t e = attn::launch_fwd(p, a->dtype, a->head_dim, stream);
   if (e != hipSuccess || splits == 1) return launch_status(e);
   attn::CombineParams c;
   c.o_part = p.o_part; c.lse_part = p.lse_part; c.o = a->o; c.lse = a->lse;
   c.o_batch = a->o_batch_stride; c.o_row = a->o_row_stride; c.o_head = a->o_head_stride;
   c.batch = a->batch; c.seqlen_q = a->seqlen_q; c.heads_q = a->heads_q; c.num_splits = splits;
-  return launch_status(attn::launch_combine(c, a->dtype, a->head_dim, (hipStream_t)stream));
+  return launch_status(attn::launch_combine(c, a->dtype, a->head_dim, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd_kvcache(const attn_kvcache_args* a, void* workspace, size_t workspace_bytes, void* stream) {
+  FwdKernelParams p;
+  size_t need = 0;
+  bool empty = false;
+  const int st = prepare_kvcache(a, p, need, empty);
+  if (st != ATTN_OK || empty) return st;
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
+    return ATTN_E_WORKSPACE;
+  return launch_kvcache(a, p, workspace, (hipStream_t)stream);
+}
+
+int attn_fwd_kvcache_noalloc(const attn_kvcache_args* a, void* stream) {
+  FwdKernelParams p;
+  size_t need = 0;
+  bool empty = false;
+  const int st = prepare_kvcache(a, p, need, empty);
+  if (st != ATTN_OK || empty) return st;
+  if (need > ATTN_NOALLOC_SCRATCH_BYTES) return ATTN_E_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0) {
+    ws = scratch_of_current_device();
+    if (ws == nullptr) return ATTN_E_LAUNCH;
+  }
+  return launch_kvcache(a, p, ws, (hipStream_t)stream);
 }
 
 size_t attn_bwd_workspace_bytes(int32_t batch, int32_t seqlen_q, int32_t heads_q) {

@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define ATTN_VERSION 130
+#define ATTN_VERSION 140
 
 enum attn_status {
   ATTN_OK = 0,
@@ -221,6 +221,30 @@ size_t attn_kvcache_workspace_bytes(int32_t batch, int32_t seqlen_q, int32_t hea
                                     int32_t head_dim, int32_t num_splits);
 int attn_fwd_kvcache(const attn_kvcache_args* args, void* workspace, size_t workspace_bytes,
                      void* stream);
+
+/*
+ * attn_fwd_kvcache_noalloc -- attn_fwd_kvcache with no workspace argument,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  It
+ * allocates nothing (no hipMalloc / hipFree, no allocating library call):
+ * the split partials go to a static device array of
+ * ATTN_NOALLOC_SCRATCH_BYTES bytes that each GPU holds for the life of the
+ * process.  The caller still owns and passes q, the caches, o and lse.
+ *   args: as for attn_fwd_kvcache (same validation, same kernels, the same
+ *     bits as attn_fwd_kvcache with the same split count).
+ *   The scratch of the current device is used, so `stream` must belong to
+ *     the current device.
+ * Returns ATTN_E_WORKSPACE when attn_kvcache_workspace_bytes() of the call
+ * exceeds ATTN_NOALLOC_SCRATCH_BYTES (pick fewer splits), ATTN_E_LAUNCH if
+ * the scratch address cannot be obtained, else as attn_fwd_kvcache.
+ * Every call on a GPU shares that GPU's scratch: calls that overlap in time
+ * on one GPU (different streams without ordering) race and must not be
+ * issued; calls on one stream are ordered and safe.  Nothing in the scratch
+ * needs to start at zero: every partial the combine reads is written by the
+ * same call first.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int attn_fwd_kvcache_noalloc(const attn_kvcache_args* args, void* stream);
 
 /*
  * attn_bwd -- gradients of attn_fwd: dQ, dK, dV for a loss whose gradient

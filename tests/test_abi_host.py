@@ -65,7 +65,7 @@ def test_debug_library_exports_both_headers():
 
 def test_version_and_status_strings():
     h = _lib()
-    assert h.attn_version() == 130
+    assert h.attn_version() == 140
     for code in range(-9, 1):
         assert binding.status_string(code)
     assert binding.status_string(-1234) == "unknown status"
@@ -209,6 +209,37 @@ def test_kvcache_workspace_and_splits():
     assert h.attn_fwd_kvcache(ctypes.byref(ka), 16, need - 1, None) == binding.ATTN_E_WORKSPACE
     ka.num_splits = 999
     assert h.attn_fwd_kvcache(ctypes.byref(ka), 16, need, None) == binding.ATTN_E_ARG
+
+
+def test_kvcache_noalloc_validation():
+    """The allocation-free kv-cache entry validates like attn_fwd_kvcache and rejects a call whose
+    split partials exceed its static scratch -- all on the host, before any HIP call (fake device
+    pointers here).  The scratch size matches the header's ATTN_NOALLOC_SCRATCH_BYTES."""
+    h = _lib()
+    ka = binding.KvcacheArgs(1, 32, 1, 32768, 32, 8, 128, 16, 16, 16, 16, None, 16, None,
+                             32 * 128, 32 * 128, 128, 32768 * 8 * 128, 8 * 128, 128,
+                             32768 * 8 * 128, 8 * 128, 128, 32 * 128, 32 * 128, 128)
+    ka.opts = binding.SoftmaxOpts(0.0, 0, -1, -1, 0.0, -1.0)
+    assert h.attn_fwd_kvcache_noalloc(None, None) == binding.ATTN_E_NULL
+    # 128 splits of 32 x 32 rows need 128 * 1024 * 129 * 4 B = 64.5 MiB > 64 MiB
+    ka.num_splits = 128
+    assert binding.attn_kvcache_workspace_bytes(32, 1, 32, 128, 128) > binding.ATTN_NOALLOC_SCRATCH_BYTES
+    assert h.attn_fwd_kvcache_noalloc(ctypes.byref(ka), None) == binding.ATTN_E_WORKSPACE
+    ka.num_splits = 999
+    assert h.attn_fwd_kvcache_noalloc(ctypes.byref(ka), None) == binding.ATTN_E_ARG
+    ka.num_splits, ka.q = 16, 24
+    assert h.attn_fwd_kvcache_noalloc(ctypes.byref(ka), None) == binding.ATTN_E_ALIGN
+    ka.q, ka.heads_q = 16, 30
+    assert h.attn_fwd_kvcache_noalloc(ctypes.byref(ka), None) == binding.ATTN_E_HEADS
+    ka.heads_q, ka.batch = 32, 0
+    assert h.attn_fwd_kvcache_noalloc(ctypes.byref(ka), None) == 0       # empty: nothing launched
+    with tempfile.TemporaryDirectory() as d:
+        src, exe = os.path.join(d, "c.c"), os.path.join(d, "c")
+        open(src, "w").write('#include <stdio.h>\n#include "attn_mi355x.h"\n'
+                             'int main(void) { printf("%zu\\n", ATTN_NOALLOC_SCRATCH_BYTES); return 0; }\n')
+        subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), src, "-o", exe], check=True)
+        out = subprocess.run([exe], capture_output=True, text=True, check=True).stdout
+    assert int(out) == binding.ATTN_NOALLOC_SCRATCH_BYTES
 
 
 def test_kvcache_paged_validation():
