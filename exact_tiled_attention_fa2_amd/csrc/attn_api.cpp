@@ -519,6 +519,9 @@ int attn_fwd_stats(const attn_fwd_args* a, uint32_t* row_stats, void* stream) {
   bool empty = false;
   const int st = prepare_fwd(a, p, empty);
   if (st != ATTN_OK || empty) return st;
+#ifndef ATTN_ROW_STATS
+  return ATTN_E_UNSUPPORTED;  // a sweep build without the counters
+#endif
   if (row_stats == nullptr) return ATTN_E_NULL;
   if (!aligned16(row_stats)) return ATTN_E_ALIGN;
   p.row_stats = row_stats;

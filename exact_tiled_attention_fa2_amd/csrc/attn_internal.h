@@ -106,6 +106,9 @@ int compute_units();
 // and sweeps, set through an explicit call, and the per-row rescale
 // counters.  The release library has neither: the kernel a call runs
 // depends on its arguments alone.
+#if defined(ATTN_DEBUG_BUILD) && !defined(ATTN_NO_ROW_STATS)
+#define ATTN_ROW_STATS 1  // per-row counters (a sweep build may leave them out)
+#endif
 #ifdef ATTN_DEBUG_BUILD
 constexpr bool kDebugBuild = true;
 struct DebugState {

@@ -374,7 +374,7 @@ fwd_tile_kernel(const FwdKernelParams p) {
     for (int dt = 0; dt < DT; ++dt) acc[g][dt] = f32x16{};
   }
 
-#ifdef ATTN_DEBUG_BUILD
+#ifdef ATTN_ROW_STATS
   // Per-row rescale counters (debug build): first max, skips, rescales, largest P.
   uint32_t st_first[QG], st_skip[QG], st_resc[QG];
   float st_pmax[QG];
@@ -477,7 +477,6 @@ fwd_tile_kernel(const FwdKernelParams p) {
       // (no exchange between the two halves is needed for that).  Otherwise
       // the halves agree on the row max and rows that rose too far rescale.
       [[maybe_unused]] const float m_before = m_run[g];
-      [[maybe_unused]] bool rescaled = false;
       if (__any(mx > m_run[g] + tau_raw)) {
         const float mx_row = fmaxf(mx, __shfl_xor(mx, 32));
         const float m_new = fmaxf(m_run[g], mx_row);
@@ -489,16 +488,19 @@ fwd_tile_kernel(const FwdKernelParams p) {
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) acc[g][dt] *= alpha;
           m_run[g] = m_new;
-          rescaled = true;
         }
       }
-#ifdef ATTN_DEBUG_BUILD
+#ifdef ATTN_ROW_STATS
       if (p.row_stats != nullptr) {  // wave-uniform
         const float mrow = fmaxf(mx, __shfl_xor(mx, 32));
+        // A live row that rescales moves its running max up (the new max exceeds the old one by
+        // more than the threshold); a skip leaves it in place.  Selects, not branches: divergent
+        // branches here made the compiler move the accumulators to scratch memory.
         if (mrow > -INFINITY) {  // the row sees a key of this step
-          if (m_before == -INFINITY) ++st_first[g];
-          else if (rescaled) ++st_resc[g];
-          else ++st_skip[g];
+          const bool first = m_before == -INFINITY;
+          st_first[g] += first ? 1u : 0u;
+          st_resc[g] += (!first && m_run[g] != m_before) ? 1u : 0u;
+          st_skip[g] += (!first && m_run[g] == m_before) ? 1u : 0u;
         }
       }
 #endif
@@ -514,7 +516,7 @@ fwd_tile_kernel(const FwdKernelParams p) {
                                 : fast_exp2(fmaf(sc[g][kt][r2 + 1], c2, nb));
           l_run[g] += p0 + p1;
           pk[g][kt][r2 >> 1] = Ty::pack(p0, p1);
-#ifdef ATTN_DEBUG_BUILD
+#ifdef ATTN_ROW_STATS
           st_pmax[g] = fmaxf(st_pmax[g], fmaxf(p0, p1));
 #endif
         }
@@ -644,7 +646,7 @@ fwd_tile_kernel(const FwdKernelParams p) {
     }
   }
 
-#ifdef ATTN_DEBUG_BUILD
+#ifdef ATTN_ROW_STATS
   if (p.row_stats != nullptr && p.o_part == nullptr) {  // one 16-byte record per valid row
 #pragma unroll
     for (int g = 0; g < QG; ++g) {
@@ -951,6 +953,11 @@ hipError_t launch_fwd_shape(const FwdKernelParams& p, int head_dim, hipStream_t 
       // 256) when the grid gives every CU two such workgroups; otherwise, for
       // decode-shaped launches and with ALiBi (whose slopes would spill), 128
       // rows at one wave per SIMD.  Variants 1 / 2 force 128 / 256 rows.
+      if constexpr (!AL && kDebugBuild) {
+        // 3: 128 rows at two waves per SIMD (two workgroups per CU); 4: 256 rows, operand lead 4.
+        if (fwd_variant() == 3) return launch_fwd_t<Ty, 256, 32, 4, 1, CAP, 2, 2, 2, false, AL>(p, stream);
+        if (fwd_variant() == 4) return launch_fwd_t<Ty, 256, 32, 8, 1, CAP, 4, 2, 2, false, AL>(p, stream);
+      }
       if constexpr (!AL) {
         const int64_t heads_grid = p.pack_gqa ? p.heads_kv : p.heads_q;
         const int64_t wgs256 = (packed + 255) / 256 * heads_grid * p.batch * p.num_splits;

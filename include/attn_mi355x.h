@@ -135,8 +135,10 @@ int attn_fwd(const attn_fwd_args* args, void* stream);
  *   max_seqlen_q / max_seqlen_k: host upper bounds of the per-sequence lengths
  *     (used for the grid; a sequence longer than its bound is truncated).
  *   o like q, lse [heads_q, total_q] contiguous fp32 (may be NULL).
- *   workspace: attn_varlen_workspace_bytes() bytes of device memory for the
- *     tile schedule (may be NULL when that size is 0).
+ *   workspace: reserved.  attn_varlen_workspace_bytes() is 0 in this version
+ *     (the grid is sized by max_seqlen_q and each workgroup reads its
+ *     sequence bounds from cu_seqlens on the device; tiles past a sequence's
+ *     end exit at once), so workspace may be NULL and is not read.
  */
 typedef struct attn_varlen_args {
   int32_t dtype;
@@ -213,8 +215,12 @@ typedef struct attn_kvcache_args {
   int32_t reserved0;          /* must be 0 */
 } attn_kvcache_args;
 
-/* Split count the library picks when num_splits == 0 (never forced to 1
- * when the problem is too small to fill the GPU). */
+/* Split count the library picks when num_splits == 0: about four workgroups
+ * per compute unit, at least four 64-key steps per split, at most 128 splits.
+ * It is never forced to 1 just because the problem is too small to fill the
+ * GPU -- the release notes of fa4-v4.0.0.beta33 on the Dao-AILab
+ * "flash-attention" project page report that upstream bug in the ROCm split
+ * heuristic.  Returns 1 for empty or non-positive sizes. */
 int32_t attn_kvcache_num_splits(int32_t batch, int32_t seqlen_q, int32_t heads_q,
                                 int32_t heads_kv, int32_t seqlen_k, int32_t head_dim);
 size_t attn_kvcache_workspace_bytes(int32_t batch, int32_t seqlen_q, int32_t heads_q,
