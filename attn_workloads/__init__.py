@@ -77,6 +77,9 @@ WORKLOADS = {
     "cfg5b_fp16_d256_causal": dict(kind="dense", seed=1006, batch=4, seqlen_q=4096,
                                    seqlen_k=4096, heads_q=32, heads_kv=8, head_dim=256,
                                    dtype="fp16", causal=True, window=(-1, -1), softcap=0.0),
+    "bwd_cfg5b_fp16_d256_causal": dict(kind="bwd", seed=1006, batch=4, seqlen_q=4096,
+                                       seqlen_k=4096, heads_q=32, heads_kv=8, head_dim=256,
+                                       dtype="fp16", causal=True, window=(-1, -1), softcap=0.0),
 }
 
 

@@ -426,11 +426,12 @@ def main():
         dec["warmup_steps_run"] = WARMUP_RUN.get("cfg5a_bf16_decode")
         line["secondary"].append(dec)
         torch.cuda.empty_cache()
-        log("secondary: backward, bf16 4x2048 16 heads D=128 causal")
-        bwd = bench_bwd("bwd_cfg2_bf16_causal_2k", args.steps, args.warmup, torch, eng, W)
-        bwd["warmup_steps_run"] = WARMUP_RUN.get("bwd_cfg2_bf16_causal_2k")
-        line["secondary"].append(bwd)
-        torch.cuda.empty_cache()
+        for name in ("bwd_cfg2_bf16_causal_2k", "bwd_cfg5b_fp16_d256_causal"):
+            log(f"secondary: backward {name}")
+            bwd = bench_bwd(name, args.steps, args.warmup, torch, eng, W)
+            bwd["warmup_steps_run"] = WARMUP_RUN.get(name)
+            line["secondary"].append(bwd)
+            torch.cuda.empty_cache()
     if not args.no_cpu_baseline and c["kind"] == "dense":
         log("cpu baseline (oracle on a bounded sample)")
         line["cpu_baseline"] = cpu_baseline(cfg)

@@ -399,7 +399,6 @@ int attn_bwd(const attn_bwd_args* a, void* workspace, size_t workspace_bytes, vo
   if (a == nullptr) return ATTN_E_NULL;
   int st = check_common(a->dtype, a->head_dim, a->heads_q, a->heads_kv, a->opts);
   if (st != ATTN_OK) return st;
-  if (a->head_dim == 256) return ATTN_E_UNSUPPORTED;
   if (a->batch < 0 || a->seqlen_q < 0 || a->seqlen_k < 0) return ATTN_E_SHAPE;
   if (a->batch == 0 || (a->seqlen_q == 0 && a->seqlen_k == 0)) return ATTN_OK;
   if (a->seqlen_q > 0 && (a->q == nullptr || a->o == nullptr || a->dout == nullptr || a->lse == nullptr ||
@@ -455,7 +454,6 @@ int attn_bwd_varlen(const attn_bwd_varlen_args* a, void* workspace, size_t works
   if (a == nullptr) return ATTN_E_NULL;
   int st = check_common(a->dtype, a->head_dim, a->heads_q, a->heads_kv, a->opts);
   if (st != ATTN_OK) return st;
-  if (a->head_dim == 256) return ATTN_E_UNSUPPORTED;
   if (a->batch < 0 || a->total_q < 0 || a->total_k < 0 || a->max_seqlen_q < 0 || a->max_seqlen_k < 0)
     return ATTN_E_SHAPE;
   if (a->batch == 0 || (a->total_q == 0 && a->total_k == 0)) return ATTN_OK;

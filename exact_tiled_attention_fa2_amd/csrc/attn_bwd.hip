@@ -275,7 +275,9 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), am
 bwd_dkdv_kernel(const BwdKernelParams p) {
   static_assert(PASSES == 1 || PASSES == 2, "one or two passes");
   constexpr int NT = NW * 64;
-  constexpr int BQ = 64;            // queries per step
+  // Queries per step: 64, or 32 at D = 256 (six stage tiles of 64 rows of
+  // 512 bytes would not fit the 160 KB of LDS).
+  constexpr int BQ = D > 128 ? 32 : 64;
   constexpr int QB = BQ / 32;       // 32-query MFMA blocks per step
   constexpr int BN = 32 * NW;       // keys per workgroup
   constexpr int ROWB = D * 2;
@@ -435,7 +437,8 @@ bwd_dkdv_kernel(const BwdKernelParams p) {
         // One wave per SIMD hides no LDS latency behind another wave: all of
         // the block's operand reads are issued before its MFMAs.
         // In batches of RB k-steps (all of them at one wave per SIMD).
-        constexpr int RB = WPE == 1 ? DS : (DS >= 4 ? 2 : DS);
+        // At D = 256 the K and V rows alone take 128 registers: batches of four.
+        constexpr int RB = (WPE == 1 && D <= 128) ? DS : (D > 128 ? 4 : (DS >= 4 ? 2 : DS));
         f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int t0 = 0; t0 < DS; t0 += RB) {
@@ -458,7 +461,7 @@ bwd_dkdv_kernel(const BwdKernelParams p) {
         // in one batch they would stall it), ahead of the elementwise work;
         // at two waves per SIMD the other wave covers their latency and the
         // registers are needed elsewhere.
-        constexpr bool TR_AHEAD = WPE == 1;
+        constexpr bool TR_AHEAD = WPE == 1 && D <= 128;
         u32x4 tg[2][DT], tq[2][DT];
         if constexpr (TR_AHEAD) {
 #pragma unroll
@@ -617,8 +620,10 @@ bwd_dkdv_kernel(const BwdKernelParams p) {
 }
 
 // ---------------------------------------------------------------- dQ
-template <class Ty, int D, bool SOFTCAP, bool ALIBI, int NW = 4>
-__global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(2, 2)))
+// NW waves of 32 queries, WPE waves per SIMD (2; 1 at D = 256, where the Q
+// and dO fragments and the dQ accumulators alone take 256 registers).
+template <class Ty, int D, bool SOFTCAP, bool ALIBI, int NW = 4, int WPE = 2>
+__global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(WPE, WPE)))
 bwd_dq_kernel(const BwdKernelParams p) {
   constexpr int NT = NW * 64;
   constexpr int BK = 64;            // keys per step
@@ -846,32 +851,45 @@ hipError_t launch_bwd_t(const BwdKernelParams& p, hipStream_t stream) {
     const dim3 grid((unsigned)((rows + RPB - 1) / RPB));
     hipLaunchKernelGGL((bwd_dot_kernel<Ty, D>), grid, dim3(256), 0, stream, p);
   }
-  if (p.seqlen_k > 0) {
-    bool two_pass = false;
-    if constexpr (kDebugBuild) {
-      if (bwd_variant() == 1) {
-        const dim3 grid((unsigned)((p.seqlen_k + 255) / 256), p.heads_kv, p.batch);
-        hipLaunchKernelGGL((bwd_dkdv_kernel<Ty, D, SOFTCAP, ALIBI, 8, 2, 2>), grid, dim3(512), 0, stream, p);
-        two_pass = true;
+  if constexpr (D > 128) {
+    // D = 256: dK/dV in two walks (dV, then dK) at one wave per SIMD, and dQ at
+    // one wave per SIMD -- the register file of two waves per SIMD is too small.
+    if (p.seqlen_k > 0) {
+      const dim3 grid((unsigned)((p.seqlen_k + 127) / 128), p.heads_kv, p.batch);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<Ty, D, SOFTCAP, ALIBI, 4, 1, 2>), grid, dim3(256), 0, stream, p);
+    }
+    if (p.seqlen_q > 0) {
+      const dim3 grid((unsigned)((p.seqlen_q + 127) / 128), p.heads_q, p.batch);
+      hipLaunchKernelGGL((bwd_dq_kernel<Ty, D, SOFTCAP, ALIBI, 4, 1>), grid, dim3(256), 0, stream, p);
+    }
+  } else {
+    if (p.seqlen_k > 0) {
+      bool two_pass = false;
+      if constexpr (kDebugBuild) {
+        if (bwd_variant() == 1) {
+          const dim3 grid((unsigned)((p.seqlen_k + 255) / 256), p.heads_kv, p.batch);
+          hipLaunchKernelGGL((bwd_dkdv_kernel<Ty, D, SOFTCAP, ALIBI, 8, 2, 2>), grid, dim3(512), 0, stream, p);
+          two_pass = true;
+        }
+      }
+      if (!two_pass) {
+        const dim3 grid((unsigned)((p.seqlen_k + 127) / 128), p.heads_kv, p.batch);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<Ty, D, SOFTCAP, ALIBI, 4, 1, 1>), grid, dim3(256), 0, stream, p);
       }
     }
-    if (!two_pass) {
-      const dim3 grid((unsigned)((p.seqlen_k + 127) / 128), p.heads_kv, p.batch);
-      hipLaunchKernelGGL((bwd_dkdv_kernel<Ty, D, SOFTCAP, ALIBI, 4, 1, 1>), grid, dim3(256), 0, stream, p);
-    }
-  }
-  if (p.seqlen_q > 0) {
-    // 256 queries per workgroup (8 waves, two per SIMD; half the K/V re-reads
-    // from L2) when that grid gives every CU two workgroups, else 128
-    // (twice the workgroups); the debug build's variant 2 forces 256, 3 forces 128.
-    const int64_t wgs256 = (int64_t)((p.seqlen_q + 255) / 256) * p.heads_q * p.batch;
-    const int v = kDebugBuild ? bwd_variant() : 0;
-    if (v == 2 || (v != 3 && wgs256 >= 2 * (int64_t)compute_units())) {
-      const dim3 grid((unsigned)((p.seqlen_q + 255) / 256), p.heads_q, p.batch);
-      hipLaunchKernelGGL((bwd_dq_kernel<Ty, D, SOFTCAP, ALIBI, 8>), grid, dim3(512), 0, stream, p);
-    } else {
-      const dim3 grid((unsigned)((p.seqlen_q + 127) / 128), p.heads_q, p.batch);
-      hipLaunchKernelGGL((bwd_dq_kernel<Ty, D, SOFTCAP, ALIBI>), grid, dim3(256), 0, stream, p);
+    if (p.seqlen_q > 0) {
+      // 256 queries per workgroup (8 waves, two per SIMD; half the K/V re-reads
+      // from L2) when that grid gives every CU two workgroups, else 128
+      // (twice the workgroups); the debug build's variant 2 forces 256, 3 forces 128.
+      const int64_t wgs256 = (int64_t)((p.seqlen_q + 255) / 256) * p.heads_q * p.batch;
+      const int v = kDebugBuild ? bwd_variant() : 0;
+      if (v == 2 || (v != 3 && wgs256 >= 2 * (int64_t)compute_units())) {
+        const dim3 grid((unsigned)((p.seqlen_q + 255) / 256), p.heads_q, p.batch);
+        hipLaunchKernelGGL((bwd_dq_kernel<Ty, D, SOFTCAP, ALIBI, 8>), grid, dim3(512), 0, stream, p);
+      } else {
+        const dim3 grid((unsigned)((p.seqlen_q + 127) / 128), p.heads_q, p.batch);
+        hipLaunchKernelGGL((bwd_dq_kernel<Ty, D, SOFTCAP, ALIBI>), grid, dim3(256), 0, stream, p);
+      }
     }
   }
   return hipGetLastError();
@@ -888,6 +906,7 @@ template <class Ty>
 hipError_t launch_bwd_ty(const BwdKernelParams& p, int head_dim, hipStream_t stream) {
   if (head_dim == 64) return launch_bwd_d<Ty, 64>(p, stream);
   if (head_dim == 128) return launch_bwd_d<Ty, 128>(p, stream);
+  if (head_dim == 256) return launch_bwd_d<Ty, 256>(p, stream);
   return hipErrorInvalidValue;
 }
 

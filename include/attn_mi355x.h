@@ -271,7 +271,8 @@ int attn_fwd_kvcache_noalloc(const attn_kvcache_args* args, void* stream);
  *   opts as for attn_fwd; rescale_threshold is not used (the backward does
  *     not run the online softmax).
  *   workspace: attn_bwd_workspace_bytes() bytes (fp32 D per query row).
- *   head_dim 64 or 128 (256: ATTN_E_UNSUPPORTED).
+ *   head_dim 64, 128 or 256 (the project survey page's csrc/flash_attn entry
+ *   lists backward kernels up to head dim 256).
  * No atomics: every output element has one owner, so results are
  * deterministic.
  */

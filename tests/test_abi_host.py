@@ -307,7 +307,7 @@ def _bwd_args(**over):
 
 
 _BAD_BWD = [
-    (dict(head_dim=256), binding.ATTN_E_UNSUPPORTED),
+    (dict(head_dim=96), binding.ATTN_E_UNSUPPORTED),
     (dict(dtype=3), binding.ATTN_E_UNSUPPORTED),
     (dict(heads_q=3), binding.ATTN_E_HEADS),
     (dict(seqlen_q=-1), binding.ATTN_E_SHAPE),

@@ -76,6 +76,10 @@ DENSE = [
     (86, 1, 300, 100, 2, 2, 128, "bf16", dict(causal=True)),          # rows with no key
     (87, 1, 64, 64, 2, 1, 128, "fp16", dict(causal=False, window=(0, 0))),
     (88, 2, 97, 161, 6, 3, 64, "bf16", dict(causal=False, softcap=5.0, alibi=True)),
+    # head_dim 256 (two-pass dK/dV and dQ at one wave per SIMD)
+    (181, 1, 257, 257, 4, 2, 256, "fp16", dict(causal=True)),
+    (182, 2, 190, 300, 4, 1, 256, "bf16", dict(causal=False, softcap=20.0, alibi=True)),
+    (183, 1, 300, 200, 2, 2, 256, "fp16", dict(causal=True, window=(64, 0))),   # rows with no key
 ]
 
 
@@ -115,6 +119,59 @@ def test_bwd_varlen():
     grad_check(np64(dq), rq, "bf16", "varlen dQ")
     grad_check(np64(dk), rk, "bf16", "varlen dK")
     grad_check(np64(dv), rv, "bf16", "varlen dV")
+
+
+def test_bwd_varlen_d256():
+    """Packed sequences at head_dim 256 (one of length 1, one empty), GQA, causal, fp16."""
+    print("[case] bwd varlen d256", flush=True)
+    eng = _eng()
+    lens = [130, 1, 0, 200, 33]
+    q, k, v, cu, lens = W.make_varlen(184, len(lens), 1, 1, 8, 2, 256, "fp16", device="cuda", lengths=lens)
+    do = _dout(184, tuple(q.shape), "fp16")
+    o, lse = eng.attn_fwd_varlen(q, k, v, cu, cu, max(lens), max(lens), causal=True)
+    dq, dk, dv = eng.attn_bwd_varlen(q, k, v, o, lse, do, cu, cu, max(lens), max(lens), causal=True)
+    torch.cuda.synchronize()
+    cu_np = cu.cpu().numpy()
+    rq, rk, rv = oracle.attention_bwd_varlen_ref(np64(q), np64(k), np64(v), np64(do), cu_np, cu_np, causal=True)
+    grad_check(np64(dq), rq, "fp16", "varlen d256 dQ")
+    grad_check(np64(dk), rk, "fp16", "varlen d256 dK")
+    grad_check(np64(dv), rv, "fp16", "varlen d256 dV")
+
+
+def test_bwd_cfg5b_shape_whole():
+    """The backward at the fp16 D=256 prefill shape (B=4, Sq=Sk=4096, 32 query / 8 KV heads,
+    causal) against the oracle on the whole dQ, dK and dV (dK, dV sum their four query heads);
+    the gradients start as NaN so an unwritten tile fails."""
+    print("[case] bwd cfg5b shape whole", flush=True)
+    eng = _eng()
+    c = W.WORKLOADS["cfg5b_fp16_d256_causal"]
+    b_, s, hq, hkv, d = c["batch"], c["seqlen_q"], c["heads_q"], c["heads_kv"], c["head_dim"]
+    q, k, v = W.make_dense(c["seed"], b_, s, s, hq, hkv, d, c["dtype"], device="cuda")
+    do = _dout(c["seed"], tuple(q.shape), c["dtype"])
+    o, lse = eng.attn_fwd(q, k, v, causal=True)
+    dq, dk, dv = nan_like(q), nan_like(k), nan_like(v)
+    eng.attn_bwd(q, k, v, o, lse, do, causal=True, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    qn, kn, vn, don = np64(q), np64(k), np64(v), np64(do)
+    g = hq // hkv
+
+    def ref(job):
+        bi, kh = job
+        hs = slice(kh * g, (kh + 1) * g)
+        return oracle.attention_bwd_ref(np.ascontiguousarray(qn[bi:bi + 1, :, hs]),
+                                        np.ascontiguousarray(kn[bi:bi + 1, :, kh:kh + 1]),
+                                        np.ascontiguousarray(vn[bi:bi + 1, :, kh:kh + 1]),
+                                        np.ascontiguousarray(don[bi:bi + 1, :, hs]), causal=True)
+
+    jobs = [(bi, kh) for bi in range(b_) for kh in range(hkv)]
+    rq, rk, rv = np.empty(qn.shape), np.empty(kn.shape), np.empty(vn.shape)
+    for (bi, kh), (gq, gk, gv) in zip(jobs, run_jobs(ref, jobs)):
+        rq[bi, :, kh * g:(kh + 1) * g] = gq[0]
+        rk[bi, :, kh], rv[bi, :, kh] = gk[0, :, 0], gv[0, :, 0]
+    del qn, kn, vn, don
+    grad_check(np64(dq), rq, "fp16", "cfg5b shape dQ")
+    grad_check(np64(dk), rk, "fp16", "cfg5b shape dK")
+    grad_check(np64(dv), rv, "fp16", "cfg5b shape dV")
 
 
 def test_bwd_deterministic():
