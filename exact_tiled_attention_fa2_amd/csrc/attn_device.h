@@ -84,6 +84,23 @@ __device__ __forceinline__ void dma16_pol(const void* g, const char* lds) {
                                    (__attribute__((address_space(3))) void*)(lds), 16, 0, CPOL);
 }
 
+// HBM -> LDS copies through a buffer resource: the tile's base address lives
+// in scalar registers and each lane adds a 32-bit byte offset, so a copy
+// costs one VGPR per lane instead of a 64-bit address.  Word 3 of the
+// resource selects raw 32-bit data on gfx9-family parts (0x00020000); the
+// record count is the whole 32-bit range, so an offset never reads past it
+// and the hardware returns zero instead of faulting for an out-of-range one.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, -1, 0x00020000);
+}
+// One 16-byte copy per lane of tile byte `voff` into LDS bytes
+// [lds + 16 lane, +16) (`lds` wave-uniform), with cache policy CPOL.
+template <int CPOL>
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, const char* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds), 16, voff, 0, 0,
+                                           CPOL);
+}
+
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
 // Workgroup barrier of a tile pipeline: this wave's LDS reads and writes have

@@ -319,12 +319,16 @@ fwd_tile_kernel(const FwdKernelParams p) {
   const int64_t k_rowb = 2 * p.k_row, v_rowb = 2 * p.v_row;
   const int64_t k_pageb = 2 * p.k_batch, v_pageb = 2 * p.v_batch;
   int cp_row[LOADS], cp_col[LOADS];  // tile row and global byte column of each copy
+  uint32_t off_k[LOADS], off_v[LOADS];  // byte offset of each copy from the tile's first row
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
     const int u = (NW * i + wave) * 64 + lane;
     const int r = u / CH, pos = u % CH;
     cp_row[i] = r;
     cp_col[i] = (pos ^ (chunk_swizzle(r & 15) & SWZ_MASK)) << 4;
+    // Row strides are below 2^24 elements, so (BK - 1) rows + a column stay below 2^31 bytes.
+    off_k[i] = (uint32_t)(r * (int)(2 * p.k_row) + cp_col[i]);
+    off_v[i] = (uint32_t)(r * (int)(2 * p.v_row) + cp_col[i]);
   }
   // Page holding KV step blk of a paged cache (clamped into the pool); a
   // tile never straddles pages (the page size is a multiple of 64).
@@ -337,8 +341,8 @@ fwd_tile_kernel(const FwdKernelParams p) {
   auto page_of = [&](int blk) __attribute__((always_inline)) -> int {
     return min(max(btab[(int64_t)b * p.bt_stride + blk * BK / p.page_size], 0), p.num_pages - 1);
   };
-  auto copy_tile = [&](const char* gbase, int64_t rowb, int64_t pageb, char* tile, int blk, int pg)
-      __attribute__((always_inline)) {
+  auto copy_tile = [&](const char* gbase, int64_t rowb, int64_t pageb, char* tile, int blk, int pg,
+                       const uint32_t (&off)[LOADS]) __attribute__((always_inline)) {
     const int j0 = blk * BK;
     const char* tb;  // row j0 of this tile
     if constexpr (paged) {
@@ -346,10 +350,10 @@ fwd_tile_kernel(const FwdKernelParams p) {
     } else {
       tb = gbase + (int64_t)j0 * rowb;
     }
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(tb);
     if (j0 + BK <= sk) {
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i)
-        dma16_pol<CPOL>(tb + (uint32_t)(cp_row[i] * (int)rowb + cp_col[i]), tile + (NW * i + wave) * 1024);
+      for (int i = 0; i < LOADS; ++i) dma16_buf<CPOL>(rs, off[i], tile + (NW * i + wave) * 1024);
     } else {
       // Last, partial step: rows at or past the valid length re-read row
       // sk-1 instead.  Their scores are masked to -inf, so P = 0 multiplies
@@ -358,7 +362,7 @@ fwd_tile_kernel(const FwdKernelParams p) {
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
         const int r = min(cp_row[i], sk - 1 - j0);
-        dma16_pol<CPOL>(tb + (int64_t)r * rowb + cp_col[i], tile + (NW * i + wave) * 1024);
+        dma16_buf<CPOL>(rs, (uint32_t)(r * (int)rowb + cp_col[i]), tile + (NW * i + wave) * 1024);
       }
     }
   };
@@ -576,8 +580,8 @@ fwd_tile_kernel(const FwdKernelParams p) {
       if constexpr (paged) {
         if (r + NSTAGE < n) pg_next = page_of(blk + NSTAGE);
       }
-      copy_tile(kbase, k_rowb, k_pageb, kbuf(std::integral_constant<int, FILL>{}), blk + NSTAGE - 1, pg);
-      copy_tile(vbase, v_rowb, v_pageb, vbuf(std::integral_constant<int, FILL>{}), blk + NSTAGE - 1, pg);
+      copy_tile(kbase, k_rowb, k_pageb, kbuf(std::integral_constant<int, FILL>{}), blk + NSTAGE - 1, pg, off_k);
+      copy_tile(vbase, v_rowb, v_pageb, vbuf(std::integral_constant<int, FILL>{}), blk + NSTAGE - 1, pg, off_v);
     }
     if (wave_live && wave_sees(blk)) {  // otherwise the wave only helps with the copies
       qk_part(kbuf(std::integral_constant<int, ST>{}));
@@ -605,21 +609,21 @@ fwd_tile_kernel(const FwdKernelParams p) {
     // Prologue: tiles of the first NSTAGE - 1 steps.
     {
       const int pg0 = paged ? page_of(blk_lo) : 0;
-      copy_tile(kbase, k_rowb, k_pageb, lds_k0, blk_lo, pg0);
-      copy_tile(vbase, v_rowb, v_pageb, lds_v0, blk_lo, pg0);
+      copy_tile(kbase, k_rowb, k_pageb, lds_k0, blk_lo, pg0, off_k);
+      copy_tile(vbase, v_rowb, v_pageb, lds_v0, blk_lo, pg0, off_v);
     }
     if constexpr (NSTAGE > 2) {
       if (n > 1) {
         const int pg1 = paged ? page_of(blk_lo + 1) : 0;
-        copy_tile(kbase, k_rowb, k_pageb, lds_k1, blk_lo + 1, pg1);
-        copy_tile(vbase, v_rowb, v_pageb, lds_v1, blk_lo + 1, pg1);
+        copy_tile(kbase, k_rowb, k_pageb, lds_k1, blk_lo + 1, pg1, off_k);
+        copy_tile(vbase, v_rowb, v_pageb, lds_v1, blk_lo + 1, pg1, off_v);
       }
     }
     if constexpr (NSTAGE > 3) {
       if (n > 2) {
         const int pg2 = paged ? page_of(blk_lo + 2) : 0;
-        copy_tile(kbase, k_rowb, k_pageb, lds_k2, blk_lo + 2, pg2);
-        copy_tile(vbase, v_rowb, v_pageb, lds_v2, blk_lo + 2, pg2);
+        copy_tile(kbase, k_rowb, k_pageb, lds_k2, blk_lo + 2, pg2, off_k);
+        copy_tile(vbase, v_rowb, v_pageb, lds_v2, blk_lo + 2, pg2, off_v);
       }
     }
     pg_next = (paged && NSTAGE - 1 < n) ? page_of(blk_lo + NSTAGE - 1) : 0;
