@@ -13,13 +13,17 @@ workload as a secondary measurement with its own fraction of roofline
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                   [--warmup-floor-ms F] [--no-cpu-baseline] [--no-secondary]
-                  [--mode copy]
+                  [--mode copy|gemm]
 
 Warm-up: W untimed steps, then more untimed steps until at least F ms
 (default 200) of wall time has gone into them -- the GPU clock settles only
 after ~20 ms of continuous work, so a fixed small W would time a ramping
 clock.  ``--mode copy`` runs a plain device copy of known size instead; it is
 the calibration kernel for the HBM byte counters (FETCH_SIZE / WRITE_SIZE).
+``--mode gemm`` times the vendor's dense GEMM (torch.matmul, 16-bit, square
+and wide shapes) with the same warm-up: the matrix-core rate this board
+sustains once its clock has settled under full load, context for the
+fraction of the published peak (not a bound the attention kernel is held to).
 """
 
 import argparse
@@ -311,6 +315,20 @@ def run_copy(steps, warmup, torch):
                       "GBps_read_plus_write": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
+def run_gemm(steps, warmup, torch):
+    for dt in (torch.float16, torch.bfloat16):
+        for m, n, k in ((8192, 8192, 8192), (16384, 16384, 8192), (8192, 8192, 16384)):
+            a = torch.randn(m, k, device="cuda", dtype=dt)
+            b = torch.randn(k, n, device="cuda", dtype=dt)
+            c = torch.empty(m, n, device="cuda", dtype=dt)
+            ms = time_region(lambda: torch.matmul(a, b, out=c), steps, warmup, torch)
+            print(json.dumps({"mode": "gemm", "dtype": str(dt).replace("torch.", ""), "m": m, "n": n, "k": k,
+                              "ms": round(ms, 4), "tflops": round(2.0 * m * n * k / (ms * 1e-3) / 1e12, 1),
+                              "note": "torch.matmul (vendor GEMM), context only"}), flush=True)
+            del a, b, c
+            torch.cuda.empty_cache()
+
+
 PREFILL_SECONDARY = ["cfg2_bf16_causal_2k", "cfg2r_bf16_causal_2k_kramp", "cfg3_bf16_varlen",
                      "cfg4_bf16_gqa_window_softcap"]
 
@@ -339,7 +357,7 @@ def main():
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--mode", default="attn", choices=["attn", "copy", "pages-latency"])
+    ap.add_argument("--mode", default="attn", choices=["attn", "copy", "gemm", "pages-latency"])
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -360,6 +378,9 @@ def main():
     eng.lib()
     if args.mode == "copy":
         run_copy(args.steps, args.warmup, torch)
+        return
+    if args.mode == "gemm":
+        run_gemm(args.steps, args.warmup, torch)
         return
     if args.mode == "pages-latency":
         run_pages_latency(args.steps, args.warmup, torch, eng, W)

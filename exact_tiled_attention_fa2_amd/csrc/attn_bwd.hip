@@ -14,21 +14,23 @@
 // Three kernels, in stream order, no atomics (every output element has one
 // owner, so the result is deterministic):
 //  * bwd_dot_kernel: D = rowsum(dO * O) in fp32 (HBM-bound, one pass).
-//  * bwd_dkdv_kernel: one workgroup per 128-key tile of one KV head.  A wave
-//    owns 32 keys, holds their K and V rows as MFMA B operands in VGPRs and
-//    walks the query tiles of every query head of its GQA group: S = Q K^T
-//    and dP = dO V^T (A = Q / dO rows read from LDS), then the elementwise
-//    P and dS, then dV^T += dO^T P and dK^T += Q^T dS (A = Q^T / dO^T read
+//  * bwd_dkdv_pair_kernel (head_dim 64 / 128; bwd_dkdv_kernel in two walks at
+//    256): one workgroup per 128-key tile of one KV head.  32 keys belong to
+//    a pair of waves on one SIMD that walks the query tiles of every query
+//    head of its GQA group: S = Q K^T and dP = dO V^T (A = Q / dO rows read
+//    from LDS, B = the keys' K / V rows held in VGPRs), the elementwise P and
+//    dS, then dV^T += dO^T P and dK^T += Q^T dS (A = Q^T / dO^T read
 //    transposed from the same LDS tiles with ds_read_b64_tr_b16, B = the
-//    packed P / dS registers).  In these accumulators a lane holds one key.
+//    packed P / dS registers); one wave of the pair forms S, P and dV, the
+//    other dP, dS and dK.  In these accumulators a lane holds one key.
 //  * bwd_dq_kernel: one workgroup per 128-query tile of one query head, the
 //    forward's orientation (a lane holds one query): S^T = K Q^T and
 //    dP^T = V dO^T (A = K / V rows from LDS, B = Q / dO held in VGPRs), the
 //    elementwise dS^T, then dQ^T += K^T dS^T (A = K^T read transposed from
 //    the K tile).  It recomputes S and dP, which the dK/dV kernel also
 //    forms: seven tile products instead of five, traded for no atomics.
-// Q/dO (dK/dV kernel) and K/V (dQ kernel) tiles stream HBM -> LDS with
-// global_load_lds in the forward's XOR-swizzled layout, double-buffered.
+// Q/dO (dK/dV kernels, three stages) and K/V (dQ kernel, two stages) tiles
+// stream HBM -> LDS with global_load_lds in the forward's XOR-swizzled layout.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -619,6 +621,364 @@ bwd_dkdv_kernel(const BwdKernelParams p) {
   if constexpr (PASSES == 2) run_pass(std::integral_constant<int, 1>{});
 }
 
+// ---------------------------------------------------------------- dK, dV in wave pairs
+// Eight waves, two per SIMD.  Waves w and w + 4 (one SIMD) own the same 32
+// keys and split a step's four tile products between them:
+//  * the P wave (w < 4) forms S = Q K^T and P = exp2(c s - LSE), accumulates
+//    dV^T += dO^T P, and leaves P (times the softcap derivative g) packed to
+//    16 bits in LDS, in its own register layout;
+//  * the dS wave (w >= 4) runs one step behind: dP = dO V^T, then
+//    dS = (P g)(dP - D) from that LDS copy, and dK^T += Q^T dS.
+// A wave holds one gradient's accumulators and one of the K / V row sets, so
+// two waves fit per SIMD without forming S twice, and the two roles' matrix
+// and elementwise phases interleave on the SIMD.  dS is formed from the
+// 16-bit P that the dV product also uses.  Q / dO tiles stream one step
+// ahead into three stages: a step reads its own tiles (P wave) and the
+// previous step's (dS wave).  Both waves of a pair derive the same mask and
+// skip decisions from the pair's key range, so the dS wave reads exactly the
+// steps the P wave wrote.
+template <class Ty, int D, bool SOFTCAP, bool ALIBI>
+__global__ void __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+bwd_dkdv_pair_kernel(const BwdKernelParams p) {
+  constexpr int NW = 8, NT = 512, NP = 4;  // waves, threads, wave pairs
+  constexpr int BQ = D > 128 ? 32 : 64;    // queries per step
+  constexpr int QB = BQ / 32;              // 32-query MFMA blocks per step
+  constexpr int BN = 32 * NP;              // keys per workgroup
+  constexpr int ROWB = D * 2;
+  constexpr int TILEB = BQ * ROWB;
+  constexpr int DS = D / 16;
+  constexpr int DT = D / 32;
+  using Copier = TileCopier<BQ, D, NT>;
+
+  __shared__ __attribute__((aligned(16))) char lds_q0[TILEB];
+  __shared__ __attribute__((aligned(16))) char lds_q1[TILEB];
+  __shared__ __attribute__((aligned(16))) char lds_q2[TILEB];
+  __shared__ __attribute__((aligned(16))) char lds_g0[TILEB];
+  __shared__ __attribute__((aligned(16))) char lds_g1[TILEB];
+  __shared__ __attribute__((aligned(16))) char lds_g2[TILEB];
+  // P hand-over: [step parity][pair][query block][half] of 64 lanes x 16 bytes.
+  __shared__ __attribute__((aligned(16))) u32x4 lds_p[2][NP][QB][2][64];
+  __shared__ __attribute__((aligned(16))) float lds_lse[3][BQ];
+  __shared__ __attribute__((aligned(16))) float lds_dd[3][BQ];
+  auto qbuf = [&](auto st) __attribute__((always_inline)) -> char* {
+    constexpr int S = decltype(st)::value;
+    if constexpr (S == 0) return lds_q0;
+    else if constexpr (S == 1) return lds_q1;
+    else return lds_q2;
+  };
+  auto gbuf = [&](auto st) __attribute__((always_inline)) -> char* {
+    constexpr int S = decltype(st)::value;
+    if constexpr (S == 0) return lds_g0;
+    else if constexpr (S == 1) return lds_g1;
+    else return lds_g2;
+  };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pair = wave & (NP - 1);
+  const bool p_wave = wave < NP;
+  const int l32 = lane & 31;
+  const int hl = lane >> 5;
+
+  const TileRank tr = tile_rank();
+  const int kvh = tr.head, b = tr.b;
+  const SeqRange sr = seq_range(p, b);
+  const int sq = sr.sq, sk = sr.sk, off = sk - sq;
+  const int n0 = tr.rank * BN;
+  if (n0 >= sk) return;
+  const int wl = p.window_left, wr = p.window_right;
+  const int G = p.group;
+
+  // This lane's key and the pair's key range.
+  const int wk_lo = n0 + 32 * pair;
+  const int key = wk_lo + l32;
+  const bool key_valid = key < sk;
+  const int keyc = key_valid ? key : sk - 1;
+  const bool wave_live = wk_lo < sk;
+  const int wk_hi = min(sk - 1, wk_lo + 31);
+
+  // Queries that see some key of this workgroup, walked per query head.
+  const int wg_hi = min(sk - 1, n0 + BN - 1);
+  const int q_lo = (wr >= 0) ? max(0, n0 - off - wr) : 0;
+  const int q_hi = (wl >= 0) ? min(sq - 1, wg_hi - off + wl) : sq - 1;
+  const int qblk_lo = q_lo / BQ;
+  const int nsph = (q_hi >= q_lo) ? (q_hi / BQ + 1 - qblk_lo) : 0;
+  const int n = G * nsph;
+
+  OperandOffsets<D> oo;
+  oo.init(lane);
+  Copier cp;
+  cp.init(wave, lane, NW);
+
+  const float c2 = p.scale_log2;
+  const float icap = p.inv_softcap;
+
+  auto advance = [&](int& h, int& q0) __attribute__((always_inline)) {
+    q0 += BQ;
+    if (q0 >= (qblk_lo + nsph) * BQ) {
+      q0 = qblk_lo * BQ;
+      ++h;
+    }
+  };
+  auto issue = [&](int h, int q0, char* qt, char* gt) __attribute__((always_inline)) {
+    const char* qb = reinterpret_cast<const char*>(p.q) +
+                     2 * (b * p.q_batch + (int64_t)(sr.q_start + q0) * p.q_row + h * p.q_head);
+    const char* gb = reinterpret_cast<const char*>(p.dout) +
+                     2 * (b * p.do_batch + (int64_t)(sr.q_start + q0) * p.do_row + h * p.do_head);
+    cp.copy(qb, 2 * p.q_row, sq - q0, qt, wave, NW);
+    cp.copy(gb, 2 * p.do_row, sq - q0, gt, wave, NW);
+  };
+  // LSE / D rows of a step: loaded by the first BQ threads (P waves) one step
+  // ahead, staged to LDS slot (step % 3) at the end of the step before.
+  float st_lse = 0.0f, st_dd = 0.0f;
+  auto issue_rows = [&](int h, int q0) __attribute__((always_inline)) {
+    if (tid < BQ) {
+      const int q = q0 + tid;
+      const int64_t li = b * p.lse_batch + (int64_t)h * p.lse_head + sr.q_start + q;
+      st_lse = q < sq ? p.lse[li] : -INFINITY;
+      st_dd = q < sq ? p.dsum[li] : 0.0f;
+    }
+  };
+  auto stage_rows = [&](int slot) __attribute__((always_inline)) {
+    if (tid < BQ) {
+      lds_lse[slot][tid] = lse_to_exp2(st_lse);
+      lds_dd[slot][tid] = st_dd;
+    }
+  };
+  // Does the pair see any (query, key) of the step at q0?  And all of them?
+  auto sees = [&](int q0) __attribute__((always_inline)) -> bool {
+    const int qv_hi = min(sq - 1, q0 + BQ - 1);
+    return wave_live && (wr < 0 || wk_lo <= qv_hi + off + wr) && (wl < 0 || wk_hi >= q0 + off - wl);
+  };
+  auto full_step = [&](int q0) __attribute__((always_inline)) -> bool {
+    return q0 + BQ - 1 < sq && wk_lo + 31 < sk && (wr < 0 || wk_lo + 31 <= q0 + off + wr) &&
+           (wl < 0 || wk_lo >= q0 + BQ - 1 + off - wl);
+  };
+  // A = rows of a 32-query block of an LDS tile, B = the lane's K or V row
+  // fragments: S (or dP) of the block, operand reads one MFMA ahead.
+  auto rows_product = [&](const char* tile, const u32x4 (&bf)[DS]) __attribute__((always_inline)) -> f32x16 {
+    f32x16 acc = f32x16{};
+    u32x4 cur = *reinterpret_cast<const u32x4*>(tile + oo.row_off[0]);
+#pragma unroll
+    for (int t = 0; t < DS; ++t) {
+      u32x4 nxt = cur;
+      if (t + 1 < DS) nxt = *reinterpret_cast<const u32x4*>(tile + oo.row_off[t + 1]);
+      acc = Ty::mfma(cur, bf[t], acc);
+      cur = nxt;
+    }
+    return acc;
+  };
+  // acc^T += tile^T B over the block's two 16-query slices (A read transposed),
+  // operands one MFMA ahead; B = the packed 16-bit P or dS of the block.
+  auto tr_product = [&](const char* tile, int qb, const uint32_t (&pk)[8], f32x16 (&acc)[DT])
+                        __attribute__((always_inline)) {
+    constexpr int NOP = 2 * DT;
+    u32x4 cur = tr_operand<D>(tile, oo, 2 * qb, 0);
+#pragma unroll
+    for (int i = 0; i < NOP; ++i) {
+      const int k2 = i / DT, dt = i % DT;
+      u32x4 nxt = cur;
+      if (i + 1 < NOP) nxt = tr_operand<D>(tile, oo, 2 * qb + (i + 1) / DT, (i + 1) % DT);
+      const u32x4 bop = {pk[4 * k2 + 0], pk[4 * k2 + 1], pk[4 * k2 + 2], pk[4 * k2 + 3]};
+      acc[dt] = Ty::mfma(cur, bop, acc[dt]);
+      cur = nxt;
+    }
+  };
+
+  f32x16 acc[DT];  // dV^T (P waves) or dK^T (dS waves)
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
+
+  if (n > 0) {
+    {
+      const int h = kvh * G, q0 = qblk_lo * BQ;
+      issue_rows(h, q0);
+      issue(h, q0, lds_q0, lds_g0);
+      stage_rows(0);
+      barrier_vmem_le<0>();
+    }
+    if (p_wave) {
+      u32x4 kf[DS];
+#pragma unroll
+      for (int t = 0; t < DS; ++t)
+        kf[t] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.k) + b * p.k_batch +
+                                                (int64_t)(sr.k_start + keyc) * p.k_row + kvh * p.k_head +
+                                                16 * t + 8 * hl);
+      int h = kvh * G, q0 = qblk_lo * BQ;
+      // Step r computes on stage ST = r % 3 and fills stage (r + 1) % 3.
+      auto step = [&](auto stc, int r) __attribute__((always_inline)) {
+        constexpr int ST = decltype(stc)::value;
+        constexpr int FILL = (ST + 1) % 3;
+        int h1 = h, q1 = q0;
+        advance(h1, q1);
+        if (r + 1 < n) {
+          issue_rows(h1, q1);
+          issue(h1, q1, qbuf(std::integral_constant<int, FILL>{}), gbuf(std::integral_constant<int, FILL>{}));
+        }
+        if (r < n && sees(q0)) {
+          const char* q_cur = qbuf(stc);
+          const char* g_cur = gbuf(stc);
+          float slope = 0.0f;
+          if constexpr (ALIBI) slope = p.alibi[b * p.alibi_bstride + h] * p.alibi_inv_scale;
+          const bool full = full_step(q0);
+          // S of every 32-query block first, then each block's P, hand-over and dV.
+          f32x16 sb[QB];
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) sb[qb] = rows_product(q_cur + qb * 32 * ROWB, kf);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            const f32x16& s = sb[qb];
+            uint32_t pp[8];
+            [[maybe_unused]] uint32_t pg[8];
+            auto elementwise = [&](auto masked_c) __attribute__((always_inline)) {
+              constexpr bool MASKED = decltype(masked_c)::value;
+#pragma unroll
+              for (int g4 = 0; g4 < 4; ++g4) {
+                const int qo = 32 * qb + 8 * g4 + 4 * hl;
+                const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lds_lse[ST][qo]);
+                float pv[4], gv[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  const int q = q0 + qo + i;
+                  float x = s[4 * g4 + i];
+                  float gcap = 1.0f;
+                  if constexpr (SOFTCAP) {
+                    x = transform_score<true>(x, p.softcap_pre, p.softcap);
+                    const float th = x * icap;
+                    gcap = fmaf(-th, th, 1.0f);
+                  }
+                  if constexpr (ALIBI) x = fmaf(-slope, fabsf((float)(q + off - key)), x);
+                  if constexpr (MASKED) {
+                    const bool vis = (q < sq) & (key < sk) & ((wr < 0) | (key <= q + off + wr)) &
+                                     ((wl < 0) | (key >= q + off - wl));
+                    x = vis ? x : -INFINITY;
+                  }
+                  pv[i] = fast_exp2(fmaf(x, c2, -l4[i]));
+                  gv[i] = pv[i] * gcap;
+                }
+                pp[2 * g4] = Ty::pack(pv[0], pv[1]);
+                pp[2 * g4 + 1] = Ty::pack(pv[2], pv[3]);
+                if constexpr (SOFTCAP) {
+                  pg[2 * g4] = Ty::pack(gv[0], gv[1]);
+                  pg[2 * g4 + 1] = Ty::pack(gv[2], gv[3]);
+                }
+              }
+            };
+            if (full) elementwise(std::false_type{});
+            else elementwise(std::true_type{});
+            if constexpr (SOFTCAP) {
+              lds_p[r & 1][pair][qb][0][lane] = u32x4{pg[0], pg[1], pg[2], pg[3]};
+              lds_p[r & 1][pair][qb][1][lane] = u32x4{pg[4], pg[5], pg[6], pg[7]};
+            } else {
+              lds_p[r & 1][pair][qb][0][lane] = u32x4{pp[0], pp[1], pp[2], pp[3]};
+              lds_p[r & 1][pair][qb][1][lane] = u32x4{pp[4], pp[5], pp[6], pp[7]};
+            }
+            tr_product(g_cur, qb, pp, acc);
+          }
+        }
+        if (r + 1 < n) stage_rows(FILL);
+        barrier_vmem_le<0>();
+        h = h1;
+        q0 = q1;
+      };
+      int r = 0;
+      for (; r + 3 <= n + 1; r += 3) {
+        step(std::integral_constant<int, 0>{}, r);
+        step(std::integral_constant<int, 1>{}, r + 1);
+        step(std::integral_constant<int, 2>{}, r + 2);
+      }
+      if (r < n + 1) step(std::integral_constant<int, 0>{}, r);
+      if (r + 1 < n + 1) step(std::integral_constant<int, 1>{}, r + 1);
+    } else {
+      u32x4 vf[DS];
+#pragma unroll
+      for (int t = 0; t < DS; ++t)
+        vf[t] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.v) + b * p.v_batch +
+                                                (int64_t)(sr.k_start + keyc) * p.v_row + kvh * p.v_head +
+                                                16 * t + 8 * hl);
+      int h = kvh * G, q0 = qblk_lo * BQ;  // position of step r
+      int qp = q0;                          // position of step r - 1 (the one computed)
+      auto step = [&](auto stc, int r) __attribute__((always_inline)) {
+        constexpr int ST = decltype(stc)::value;
+        constexpr int FILL = (ST + 1) % 3;
+        constexpr int PREV = (ST + 2) % 3;
+        int h1 = h, q1 = q0;
+        advance(h1, q1);
+        if (r + 1 < n) issue(h1, q1, qbuf(std::integral_constant<int, FILL>{}), gbuf(std::integral_constant<int, FILL>{}));
+        if (r >= 1 && sees(qp)) {
+          const char* q_prev = qbuf(std::integral_constant<int, PREV>{});
+          const char* g_prev = gbuf(std::integral_constant<int, PREV>{});
+          // dP of every 32-query block first, then each block's dS and dK.
+          f32x16 db[QB];
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) db[qb] = rows_product(g_prev + qb * 32 * ROWB, vf);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            const f32x16& dp = db[qb];
+            const u32x4 h0 = lds_p[(r - 1) & 1][pair][qb][0][lane];
+            const u32x4 h1v = lds_p[(r - 1) & 1][pair][qb][1][lane];
+            const uint32_t ph[8] = {h0[0], h0[1], h0[2], h0[3], h1v[0], h1v[1], h1v[2], h1v[3]};
+            uint32_t ps[8];
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+              const int qo = 32 * qb + 8 * g4 + 4 * hl;
+              const f32x4 d4 = *reinterpret_cast<const f32x4*>(&lds_dd[PREV][qo]);
+              const f32x2 pa = unpack2<Ty>(ph[2 * g4]);
+              const f32x2 pb = unpack2<Ty>(ph[2 * g4 + 1]);
+              ps[2 * g4] = Ty::pack(pa[0] * (dp[4 * g4 + 0] - d4[0]), pa[1] * (dp[4 * g4 + 1] - d4[1]));
+              ps[2 * g4 + 1] = Ty::pack(pb[0] * (dp[4 * g4 + 2] - d4[2]), pb[1] * (dp[4 * g4 + 3] - d4[3]));
+            }
+            tr_product(q_prev, qb, ps, acc);
+          }
+        }
+        barrier_vmem_le<0>();
+        qp = q0;
+        h = h1;
+        q0 = q1;
+      };
+      int r = 0;
+      for (; r + 3 <= n + 1; r += 3) {
+        step(std::integral_constant<int, 0>{}, r);
+        step(std::integral_constant<int, 1>{}, r + 1);
+        step(std::integral_constant<int, 2>{}, r + 2);
+      }
+      if (r < n + 1) step(std::integral_constant<int, 0>{}, r);
+      if (r + 1 < n + 1) step(std::integral_constant<int, 1>{}, r + 1);
+    }
+  }
+
+  // dV (P waves) and dK (dS waves) leave through the idle Q / dO stage
+  // buffers when eight 32-row blocks fit them (the last step's barrier has
+  // retired every read of them).
+  uint16_t* dst0;
+  float mul;
+  if (p_wave) {
+    dst0 = reinterpret_cast<uint16_t*>(p.dv) + b * p.dv_batch + (int64_t)(sr.k_start + wk_lo) * p.dv_row +
+           kvh * p.dv_head;
+    mul = 1.0f;
+  } else {
+    dst0 = reinterpret_cast<uint16_t*>(p.dk) + b * p.dk_batch + (int64_t)(sr.k_start + wk_lo) * p.dk_row +
+           kvh * p.dk_head;
+    mul = p.scale;
+  }
+  const int64_t drow = p_wave ? p.dv_row : p.dk_row;
+  constexpr int REGB = 32 * ROWB;
+  constexpr int RPBUF = TILEB / REGB;  // 32-row blocks per stage buffer
+  if constexpr (6 * RPBUF >= NW) {
+    if (n > 0 && rows_aligned16(p.dk, p.dk_batch, p.dk_row, p.dk_head) &&
+        rows_aligned16(p.dv, p.dv_batch, p.dv_row, p.dv_head)) {
+      const int bi = wave / RPBUF;
+      char* base = bi == 0 ? lds_q0 : bi == 1 ? lds_q1 : bi == 2 ? lds_q2 : bi == 3 ? lds_g0 : bi == 4 ? lds_g1 : lds_g2;
+      store_rows_staged<Ty, D>(base + (wave % RPBUF) * REGB, acc, mul, lane, [&](int rr) -> uint16_t* {
+        return wk_lo + rr < sk ? dst0 + (int64_t)rr * drow : nullptr;
+      });
+      return;
+    }
+  }
+  if (key_valid) store_rows<Ty, D>(dst0 + (int64_t)l32 * drow, acc, mul, hl);
+}
+
 // ---------------------------------------------------------------- dQ
 // NW waves of 32 queries, WPE waves per SIMD (2; 1 at D = 256, where the Q
 // and dO fragments and the dQ accumulators alone take 256 registers).
@@ -839,7 +1199,8 @@ bwd_dq_kernel(const BwdKernelParams p) {
 
 // Kernel-shape overrides of the debug build (attn_debug_set_variants; the
 // release library compiles none of them): 1 = dK/dV in two passes at 8
-// waves; 2 / 3 = dQ with 8 / 4 waves (256 / 128 queries per workgroup).
+// waves; 2 / 3 = dQ with 8 / 4 waves (256 / 128 queries per workgroup);
+// 4 = dK/dV in one pass at one wave per SIMD (4 waves).
 
 // D first (both gradient kernels read it), then dK/dV, then dQ; a kernel
 // whose grid would be empty (no queries, or no keys) is not launched.
@@ -864,17 +1225,24 @@ hipError_t launch_bwd_t(const BwdKernelParams& p, hipStream_t stream) {
     }
   } else {
     if (p.seqlen_k > 0) {
-      bool two_pass = false;
+      // Default: the paired kernel (eight waves, two per SIMD; 128 keys per
+      // workgroup).  Debug overrides: 1 = two passes at eight waves (256 keys),
+      // 4 = one pass at one wave per SIMD (four waves, 128 keys).
+      bool launched = false;
       if constexpr (kDebugBuild) {
         if (bwd_variant() == 1) {
           const dim3 grid((unsigned)((p.seqlen_k + 255) / 256), p.heads_kv, p.batch);
           hipLaunchKernelGGL((bwd_dkdv_kernel<Ty, D, SOFTCAP, ALIBI, 8, 2, 2>), grid, dim3(512), 0, stream, p);
-          two_pass = true;
+          launched = true;
+        } else if (bwd_variant() == 4) {
+          const dim3 grid((unsigned)((p.seqlen_k + 127) / 128), p.heads_kv, p.batch);
+          hipLaunchKernelGGL((bwd_dkdv_kernel<Ty, D, SOFTCAP, ALIBI, 4, 1, 1>), grid, dim3(256), 0, stream, p);
+          launched = true;
         }
       }
-      if (!two_pass) {
+      if (!launched) {
         const dim3 grid((unsigned)((p.seqlen_k + 127) / 128), p.heads_kv, p.batch);
-        hipLaunchKernelGGL((bwd_dkdv_kernel<Ty, D, SOFTCAP, ALIBI, 4, 1, 1>), grid, dim3(256), 0, stream, p);
+        hipLaunchKernelGGL((bwd_dkdv_pair_kernel<Ty, D, SOFTCAP, ALIBI>), grid, dim3(512), 0, stream, p);
       }
     }
     if (p.seqlen_q > 0) {

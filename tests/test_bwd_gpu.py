@@ -76,7 +76,7 @@ DENSE = [
     (86, 1, 300, 100, 2, 2, 128, "bf16", dict(causal=True)),          # rows with no key
     (87, 1, 64, 64, 2, 1, 128, "fp16", dict(causal=False, window=(0, 0))),
     (88, 2, 97, 161, 6, 3, 64, "bf16", dict(causal=False, softcap=5.0, alibi=True)),
-    # head_dim 256 (two-pass dK/dV and dQ at one wave per SIMD)
+    # head_dim 256 (two-pass dK/dV and dQ at one wave per SIMD; 64 and 128 use the paired dK/dV kernel)
     (181, 1, 257, 257, 4, 2, 256, "fp16", dict(causal=True)),
     (182, 2, 190, 300, 4, 1, 256, "bf16", dict(causal=False, softcap=20.0, alibi=True)),
     (183, 1, 300, 200, 2, 2, 256, "fp16", dict(causal=True, window=(64, 0))),   # rows with no key
@@ -216,10 +216,10 @@ def test_bwd_finite_2k(dtype):
         assert torch.isfinite(g).all()
 
 
-@pytest.mark.parametrize("variant", ["1", "2", "3"])
+@pytest.mark.parametrize("variant", ["1", "2", "3", "4"])
 def test_bwd_variants(variant, request):
-    """The selectable kernel shapes (two-pass dK/dV; dQ with 256 / 128 queries per workgroup) on a
-    ragged GQA causal case with a window and softcap."""
+    """The debug build's kernel shapes (two-pass dK/dV; dQ with 256 / 128 queries per workgroup;
+    one-pass dK/dV at one wave per SIMD) on a ragged GQA causal case with a window and softcap."""
     force_variants(request, bwd=int(variant))
     print(f"[case] bwd variant {variant}", flush=True)
     eng = _eng()
