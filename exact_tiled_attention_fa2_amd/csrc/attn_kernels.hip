@@ -861,11 +861,14 @@ __global__ void __launch_bounds__(256) combine_kernel(const CombineParams p) {
   if (lane == 0 && p.lse != nullptr) p.lse[r] = lse;
 }
 
-// Columns per longest-first group: as many as keep ~8 MB of K/V live per XCD.
+// Columns per longest-first group: as many as keep their K/V within an XCD's
+// 4 MB L2, but at least two.  (With one column per group, all 32 CUs of an XCD
+// read the same lines: at D = 256, where a column's K/V alone is 4 MB, that
+// ran 1% slower than two columns, although it fetched 22% fewer HBM bytes.)
 int col_group_for(const FwdKernelParams& p, int heads_grid, int nz, int head_dim) {
   const int64_t kv_bytes = 2 * (int64_t)std::max(p.seqlen_k, 1) * head_dim * 2 / p.num_splits;
   const int per_xcd = std::max(1, heads_grid * nz / 8);
-  return (int)std::min<int64_t>(per_xcd, std::max<int64_t>(1, (int64_t(8) << 20) / kv_bytes));
+  return (int)std::min<int64_t>(per_xcd, std::max<int64_t>(2, (int64_t(4) << 20) / kv_bytes));
 }
 
 template <class Ty, int D, int BK, int NW, int QG, bool SOFTCAP, int LEAD, int WPE, int NSTAGE = 2,

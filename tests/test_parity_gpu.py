@@ -461,6 +461,29 @@ def test_d256_256row_tile_small(case, request):
     gate_check(np64(o), ro, np64(lse), rl, dtype, f"d256-256row {seed}")
 
 
+# ------------------------------------------------------------------ O stored from the accumulator layout (variant 6)
+
+def test_direct_store_variant_full(request):
+    """The 256-row D = 128 tile that stores O straight from the accumulator layout (8-byte stores,
+    no LDS staging; debug override 6) on the full causal workload: whole output, NaN-prefilled."""
+    force_variants(request, fwd=6)
+    _whole_dense("cfg2_bf16_causal_2k")
+
+
+@pytest.mark.parametrize("case", [(110, 2, 333, 333, 8, 2, 128, "bf16", dict(causal=True)),
+                                  (111, 1, 130, 517, 4, 4, 128, "fp16", dict(causal=False, softcap=30.0)),
+                                  (112, 1, 300, 200, 4, 1, 128, "bf16", dict(causal=True, window=(100, 0)))],
+                         ids=["s110", "s111", "s112"])
+def test_direct_store_variant_small(case, request):
+    """The same tile on small ragged grids: GQA causal, softcap with Sq < Sk, a window with
+    Sq > Sk (rows with no key)."""
+    force_variants(request, fwd=6)
+    seed, b, sq, sk, hq, hkv, d, dtype, kw = case
+    print(f"[case] direct-store seed={seed} b={b} sq={sq} sk={sk} hq={hq} hkv={hkv} d={d} {dtype} {kw}", flush=True)
+    o, lse, ro, rl = _dense_case(seed, b, sq, sk, hq, hkv, d, dtype, **kw)
+    gate_check(np64(o), ro, np64(lse), rl, dtype, f"direct-store {seed}")
+
+
 # ------------------------------------------------------------------ four copy stages (D = 128)
 
 @pytest.mark.parametrize("case", [(99, 2, 333, 333, 8, 2, 128, "bf16", dict(causal=True)),
