@@ -14,8 +14,7 @@
 // Three kernels, in stream order, no atomics (every output element has one
 // owner, so the result is deterministic):
 //  * bwd_dot_kernel: D = rowsum(dO * O) in fp32 (HBM-bound, one pass).
-//  * bwd_dkdv_pair_kernel (head_dim 64 / 128; bwd_dkdv_kernel in two walks at
-//    256): one workgroup per 128-key tile of one KV head.  32 keys belong to
+//  * bwd_dkdv_pair_kernel: one workgroup per 128-key tile of one KV head.  32 keys belong to
 //    a pair of waves on one SIMD that walks the query tiles of every query
 //    head of its GQA group: S = Q K^T and dP = dO V^T (A = Q / dO rows read
 //    from LDS, B = the keys' K / V rows held in VGPRs), the elementwise P and
@@ -169,7 +168,11 @@ struct TileCopier {
 
 // Per-lane LDS byte offsets of the MFMA operands in the swizzled layout:
 // row reads (A operand of a 32-row slice, 8 consecutive dims per lane) and
-// transposing reads (A operand that contracts over 16 rows).
+// transposing reads (A operand that contracts over 16 rows).  The swizzle
+// changes only the low 4 bits of a chunk index, so with more than 16 chunks
+// per row (D = 256) chunks 16.. sit at the offsets of chunks 0.. plus 256
+// bytes: only the first 16 chunks' offsets are kept in registers (the rest
+// become immediate offsets of the reads).
 template <int D>
 struct OperandOffsets {
   static constexpr int CH = D / 8;
@@ -177,22 +180,26 @@ struct OperandOffsets {
   static constexpr int DS = D / 16;
   static constexpr int DT = D / 32;
   static constexpr int SWZ_MASK = CH < 16 ? CH - 1 : 15;
-  int row_off[DS];
-  int tr_off[2][DT];
+  static constexpr int NRO = CH > 16 ? 8 : DS;  // distinct row-read offsets (a k-step covers 2 chunks)
+  static constexpr int NTO = CH > 16 ? 4 : DT;  // distinct transposing-read offsets (4 chunks per 32 dims)
+  int row_off_[NRO];
+  int tr_off_[2][NTO];
   __device__ __forceinline__ void init(int lane) {
     const int l32 = lane & 31, hl = lane >> 5;
     const int sw = chunk_swizzle(lane & 15) & SWZ_MASK;
 #pragma unroll
-    for (int t = 0; t < DS; ++t) row_off[t] = l32 * ROWB + (((2 * t + hl) ^ sw) << 4);
+    for (int t = 0; t < NRO; ++t) row_off_[t] = l32 * ROWB + (((2 * t + hl) ^ sw) << 4);
     const int cl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
 #pragma unroll
     for (int r2 = 0; r2 < 2; ++r2) {
       const int vrow = 4 * hl + 8 * r2 + ((lane & 15) >> 2);
       const int x = cl ^ (chunk_swizzle(vrow) & SWZ_MASK);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) tr_off[r2][dt] = vrow * ROWB + (((4 * dt) ^ x) << 4) + ((lane & 1) << 3);
+      for (int dt = 0; dt < NTO; ++dt) tr_off_[r2][dt] = vrow * ROWB + (((4 * dt) ^ x) << 4) + ((lane & 1) << 3);
     }
   }
+  __device__ __forceinline__ int row_off(int t) const { return row_off_[t % NRO] + (t / NRO) * 256; }
+  __device__ __forceinline__ int tr_off(int r2, int dt) const { return tr_off_[r2][dt % NTO] + (dt / NTO) * 256; }
 };
 
 // A operand for the contraction over the 16 rows of slice ks of a tile,
@@ -200,8 +207,8 @@ struct OperandOffsets {
 template <int D>
 __device__ __forceinline__ u32x4 tr_operand(const char* tile, const OperandOffsets<D>& o, int ks, int dt) {
   constexpr int ROWB = D * 2;
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + ks * 16 * ROWB + o.tr_off[0][dt]));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + ks * 16 * ROWB + o.tr_off[1][dt]));
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + ks * 16 * ROWB + o.tr_off(0, dt)));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + ks * 16 * ROWB + o.tr_off(1, dt)));
   const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
   const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
   return u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
@@ -447,8 +454,8 @@ bwd_dkdv_kernel(const BwdKernelParams p) {
           u32x4 aq[RB], ag[RB];
 #pragma unroll
           for (int t = 0; t < RB; ++t) {
-            aq[t] = *reinterpret_cast<const u32x4*>(q_cur + qb * 32 * ROWB + oo.row_off[t0 + t]);
-            if constexpr (DO_DK) ag[t] = *reinterpret_cast<const u32x4*>(g_cur + qb * 32 * ROWB + oo.row_off[t0 + t]);
+            aq[t] = *reinterpret_cast<const u32x4*>(q_cur + qb * 32 * ROWB + oo.row_off(t0 + t));
+            if constexpr (DO_DK) ag[t] = *reinterpret_cast<const u32x4*>(g_cur + qb * 32 * ROWB + oo.row_off(t0 + t));
           }
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -759,11 +766,11 @@ bwd_dkdv_pair_kernel(const BwdKernelParams p) {
   // fragments: S (or dP) of the block, operand reads one MFMA ahead.
   auto rows_product = [&](const char* tile, const u32x4 (&bf)[DS]) __attribute__((always_inline)) -> f32x16 {
     f32x16 acc = f32x16{};
-    u32x4 cur = *reinterpret_cast<const u32x4*>(tile + oo.row_off[0]);
+    u32x4 cur = *reinterpret_cast<const u32x4*>(tile + oo.row_off(0));
 #pragma unroll
     for (int t = 0; t < DS; ++t) {
       u32x4 nxt = cur;
-      if (t + 1 < DS) nxt = *reinterpret_cast<const u32x4*>(tile + oo.row_off[t + 1]);
+      if (t + 1 < DS) nxt = *reinterpret_cast<const u32x4*>(tile + oo.row_off(t + 1));
       acc = Ty::mfma(cur, bf[t], acc);
       cur = nxt;
     }
@@ -1094,9 +1101,9 @@ bwd_dq_kernel(const BwdKernelParams p) {
       for (int t = 0; t < DS; ++t) {
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(k_cur + kt * 32 * ROWB + oo.row_off[t]);
+          const u32x4 a = *reinterpret_cast<const u32x4*>(k_cur + kt * 32 * ROWB + oo.row_off(t));
           s[kt] = Ty::mfma(a, qf[t], s[kt]);
-          const u32x4 a2 = *reinterpret_cast<const u32x4*>(v_cur + kt * 32 * ROWB + oo.row_off[t]);
+          const u32x4 a2 = *reinterpret_cast<const u32x4*>(v_cur + kt * 32 * ROWB + oo.row_off(t));
           dp[kt] = Ty::mfma(a2, gf[t], dp[kt]);
         }
       }
@@ -1199,8 +1206,9 @@ bwd_dq_kernel(const BwdKernelParams p) {
 
 // Kernel-shape overrides of the debug build (attn_debug_set_variants; the
 // release library compiles none of them): 1 = dK/dV in two passes at 8
-// waves; 2 / 3 = dQ with 8 / 4 waves (256 / 128 queries per workgroup);
-// 4 = dK/dV in one pass at one wave per SIMD (4 waves).
+// waves (head_dim 64 / 128); 2 / 3 = dQ with 8 / 4 waves (256 / 128 queries
+// per workgroup); 4 = dK/dV at one wave per SIMD (4 waves: one pass at head_dim
+// 64 / 128, two walks at 256).
 
 // D first (both gradient kernels read it), then dK/dV, then dQ; a kernel
 // whose grid would be empty (no queries, or no keys) is not launched.
@@ -1213,11 +1221,22 @@ hipError_t launch_bwd_t(const BwdKernelParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((bwd_dot_kernel<Ty, D>), grid, dim3(256), 0, stream, p);
   }
   if constexpr (D > 128) {
-    // D = 256: dK/dV in two walks (dV, then dK) at one wave per SIMD, and dQ at
-    // one wave per SIMD -- the register file of two waves per SIMD is too small.
+    // D = 256: the paired dK/dV kernel with 32-query steps (each wave's one
+    // gradient and one K / V row set fill its 256 registers; a few values
+    // spill to scratch, still 29% faster than two walks at one wave per SIMD,
+    // which debug override 4 selects), and dQ at one wave per SIMD -- the Q and
+    // dO rows and the dQ accumulators alone take 256 registers.
     if (p.seqlen_k > 0) {
       const dim3 grid((unsigned)((p.seqlen_k + 127) / 128), p.heads_kv, p.batch);
-      hipLaunchKernelGGL((bwd_dkdv_kernel<Ty, D, SOFTCAP, ALIBI, 4, 1, 2>), grid, dim3(256), 0, stream, p);
+      bool launched = false;
+      if constexpr (kDebugBuild) {
+        if (bwd_variant() == 4) {
+          hipLaunchKernelGGL((bwd_dkdv_kernel<Ty, D, SOFTCAP, ALIBI, 4, 1, 2>), grid, dim3(256), 0, stream, p);
+          launched = true;
+        }
+      }
+      if (!launched)
+        hipLaunchKernelGGL((bwd_dkdv_pair_kernel<Ty, D, SOFTCAP, ALIBI>), grid, dim3(512), 0, stream, p);
     }
     if (p.seqlen_q > 0) {
       const dim3 grid((unsigned)((p.seqlen_q + 127) / 128), p.heads_q, p.batch);

@@ -76,7 +76,7 @@ DENSE = [
     (86, 1, 300, 100, 2, 2, 128, "bf16", dict(causal=True)),          # rows with no key
     (87, 1, 64, 64, 2, 1, 128, "fp16", dict(causal=False, window=(0, 0))),
     (88, 2, 97, 161, 6, 3, 64, "bf16", dict(causal=False, softcap=5.0, alibi=True)),
-    # head_dim 256 (two-pass dK/dV and dQ at one wave per SIMD; 64 and 128 use the paired dK/dV kernel)
+    # head_dim 256 (32-query steps in the paired dK/dV kernel; dQ at one wave per SIMD)
     (181, 1, 257, 257, 4, 2, 256, "fp16", dict(causal=True)),
     (182, 2, 190, 300, 4, 1, 256, "bf16", dict(causal=False, softcap=20.0, alibi=True)),
     (183, 1, 300, 200, 2, 2, 256, "fp16", dict(causal=True, window=(64, 0))),   # rows with no key
@@ -233,6 +233,31 @@ def test_bwd_variants(variant, request):
     grad_check(np64(dq), rq, "bf16", f"variant {variant} dQ")
     grad_check(np64(dk), rk, "bf16", f"variant {variant} dK")
     grad_check(np64(dv), rv, "bf16", f"variant {variant} dV")
+
+
+D256 = [c for c in DENSE if c[6] == 256]
+
+
+@pytest.mark.parametrize("case", D256, ids=[f"s{c[0]}" for c in D256])
+def test_bwd_d256_two_walk_variant(case, request):
+    """dK/dV in two walks at one wave per SIMD (debug override 4 at head_dim 256: dV from S and P,
+    then dK from S, dP and dS) on the D = 256 cases."""
+    force_variants(request, bwd=4)
+    seed, b, sq, sk, hq, hkv, d, dtype, kw = case
+    kw = dict(kw)
+    print(f"[case] bwd d256 two-walk seed={seed} b={b} sq={sq} sk={sk} hq={hq} hkv={hkv} {dtype} {kw}", flush=True)
+    if kw.pop("alibi", False):
+        kw["alibi_slopes"] = W.alibi_slopes(hq, b, device="cuda")
+    eng = _eng()
+    q, k, v = W.make_dense(seed, b, sq, sk, hq, hkv, d, dtype, device="cuda")
+    do = _dout(seed, (b, sq, hq, d), dtype)
+    o, lse = eng.attn_fwd(q, k, v, **kw)
+    dq, dk, dv = eng.attn_bwd(q, k, v, o, lse, do, **kw)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.attention_bwd_ref(np64(q), np64(k), np64(v), np64(do), **_opts_np(kw))
+    grad_check(np64(dq), rq, dtype, f"two-walk d256 dQ {seed}")
+    grad_check(np64(dk), rk, dtype, f"two-walk d256 dK {seed}")
+    grad_check(np64(dv), rv, dtype, f"two-walk d256 dV {seed}")
 
 
 def test_bwd_headline_whole():
