@@ -231,6 +231,7 @@ fwd_tile_kernel(const FwdKernelParams p) {
   // [m0 + 32 (QG rb + g), +32).
   const int rb = wave < NW / 2 ? 2 * wave : NW - 1 - 2 * (wave - NW / 2);
   int row[QG], hq[QG], kmin[QG], kmax[QG], grow_lo[QG], grow_hi[QG];
+  uint32_t kspan[QG];
   bool q_valid[QG];
 #pragma unroll
   for (int g = 0; g < QG; ++g) {
@@ -241,9 +242,12 @@ fwd_tile_kernel(const FwdKernelParams p) {
     hq[g] = p.pack_gqa ? head * G + (q_valid[g] ? pq - row[g] * G : 0) : head;
     grow_lo[g] = gpq_lo / G;
     grow_hi[g] = min(packed - 1, gpq_lo + 31) / G;
-    // Key bounds visible to this lane's row (inclusive), including the valid length.
-    kmin[g] = (wl >= 0) ? row[g] + off - wl : -0x40000000;
+    // Key bounds visible to this lane's row (inclusive), including the valid
+    // length; keys are never negative, so the lower bound is at least 0 and
+    // both bounds and their difference stay within int range.
+    kmin[g] = (wl >= 0) ? max(row[g] + off - wl, 0) : 0;
     kmax[g] = min(sk - 1, (wr >= 0) ? row[g] + off + wr : 0x3fffffff);
+    kspan[g] = kmax[g] >= kmin[g] ? (uint32_t)(kmax[g] - kmin[g] + 1) : 0u;  // visible keys
   }
   // ALiBi slope of this lane's query head, in raw-score units.
   float slope[QG];
@@ -460,12 +464,18 @@ fwd_tile_kernel(const FwdKernelParams p) {
       const int full_lo = (wl >= 0) ? grow_hi[g] + off - wl : -0x40000000;
       const int full_hi = min(sk - 1, (wr >= 0) ? grow_lo[g] + off + wr : 0x3fffffff);
       if (!(j0 >= full_lo && j0 + BK - 1 <= full_hi)) {
+        // Visible iff key - kmin lies in [0, span) as one unsigned compare
+        // (span = 0 for a row that sees no key; a key below kmin wraps to
+        // at least 2^31 > span): one compare into VCC and one select per
+        // score, where two compares into scalar register pairs ran the
+        // kernel out of scalar registers.
+        const uint32_t base = (uint32_t)(j0 + 4 * hl - kmin[g]);
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
           for (int r2 = 0; r2 < 16; ++r2) {
-            const int key = j0 + 32 * kt + 8 * (r2 >> 2) + 4 * hl + (r2 & 3);
-            if (key < kmin[g] || key > kmax[g]) sc[g][kt][r2] = -INFINITY;
+            const uint32_t rel = base + (uint32_t)(32 * kt + 8 * (r2 >> 2) + (r2 & 3));
+            sc[g][kt][r2] = rel < kspan[g] ? sc[g][kt][r2] : -INFINITY;
           }
         }
       }
