@@ -720,6 +720,11 @@ bwd_dkdv_pair_kernel(const BwdKernelParams p) {
 
   const float c2 = p.scale_log2;
   const float icap = p.inv_softcap;
+  // Queries that see this lane's key: [qlo, qlo + qspan) (empty for a key past
+  // the valid length), so a score is masked by one unsigned compare.
+  const int qlo = (wr >= 0) ? max(0, key - off - wr) : 0;
+  const int qhi = min(sq - 1, (wl >= 0) ? key - off + wl : 0x3fffffff);
+  const uint32_t qspan = (key_valid && qhi >= qlo) ? (uint32_t)(qhi - qlo + 1) : 0u;
 
   auto advance = [&](int& h, int& q0) __attribute__((always_inline)) {
     q0 += BQ;
@@ -856,11 +861,7 @@ bwd_dkdv_pair_kernel(const BwdKernelParams p) {
                     gcap = fmaf(-th, th, 1.0f);
                   }
                   if constexpr (ALIBI) x = fmaf(-slope, fabsf((float)(q + off - key)), x);
-                  if constexpr (MASKED) {
-                    const bool vis = (q < sq) & (key < sk) & ((wr < 0) | (key <= q + off + wr)) &
-                                     ((wl < 0) | (key >= q + off - wl));
-                    x = vis ? x : -INFINITY;
-                  }
+                  if constexpr (MASKED) x = (uint32_t)(q - qlo) < qspan ? x : -INFINITY;
                   pv[i] = fast_exp2(fmaf(x, c2, -l4[i]));
                   gv[i] = pv[i] * gcap;
                 }
