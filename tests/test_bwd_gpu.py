@@ -121,6 +121,30 @@ def test_bwd_varlen():
     grad_check(np64(dv), rv, "bf16", "varlen dV")
 
 
+@pytest.mark.parametrize("case", [(185, 64, "fp16", dict(causal=True, window=(48, 0), softcap=10.0)),
+                                  (186, 128, "bf16", dict(causal=False, window=(80, 40)))],
+                         ids=["s185", "s186"])
+def test_bwd_varlen_alibi(case):
+    """Packed sequences (one of length 1, one empty) with per-sequence ALiBi slopes [B, Hq], GQA,
+    and a window (with softcap, or non-causal with both bounds)."""
+    seed, d, dtype, kw = case
+    print(f"[case] bwd varlen alibi seed={seed} d={d} {dtype} {kw}", flush=True)
+    eng = _eng()
+    lens = [90, 1, 0, 211, 47]
+    q, k, v, cu, lens = W.make_varlen(seed, len(lens), 1, 1, 8, 2, d, dtype, device="cuda", lengths=lens)
+    sl = W.alibi_slopes(8, len(lens), device="cuda")
+    do = _dout(seed, tuple(q.shape), dtype)
+    o, lse = eng.attn_fwd_varlen(q, k, v, cu, cu, max(lens), max(lens), alibi_slopes=sl, **kw)
+    dq, dk, dv = eng.attn_bwd_varlen(q, k, v, o, lse, do, cu, cu, max(lens), max(lens), alibi_slopes=sl, **kw)
+    torch.cuda.synchronize()
+    cu_np = cu.cpu().numpy()
+    rq, rk, rv = oracle.attention_bwd_varlen_ref(np64(q), np64(k), np64(v), np64(do), cu_np, cu_np,
+                                                 alibi_slopes=np64(sl), **kw)
+    grad_check(np64(dq), rq, dtype, f"varlen alibi {seed} dQ")
+    grad_check(np64(dk), rk, dtype, f"varlen alibi {seed} dK")
+    grad_check(np64(dv), rv, dtype, f"varlen alibi {seed} dV")
+
+
 def test_bwd_varlen_d256():
     """Packed sequences at head_dim 256 (one of length 1, one empty), GQA, causal, fp16."""
     print("[case] bwd varlen d256", flush=True)
