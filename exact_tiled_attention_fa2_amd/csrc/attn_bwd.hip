@@ -906,7 +906,43 @@ bwd_dkdv_pair_kernel(const BwdKernelParams p) {
                                                 (int64_t)(sr.k_start + keyc) * p.v_row + kvh * p.v_head +
                                                 16 * t + 8 * hl);
       int h = kvh * G, q0 = qblk_lo * BQ;  // position of step r
-      int qp = q0;                          // position of step r - 1 (the one computed)
+      int qp = q0;                          // position of step r - 1
+      f32x16 db[QB];                        // dP of the blocks of a step
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) db[qb] = f32x16{};
+      auto form_dp = [&](const char* g_tile) __attribute__((always_inline)) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) db[qb] = rows_product(g_tile + qb * 32 * ROWB, vf);
+      };
+      // dS = P (dP - D) of step r - 1 from db and the P the P wave handed over,
+      // then dK^T += Q^T dS.
+      auto finish = [&](int r, const char* q_prev, const float* dd_prev) __attribute__((always_inline)) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const f32x16& dp = db[qb];
+          const u32x4 h0 = lds_p[(r - 1) & 1][pair][qb][0][lane];
+          const u32x4 h1v = lds_p[(r - 1) & 1][pair][qb][1][lane];
+          const uint32_t ph[8] = {h0[0], h0[1], h0[2], h0[3], h1v[0], h1v[1], h1v[2], h1v[3]};
+          uint32_t ps[8];
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int qo = 32 * qb + 8 * g4 + 4 * hl;
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dd_prev[qo]);
+            const f32x2 pa = unpack2<Ty>(ph[2 * g4]);
+            const f32x2 pb = unpack2<Ty>(ph[2 * g4 + 1]);
+            ps[2 * g4] = Ty::pack(pa[0] * (dp[4 * g4 + 0] - d4[0]), pa[1] * (dp[4 * g4 + 1] - d4[1]));
+            ps[2 * g4 + 1] = Ty::pack(pb[0] * (dp[4 * g4 + 2] - d4[2]), pb[1] * (dp[4 * g4 + 3] - d4[3]));
+          }
+          tr_product(q_prev, qb, ps, acc);
+        }
+      };
+      // At head_dim 256 step r first finishes step r - 1 (its dP carried over
+      // the barrier) and then forms dP of step r, so its dS arithmetic runs
+      // under the P wave's S MFMAs and its dK MFMAs under the P wave's
+      // exponentials (+2%).  At 64 / 128 that order measured 1% slower, so
+      // there step r forms dP of step r - 1 and finishes it at once.
+      constexpr bool CARRY = D > 128;
+      bool carried = false;  // CARRY: db holds dP of step r - 1
       auto step = [&](auto stc, int r) __attribute__((always_inline)) {
         constexpr int ST = decltype(stc)::value;
         constexpr int FILL = (ST + 1) % 3;
@@ -914,30 +950,14 @@ bwd_dkdv_pair_kernel(const BwdKernelParams p) {
         int h1 = h, q1 = q0;
         advance(h1, q1);
         if (r + 1 < n) issue(h1, q1, qbuf(std::integral_constant<int, FILL>{}), gbuf(std::integral_constant<int, FILL>{}));
-        if (r >= 1 && sees(qp)) {
-          const char* q_prev = qbuf(std::integral_constant<int, PREV>{});
-          const char* g_prev = gbuf(std::integral_constant<int, PREV>{});
-          // dP of every 32-query block first, then each block's dS and dK.
-          f32x16 db[QB];
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) db[qb] = rows_product(g_prev + qb * 32 * ROWB, vf);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) {
-            const f32x16& dp = db[qb];
-            const u32x4 h0 = lds_p[(r - 1) & 1][pair][qb][0][lane];
-            const u32x4 h1v = lds_p[(r - 1) & 1][pair][qb][1][lane];
-            const uint32_t ph[8] = {h0[0], h0[1], h0[2], h0[3], h1v[0], h1v[1], h1v[2], h1v[3]};
-            uint32_t ps[8];
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-              const int qo = 32 * qb + 8 * g4 + 4 * hl;
-              const f32x4 d4 = *reinterpret_cast<const f32x4*>(&lds_dd[PREV][qo]);
-              const f32x2 pa = unpack2<Ty>(ph[2 * g4]);
-              const f32x2 pb = unpack2<Ty>(ph[2 * g4 + 1]);
-              ps[2 * g4] = Ty::pack(pa[0] * (dp[4 * g4 + 0] - d4[0]), pa[1] * (dp[4 * g4 + 1] - d4[1]));
-              ps[2 * g4 + 1] = Ty::pack(pb[0] * (dp[4 * g4 + 2] - d4[2]), pb[1] * (dp[4 * g4 + 3] - d4[3]));
-            }
-            tr_product(q_prev, qb, ps, acc);
+        if constexpr (CARRY) {
+          if (carried) finish(r, qbuf(std::integral_constant<int, PREV>{}), lds_dd[PREV]);
+          carried = r < n && sees(q0);
+          if (carried) form_dp(gbuf(stc));
+        } else {
+          if (r >= 1 && sees(qp)) {
+            form_dp(gbuf(std::integral_constant<int, PREV>{}));
+            finish(r, qbuf(std::integral_constant<int, PREV>{}), lds_dd[PREV]);
           }
         }
         barrier_vmem_le<0>();
