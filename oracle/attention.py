@@ -18,7 +18,7 @@ the whole score row materialised:
     O_i   = sum_{j allowed} exp(t_ij - LSE_i) * V_j
     a row with no allowed key: O_i = 0, LSE_i = -inf
 
-Readings where the pages are silent (each one is listed in the design doc):
+Readings where the pages are silent:
 
 * causal and window masks are aligned to the bottom-right corner,
   off = Sk - Sq; key j is allowed for query i iff
