@@ -50,6 +50,7 @@ def _draw(seed, head_dims):
 
 FWD_SEEDS = list(range(5000, 5036))
 BWD_SEEDS = list(range(6000, 6012))
+BWD_SEEDS_D256 = list(range(6100, 6106))
 
 
 @pytest.mark.parametrize("seed", FWD_SEEDS)
@@ -83,10 +84,12 @@ def _grad_check(got, ref, dtype, what):
     assert np.all(np.isfinite(got)) and rl <= rel_gate and cs >= cos_gate, f"{what}: {rl} {cs}"
 
 
-@pytest.mark.parametrize("seed", BWD_SEEDS)
+@pytest.mark.parametrize("seed", BWD_SEEDS + BWD_SEEDS_D256)
 def test_random_backward(seed, request):
-    c = _draw(seed, [64, 128])
-    bwd_variant = str(np.random.default_rng(seed + 1).choice(["0", "1", "2", "3"]))
+    c = _draw(seed, [256] if seed in BWD_SEEDS_D256 else [64, 128])
+    # head_dim 256 has one override (4: the two-walk dK/dV kernel); 64 / 128 have 1-3
+    choices = ["0", "4"] if c["d"] == 256 else ["0", "1", "2", "3"]
+    bwd_variant = str(np.random.default_rng(seed + 1).choice(choices))
     force_variants(request, bwd=int(bwd_variant))
     print(f"[case] random backward {c} bwd_variant={bwd_variant}", flush=True)
     kw = dict(c["kw"])
