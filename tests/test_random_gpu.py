@@ -109,3 +109,79 @@ def test_random_backward(seed, request):
     _grad_check(np64(dq), rq, c["dtype"], f"random dQ {seed}")
     _grad_check(np64(dk), rk, c["dtype"], f"random dK {seed}")
     _grad_check(np64(dv), rv, c["dtype"], f"random dV {seed}")
+
+
+# ------------------------------------------------------------------ packed variable-length problems
+
+def _draw_varlen(seed, head_dims):
+    """A random packed batch: 1-6 sequences whose query and key lengths are drawn separately
+    (0, 1, short or long; the first sequence has at least one query), and the options of _draw."""
+    rng = np.random.default_rng(seed)
+
+    def length():
+        u = rng.random()
+        return 0 if u < 0.1 else 1 if u < 0.2 else int(rng.integers(2, 100)) if u < 0.5 else int(rng.integers(100, 700))
+
+    n = int(rng.integers(1, 7))
+    lq = [length() for _ in range(n)]
+    lq[0] = max(lq[0], 1)
+    lk = [lq[i] if rng.random() < 0.5 else length() for i in range(n)]
+    base = _draw(seed, head_dims)
+    return dict(base, lq=lq, lk=lk)
+
+
+def _varlen_inputs(c):
+    cq = np.concatenate([[0], np.cumsum(c["lq"])]).astype(np.int32)
+    ck = np.concatenate([[0], np.cumsum(c["lk"])]).astype(np.int32)
+    gen = torch.Generator(device="cuda").manual_seed(c["seed"] + 31)
+    q = W.randn16((int(cq[-1]), c["hq"], c["d"]), c["dtype"], gen, device="cuda")
+    k = W.randn16((int(ck[-1]), c["hkv"], c["d"]), c["dtype"], gen, device="cuda")
+    v = W.randn16((int(ck[-1]), c["hkv"], c["d"]), c["dtype"], gen, device="cuda")
+    kw = dict(c["kw"])
+    if c["alibi"]:  # per-sequence slopes
+        kw["alibi_slopes"] = W.alibi_slopes(c["hq"], len(c["lq"]), device="cuda")
+    return q, k, v, torch.tensor(cq, device="cuda"), torch.tensor(ck, device="cuda"), cq, ck, kw
+
+
+def _np_kw(kw):
+    out = dict(kw)
+    if out.get("alibi_slopes") is not None:
+        out["alibi_slopes"] = np64(out["alibi_slopes"])
+    return out
+
+
+VARLEN_FWD_SEEDS = list(range(5100, 5114)) + [5118, 5119]  # the last four draw head_dim 128
+VARLEN_BWD_SEEDS = list(range(6200, 6206)) + [6206, 6208]  # the last two draw head_dim 128
+
+
+@pytest.mark.parametrize("seed", VARLEN_FWD_SEEDS)
+def test_random_varlen_forward(seed, request):
+    c = _draw_varlen(seed, [64, 128, 256])
+    force_variants(request, fwd=int(c["variant"]))
+    print(f"[case] random varlen forward {c}", flush=True)
+    q, k, v, cu_q, cu_k, cq, ck, kw = _varlen_inputs(c)
+    o, lse = _eng().attn_fwd_varlen(q, k, v, cu_q, cu_k, max(c["lq"]), max(max(c["lk"]), 1), **kw)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_varlen_ref(np64(q), np64(k), np64(v), cq, ck, **_np_kw(kw))
+    gate_check(np64(o), ro, np64(lse), rl, c["dtype"], f"random varlen forward {seed}")
+
+
+@pytest.mark.parametrize("seed", VARLEN_BWD_SEEDS)
+def test_random_varlen_backward(seed, request):
+    c = _draw_varlen(seed, [64, 128, 256])
+    print(f"[case] random varlen backward {c}", flush=True)
+    q, k, v, cu_q, cu_k, cq, ck, kw = _varlen_inputs(c)
+    eng = _eng()
+    mq, mk = max(c["lq"]), max(max(c["lk"]), 1)
+    gen = torch.Generator(device="cuda").manual_seed(seed + 7777)
+    do = W.randn16(tuple(q.shape), c["dtype"], gen, device="cuda")
+    o, lse = eng.attn_fwd_varlen(q, k, v, cu_q, cu_k, mq, mk, **kw)
+    dq, dk, dv = eng.attn_bwd_varlen(q, k, v, o, lse, do, cu_q, cu_k, mq, mk, **kw)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.attention_bwd_varlen_ref(np64(q), np64(k), np64(v), np64(do), cq, ck, **_np_kw(kw))
+    if k.shape[0] == 0:
+        assert dk.numel() == 0 and dv.numel() == 0
+    _grad_check(np64(dq), rq, c["dtype"], f"random varlen dQ {seed}")
+    if k.shape[0] > 0:
+        _grad_check(np64(dk), rk, c["dtype"], f"random varlen dK {seed}")
+        _grad_check(np64(dv), rv, c["dtype"], f"random varlen dV {seed}")
