@@ -185,3 +185,52 @@ def test_random_varlen_backward(seed, request):
     if k.shape[0] > 0:
         _grad_check(np64(dk), rk, c["dtype"], f"random varlen dK {seed}")
         _grad_check(np64(dv), rv, c["dtype"], f"random varlen dV {seed}")
+
+
+# ------------------------------------------------------------------ split-KV against a cache
+
+def _draw_kvcache(seed):
+    """A random decode or chunked-prefill problem against a cache: random valid lengths with NaN
+    past them, contiguous or paged (shuffled pages), a random split count (0 = the heuristic),
+    the options of _draw and a random decode tile override."""
+    rng = np.random.default_rng(seed)
+    d = int(rng.choice([64, 128, 256]))
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    g = int(rng.choice([1, 2, 4, 8]))
+    sq = int(rng.choice([1, 1, 1, int(rng.integers(2, 9)), int(rng.integers(16, 200))]))
+    kw = dict(causal=bool(rng.random() < 0.7))
+    if rng.random() < 0.3:
+        kw["window"] = (int(rng.integers(0, 500)), 0 if kw["causal"] else int(rng.integers(0, 50)))
+    if rng.random() < 0.3:
+        kw["softcap"] = float(rng.choice([5.0, 30.0]))
+    return dict(seed=seed, b=int(rng.integers(1, 5)), sq=sq, sk=int(rng.integers(1, 3000)), hq=hkv * g,
+                hkv=hkv, d=d, dtype=str(rng.choice(["bf16", "fp16"])), kw=kw,
+                alibi=bool(rng.random() < 0.25), splits=int(rng.choice([0, 1, 2, 3, 5, 8, 16])),
+                page=int(rng.choice([0, 0, 64, 128, 256])), dec_variant=int(rng.choice([0, 1, 2])))
+
+
+KVCACHE_SEEDS = list(range(5300, 5320))
+
+
+@pytest.mark.parametrize("seed", KVCACHE_SEEDS)
+def test_random_kvcache(seed, request):
+    c = _draw_kvcache(seed)
+    force_variants(request, dec=c["dec_variant"])
+    print(f"[case] random kvcache {c}", flush=True)
+    eng = _eng()
+    q, kc, vc, lens = W.make_kvcache(seed, c["b"], c["sq"], c["sk"], c["hq"], c["hkv"], c["d"], c["dtype"],
+                                     device="cuda", random_lengths=True, nan_tail=True)
+    kw = dict(c["kw"])
+    if c["alibi"]:
+        kw["alibi_slopes"] = W.alibi_slopes(c["hq"], c["b"], device="cuda")
+    table = None
+    if c["page"]:
+        kc, vc, table = W.page_cache(kc, vc, lens, c["page"], seed)
+    o, lse = eng.attn_fwd_kvcache(q, kc, vc, cache_seqlens=lens, num_splits=c["splits"], block_table=table, **kw)
+    torch.cuda.synchronize()
+    ref_kw = dict(kw)
+    if c["alibi"]:
+        ref_kw["alibi_slopes"] = np64(kw["alibi_slopes"])
+    ro, rl = oracle.attention_kvcache_ref(np64(q), np64(kc), np64(vc), lens.cpu().numpy(),
+                                          block_table=None if table is None else table.cpu().numpy(), **ref_kw)
+    gate_check(np64(o), ro, np64(lse), rl, c["dtype"], f"random kvcache {seed}")
