@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -18,16 +19,19 @@
 
 namespace attn {
 
-// Compute units of the current device (queried once per device).
+// Compute units of the current device (queried once per device; threads that
+// race on the first query store the same value).
 int compute_units() {
-  static int cus[64] = {0};
+  static std::atomic<int> cus[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
-    cus[dev] = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) ? n : 256;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    int q = 0;
+    n = (hipDeviceGetAttribute(&q, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && q > 0) ? q : 256;
+    cus[dev].store(n, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return n;
 }
 
 #ifdef ATTN_DEBUG_BUILD

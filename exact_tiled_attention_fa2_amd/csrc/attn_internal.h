@@ -115,7 +115,7 @@ struct DebugState {
   int fwd_variant;   // forward tile override (0: per-shape default)
   int dec_variant;   // decode tile override
   int bwd_variant;   // backward kernel-shape override
-  int last_block_k;  // KV step of the last forward tile launch on this thread
+  int last_block_k;  // KV step of the last forward tile launch (process-wide)
 };
 DebugState& debug_state();
 inline int fwd_variant() { return debug_state().fwd_variant; }

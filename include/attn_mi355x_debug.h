@@ -32,11 +32,13 @@ extern "C" {
  * 3 = 32-key steps with four LDS stages, 4 = exp2 (and softcap's tanh) on
  * the FMA pipe, 5 = 128 rows of 32-key steps at three waves per SIMD,
  * 6 = 256 rows storing O straight from the accumulators; head_dim 256:
- * 1 = 128 rows, 2 = 256 rows; head_dim 64: 1 = two waves per SIMD.  Decode:
- * 1 = 32-key steps with four stages, 2 = K/V copies with the default cache
- * policy.  Backward: 1 = dK/dV in two passes, 2 / 3 = dQ with 256 / 128
- * queries per workgroup.  Unknown values select the default.  Not
- * thread-safe; the setting is process-wide.
+ * 1 = 128 rows, 2 = 256 rows, 3 = 128 rows at two waves per SIMD, 4 = 256
+ * rows with the operand reads four ahead; head_dim 64: 1 = two waves per
+ * SIMD.  Decode: 1 = 32-key steps with four stages, 2 = K/V copies with the
+ * default cache policy.  Backward: 1 = dK/dV in two passes (head_dim 64 /
+ * 128), 2 / 3 = dQ with 256 / 128 queries per workgroup (64 / 128), 4 = dK/dV
+ * at one wave per SIMD (one pass at 64 / 128, two walks at 256).  Unknown
+ * values select the default.  Not thread-safe; the setting is process-wide.
  */
 void attn_debug_set_variants(int32_t fwd, int32_t dec, int32_t bwd);
 
