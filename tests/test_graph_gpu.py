@@ -1,4 +1,5 @@
-"""The entry points captured in a HIP graph (torch.cuda.CUDAGraph) and replayed.
+"""The entry points captured in a HIP graph (torch.cuda.CUDAGraph) and replayed, and run
+concurrently on two streams and from two host threads.
 
 The library allocates nothing and enqueues no memset or copy: a call is its kernel launches on the
 caller's stream, with the arguments fixed at the call.  So a captured call replays the same
@@ -135,3 +136,67 @@ def test_graph_bwd():
     q, k, v, o, lse, do = bufs
     _check_replays(lambda: eng.attn_bwd(q, k, v, o, lse, do, causal=True), bufs,
                    lambda i: make(341 + i), "attn_bwd bf16 D=128 causal")
+
+
+def test_two_streams_and_threads():
+    """The library keeps no per-call state: calls interleaved on two streams, and issued from two
+    host threads, give the same bits as the same calls one after another on one stream."""
+    import threading
+    eng = _eng()
+    print("[case] two streams / two threads: forward D=128 and D=256, backward, decode", flush=True)
+    qa, ka, va = W.make_dense(350, 2, 700, 700, 8, 2, 128, "bf16", device="cuda")
+    qb, kb, vb = W.make_dense(351, 1, 500, 800, 8, 4, 256, "fp16", device="cuda")
+    qc, kc, vc, lens = W.make_kvcache(352, 4, 1, 3000, 16, 4, 128, "bf16", device="cuda",
+                                      random_lengths=True, nan_tail=True)
+    do_a = W.randn16(tuple(qa.shape), "bf16", W._gen(353, "cuda"), "cuda")
+
+    def job_a():
+        o, l = eng.attn_fwd(qa, ka, va, causal=True)
+        return [o, l, *eng.attn_bwd(qa, ka, va, o, l, do_a, causal=True)]
+
+    def job_b():
+        o, l = eng.attn_fwd(qb, kb, vb, causal=True, softcap=20.0)
+        oc, lc = eng.attn_fwd_kvcache(qc, kc, vc, cache_seqlens=lens, num_splits=8)
+        return [o, l, oc, lc]
+
+    ref_a, ref_b = job_a(), job_b()
+    torch.cuda.synchronize()
+
+    def same(xs, ys):
+        return all(torch.equal(_bits(x), _bits(y)) for x, y in zip(xs, ys))
+
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            outs.append(("a", job_a()))
+        with torch.cuda.stream(s2):
+            outs.append(("b", job_b()))
+    torch.cuda.synchronize()
+    for tag, xs in outs:
+        assert same(xs, ref_a if tag == "a" else ref_b), f"stream run of job {tag} differs"
+
+    results, errors = {}, []
+
+    def worker(tag, fn):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                r = [fn() for _ in range(3)]
+            s.synchronize()
+            results[tag] = r
+        except Exception as e:  # surfaced below
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=("a", job_a)), threading.Thread(target=worker, args=("b", job_b))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for r in results["a"]:
+        assert same(r, ref_a), "threaded run of job a differs"
+    for r in results["b"]:
+        assert same(r, ref_b), "threaded run of job b differs"
