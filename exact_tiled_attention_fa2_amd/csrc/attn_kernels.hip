@@ -26,11 +26,11 @@
 //    transpose hands lane l the element l % 4 of the rows addressed by
 //    lanes 4j + l / 4 -- two such reads give the 8 keys of one lane.
 //  * K and V tiles (BK keys x D) stream HBM -> LDS with 16-byte
-//    global_load_lds copies (no VGPR staging), double-buffered in LDS (one
-//    barrier per KV step); the copies of step j+1 are in flight while step j
-//    computes.  16-byte chunks of a row are XOR-swizzled so that both the K
-//    reads (8/16 rows, same chunk) and the transposing V reads (4 rows x 2
-//    chunks) hit distinct banks.
+//    buffer_load ... lds copies (no VGPR staging, one 32-bit offset register
+//    per copy), double-buffered in LDS (one barrier per KV step); the copies
+//    of step j+1 are in flight while step j computes.  16-byte chunks of a
+//    row are XOR-swizzled so that both the K reads (8/16 rows, same chunk)
+//    and the transposing V reads (4 rows x 2 chunks) hit distinct banks.
 //  * Masks run only on KV steps that cross a mask edge for the wave; steps
 //    that are fully masked for a wave are skipped by that wave.
 //  * Keys at or beyond the valid length are never loaded (the last partial
@@ -907,9 +907,10 @@ hipError_t launch_fwd_t(FwdKernelParams p, hipStream_t stream) {
 // rows, 2 = 256 rows, 3 = 32-key steps with four stages, 4 = P (and
 // softcap's tanh) with exp2 on the FMA pipe, 5 = 128 rows of 32-key steps at
 // three waves per SIMD, 6 = 256 rows with O stored directly from the
-// accumulator layout; D = 256: 1 = 128 rows, 2 = 256 rows; D = 64: 1 = two
-// waves per SIMD.  Decode: 1 = 32-key steps with four stages, 2 = K/V copies
-// without the non-temporal policy.
+// accumulator layout; D = 256: 1 = 128 rows, 2 = 256 rows, 3 = 128 rows at
+// two waves per SIMD, 4 = 256 rows with the operand reads four ahead; D = 64:
+// 1 = two waves per SIMD.  Decode: 1 = 32-key steps with four stages, 2 = K/V
+// copies without the non-temporal policy.
 
 template <class Ty, bool CAP, bool AL>
 hipError_t launch_fwd_shape(const FwdKernelParams& p, int head_dim, hipStream_t stream) {
