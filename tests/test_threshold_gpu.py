@@ -25,7 +25,9 @@ from gpu_common import gpu_required, np64, run_jobs
 
 pytestmark = pytest.mark.gpu
 
-P_BOUND = 256.0 * (1.0 + 2.0 ** -16)   # exp2(8), with room for the fp32 exponent's rounding
+def p_bound(tau):
+    """exp2(tau), with room for the rounding of the fp32 exponent."""
+    return 2.0 ** tau * (1.0 + 2.0 ** -16)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -46,6 +48,11 @@ CASES = [
     ("cfg2_bf16_causal_2k", {}, 0.0, [(1, 2)]),
     ("cfg5b_fp16_d256_causal", {}, 8.0, [(0, 0), (3, 31)]),
     ("cfg4_bf16_gqa_window_softcap", {"q_scale": 8.0}, 8.0, [(0, 0), (1, 17)]),
+    # other thresholds the API accepts (0 to 15); at 15 in fp16 a lagging max lets P reach 2^15,
+    # which fp16 still holds (65504), and the sampled heads are also checked against the oracle
+    ("cfg2r_bf16_causal_2k_kramp", {}, 2.0, [(0, 0), (2, 9)]),
+    ("cfg2r_bf16_causal_2k_kramp", {}, 4.0, [(1, 5)]),
+    ("cfg2r_bf16_causal_2k_kramp", {"dtype": "fp16"}, 15.0, [(0, 0), (3, 15)]),
 ]
 
 
@@ -56,8 +63,10 @@ def test_threshold_counters_match_oracle(case):
     name, extra, tau, pairs = case
     c = W.WORKLOADS[name]
     print(f"[case] threshold counters {name} tau={tau} {extra}", flush=True)
+    extra = dict(extra)
+    dtype = extra.pop("dtype", c["dtype"])
     q, k, v = W.make_dense(c["seed"], c["batch"], c["seqlen_q"], c["seqlen_k"], c["heads_q"], c["heads_kv"],
-                           c["head_dim"], c["dtype"], k_ramp=c.get("k_ramp", False), device="cuda", **extra)
+                           c["head_dim"], dtype, k_ramp=c.get("k_ramp", False), device="cuda", **extra)
     kw = dict(causal=c["causal"], window=c["window"], softcap=c["softcap"], rescale_threshold=tau)
     o_rel, l_rel = _eng().attn_fwd(q, k, v, **kw)
     o_dbg, l_dbg, st = debug.attn_fwd_stats(q, k, v, **kw)
@@ -94,7 +103,7 @@ def test_threshold_counters_match_oracle(case):
         tot["rescales"] += int(resc.sum())
         tot["ref_skips"] += int(rs["skips"][0, 0].sum())
         tot["ref_rescales"] += int(rs["rescales"][0, 0].sum())
-        assert np.all(np.isfinite(kp)) and np.all(kp <= P_BOUND), (b, h, float(kp.max()))
+        assert np.all(np.isfinite(kp)) and np.all(kp <= p_bound(tau)), (b, h, float(kp.max()))
         # where the decisions agree, the largest P agrees to fp32 rounding
         rp = rs["max_p"][0, 0]
         assert np.all(np.abs(kp[same] - rp[same]) <= 1e-3 * np.maximum(rp[same], 1.0)), (b, h)
@@ -105,5 +114,17 @@ def test_threshold_counters_match_oracle(case):
     assert tot["skips"] > 0
     if c.get("k_ramp") or tau == 0.0:
         assert tot["rescales"] > 0
-    if tau == 8.0 and c.get("k_ramp"):
+    if tau >= 8.0 and c.get("k_ramp"):
         assert pmax > 16.0   # the lagging max lets P grow well above 1 on a rising max
+    if tau == 15.0:
+        def exact(job):
+            b, h = job
+            return oracle.attention_ref(np.ascontiguousarray(qn[b:b + 1, :, h:h + 1]),
+                                        np.ascontiguousarray(kn[b:b + 1, :, h // g:h // g + 1]),
+                                        np.ascontiguousarray(vn[b:b + 1, :, h // g:h // g + 1]),
+                                        causal=c["causal"], window=c["window"], softcap=c["softcap"])
+        on, ln = np64(o_rel), np64(l_rel)
+        for (b, h), (ro, rl) in zip(pairs, run_jobs(exact, pairs)):
+            r = oracle.compare(on[b:b + 1, :, h:h + 1], ro, ln[b:b + 1, h:h + 1], rl, dtype=dtype)
+            print(f"[parity] tau=15 {dtype} ({b}, {h}): {r}", flush=True)
+            assert r["pass"], (b, h, r)
