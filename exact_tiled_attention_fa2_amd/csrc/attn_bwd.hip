@@ -916,18 +916,40 @@ bwd_dkdv_pair_kernel(const BwdKernelParams p) {
       };
       // dS = P (dP - D) of step r - 1 from db and the P the P wave handed over,
       // then dK^T += Q^T dS.
-      auto finish = [&](int r, const char* q_prev, const float* dd_prev) __attribute__((always_inline)) {
+      // P and D of step r - 1, read from LDS ahead of the dP MFMAs (D = 64 / 128 order).
+      u32x4 pre_p[QB][2];
+      f32x4 pre_d[QB][4];
+      auto load_pd = [&](int r, const float* dd_prev) __attribute__((always_inline)) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          pre_p[qb][0] = lds_p[(r - 1) & 1][pair][qb][0][lane];
+          pre_p[qb][1] = lds_p[(r - 1) & 1][pair][qb][1][lane];
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4)
+            pre_d[qb][g4] = *reinterpret_cast<const f32x4*>(&dd_prev[32 * qb + 8 * g4 + 4 * hl]);
+        }
+      };
+      auto finish = [&](int r, const char* q_prev, const float* dd_prev, auto pre_c) __attribute__((always_inline)) {
+        constexpr bool PRE = decltype(pre_c)::value;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
           const f32x16& dp = db[qb];
-          const u32x4 h0 = lds_p[(r - 1) & 1][pair][qb][0][lane];
-          const u32x4 h1v = lds_p[(r - 1) & 1][pair][qb][1][lane];
+          u32x4 h0, h1v;
+          if constexpr (PRE) {
+            h0 = pre_p[qb][0];
+            h1v = pre_p[qb][1];
+          } else {
+            h0 = lds_p[(r - 1) & 1][pair][qb][0][lane];
+            h1v = lds_p[(r - 1) & 1][pair][qb][1][lane];
+          }
           const uint32_t ph[8] = {h0[0], h0[1], h0[2], h0[3], h1v[0], h1v[1], h1v[2], h1v[3]};
           uint32_t ps[8];
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4) {
             const int qo = 32 * qb + 8 * g4 + 4 * hl;
-            const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dd_prev[qo]);
+            f32x4 d4;
+            if constexpr (PRE) d4 = pre_d[qb][g4];
+            else d4 = *reinterpret_cast<const f32x4*>(&dd_prev[qo]);
             const f32x2 pa = unpack2<Ty>(ph[2 * g4]);
             const f32x2 pb = unpack2<Ty>(ph[2 * g4 + 1]);
             ps[2 * g4] = Ty::pack(pa[0] * (dp[4 * g4 + 0] - d4[0]), pa[1] * (dp[4 * g4 + 1] - d4[1]));
@@ -951,13 +973,14 @@ bwd_dkdv_pair_kernel(const BwdKernelParams p) {
         advance(h1, q1);
         if (r + 1 < n) issue(h1, q1, qbuf(std::integral_constant<int, FILL>{}), gbuf(std::integral_constant<int, FILL>{}));
         if constexpr (CARRY) {
-          if (carried) finish(r, qbuf(std::integral_constant<int, PREV>{}), lds_dd[PREV]);
+          if (carried) finish(r, qbuf(std::integral_constant<int, PREV>{}), lds_dd[PREV], std::false_type{});
           carried = r < n && sees(q0);
           if (carried) form_dp(gbuf(stc));
         } else {
           if (r >= 1 && sees(qp)) {
+            load_pd(r, lds_dd[PREV]);
             form_dp(gbuf(std::integral_constant<int, PREV>{}));
-            finish(r, qbuf(std::integral_constant<int, PREV>{}), lds_dd[PREV]);
+            finish(r, qbuf(std::integral_constant<int, PREV>{}), lds_dd[PREV], std::true_type{});
           }
         }
         barrier_vmem_le<0>();
