@@ -413,7 +413,7 @@ def main():
                                                                            "causal")}},
                 "roofline": {"bound": "mfma", "achieved": sec["value"], "peak": sec["peak"], "unit": "TFLOP/s",
                              "frac": sec["frac_of_mfma_peak"], "traffic": None,
-                             "kernel": "bwd_dot + bwd_dkdv + bwd_dq (one attn_bwd call per step)"},
+                             "kernel": "bwd_dq (with D) + bwd_dkdv (one attn_bwd call per step)"},
                 "warmup_steps_run": WARMUP_RUN.get(args.workload), "note": sec["note"]}
         print(json.dumps(line), flush=True)
         return

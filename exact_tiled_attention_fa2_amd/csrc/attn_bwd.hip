@@ -11,23 +11,24 @@
 // where g = 1 - tanh^2 is the softcap derivative (1 without softcap) and
 // D_i = sum_j P_ij dP_ij = <dO_i, O_i> is the softmax Jacobian's row term.
 //
-// Three kernels, in stream order, no atomics (every output element has one
+// Two kernels, in stream order, no atomics (every output element has one
 // owner, so the result is deterministic):
-//  * bwd_dot_kernel: D = rowsum(dO * O) in fp32 (HBM-bound, one pass).
-//  * bwd_dkdv_pair_kernel: one workgroup per 128-key tile of one KV head.  32 keys belong to
-//    a pair of waves on one SIMD that walks the query tiles of every query
-//    head of its GQA group: S = Q K^T and dP = dO V^T (A = Q / dO rows read
-//    from LDS, B = the keys' K / V rows held in VGPRs), the elementwise P and
-//    dS, then dV^T += dO^T P and dK^T += Q^T dS (A = Q^T / dO^T read
-//    transposed from the same LDS tiles with ds_read_b64_tr_b16, B = the
-//    packed P / dS registers); one wave of the pair forms S, P and dV, the
-//    other dP, dS and dK.  In these accumulators a lane holds one key.
-//  * bwd_dq_kernel: one workgroup per 128-query tile of one query head, the
-//    forward's orientation (a lane holds one query): S^T = K Q^T and
-//    dP^T = V dO^T (A = K / V rows from LDS, B = Q / dO held in VGPRs), the
-//    elementwise dS^T, then dQ^T += K^T dS^T (A = K^T read transposed from
-//    the K tile).  It recomputes S and dP, which the dK/dV kernel also
-//    forms: seven tile products instead of five, traded for no atomics.
+//  * bwd_dq_kernel: one workgroup per 128- or 256-query tile of one query
+//    head, the forward's orientation (a lane holds one query): S^T = K Q^T
+//    and dP^T = V dO^T (A = K / V rows from LDS, B = Q / dO held in VGPRs),
+//    the elementwise dS^T, then dQ^T += K^T dS^T (A = K^T read transposed
+//    from the K tile).  It recomputes S and dP, which the dK/dV kernel also
+//    forms: seven tile products instead of five, traded for no atomics.  It
+//    also forms D = rowsum(dO * O) in fp32 for its queries (from the dO rows
+//    it holds) and writes it for the next kernel.
+//  * bwd_dkdv_pair_kernel: one workgroup per 128-key tile of one KV head.
+//    32 keys belong to a pair of waves on one SIMD that walks the query tiles
+//    of every query head of its GQA group: S = Q K^T and dP = dO V^T (A = Q /
+//    dO rows read from LDS, B = the keys' K / V rows held in VGPRs), the
+//    elementwise P and dS, then dV^T += dO^T P and dK^T += Q^T dS (A = Q^T /
+//    dO^T read transposed from the same LDS tiles with ds_read_b64_tr_b16,
+//    B = the packed P / dS registers); one wave of the pair forms S, P and
+//    dV, the other dP, dS and dK.  In these accumulators a lane holds one key.
 // Q/dO (dK/dV kernels, three stages) and K/V (dQ kernel, two stages) tiles
 // stream HBM -> LDS with global_load_lds in the forward's XOR-swizzled layout.
 #include <hip/hip_runtime.h>
@@ -87,46 +88,6 @@ __device__ __forceinline__ TileRank tile_rank() {
   const int lin = (int)blockIdx.x + (int)gridDim.x * ((int)blockIdx.y + (int)gridDim.y * (int)blockIdx.z);
   const int c = lin % cols;
   return TileRank{lin / cols, c % (int)gridDim.y, c / (int)gridDim.y};
-}
-
-// ---------------------------------------------------------------- D = rowsum(dO * O)
-// D/8 consecutive lanes cover one (token, head) row, 8 elements each.
-template <class Ty, int D>
-__global__ void __launch_bounds__(256) bwd_dot_kernel(const BwdKernelParams p) {
-  constexpr int CHR = D / 8;
-  constexpr int RPB = 256 / CHR;
-  const int64_t nrows = (int64_t)p.total_q * p.heads_q;
-  const int64_t r = (int64_t)blockIdx.x * RPB + threadIdx.x / CHR;
-  const int c = threadIdx.x % CHR;
-  float acc = 0.0f;
-  int64_t didx = 0;
-  if (r < nrows) {
-    const int h = (int)(r % p.heads_q);
-    const int64_t tq = r / p.heads_q;  // dense: b * seqlen_q + row; varlen: packed row
-    int b = 0;
-    int64_t row = tq;
-    if (p.cu_seqlens_q == nullptr) {
-      b = (int)(tq / p.seqlen_q);
-      row = tq - (int64_t)b * p.seqlen_q;
-    }
-    const uint16_t* op = reinterpret_cast<const uint16_t*>(p.o) + b * p.o_batch + row * p.o_row +
-                         h * p.o_head + 8 * c;
-    const uint16_t* gp = reinterpret_cast<const uint16_t*>(p.dout) + b * p.do_batch + row * p.do_row +
-                         h * p.do_head + 8 * c;
-    const u32x4 ov = *reinterpret_cast<const u32x4*>(op);
-    const u32x4 gv = *reinterpret_cast<const u32x4*>(gp);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f32x2 a = unpack2<Ty>(ov[i]);
-      const f32x2 g = unpack2<Ty>(gv[i]);
-      acc = fmaf(a[0], g[0], acc);
-      acc = fmaf(a[1], g[1], acc);
-    }
-    didx = (int64_t)b * p.lse_batch + (int64_t)h * p.lse_head + row;
-  }
-#pragma unroll
-  for (int o = CHR / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
-  if (r < nrows && c == 0) p.dsum[didx] = acc;
 }
 
 // HBM -> LDS copy of a tile of NR rows (one 16-byte chunk per lane per copy)
@@ -667,6 +628,13 @@ bwd_dkdv_pair_kernel(const BwdKernelParams p) {
   __shared__ __attribute__((aligned(16))) u32x4 lds_p[2][NP][QB][2][64];
   __shared__ __attribute__((aligned(16))) float lds_lse[3][BQ];
   __shared__ __attribute__((aligned(16))) float lds_dd[3][BQ];
+  // At D = 256 the last NX fragments of each lane's K / V row sit in LDS (one
+  // slot per wave, written once) rather than in VGPRs: held in registers they
+  // overflowed the 256 available and were spilled, and a scratch reload, being
+  // a vector-memory load, waits for every copy in flight before it.
+  constexpr int NX = D > 128 ? 5 : 0;
+  constexpr int NR = DS - NX;  // fragments held in VGPRs
+  __shared__ __attribute__((aligned(16))) u32x4 lds_kx[NX > 0 ? NW * NX * 64 : 1];
   auto qbuf = [&](auto st) __attribute__((always_inline)) -> char* {
     constexpr int S = decltype(st)::value;
     if constexpr (S == 0) return lds_q0;
@@ -769,14 +737,19 @@ bwd_dkdv_pair_kernel(const BwdKernelParams p) {
   };
   // A = rows of a 32-query block of an LDS tile, B = the lane's K or V row
   // fragments: S (or dP) of the block, operand reads one MFMA ahead.
-  auto rows_product = [&](const char* tile, const u32x4 (&bf)[DS]) __attribute__((always_inline)) -> f32x16 {
+  auto rows_product = [&](const char* tile, const u32x4 (&bf)[NR]) __attribute__((always_inline)) -> f32x16 {
     f32x16 acc = f32x16{};
     u32x4 cur = *reinterpret_cast<const u32x4*>(tile + oo.row_off(0));
 #pragma unroll
     for (int t = 0; t < DS; ++t) {
       u32x4 nxt = cur;
       if (t + 1 < DS) nxt = *reinterpret_cast<const u32x4*>(tile + oo.row_off(t + 1));
-      acc = Ty::mfma(cur, bf[t], acc);
+      if constexpr (NX > 0) {
+        const u32x4 bt = t < NR ? bf[t < NR ? t : 0] : lds_kx[(wave * NX + (t - NR)) * 64 + lane];
+        acc = Ty::mfma(cur, bt, acc);
+      } else {
+        acc = Ty::mfma(cur, bf[t], acc);
+      }
       cur = nxt;
     }
     return acc;
@@ -803,6 +776,23 @@ bwd_dkdv_pair_kernel(const BwdKernelParams p) {
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
 
   if (n > 0) {
+    // The key's K row (P waves) or V row (dS waves), loaded before the first
+    // stage's wait so that it has arrived when the walk starts: a load still
+    // in flight at the loop entry would make the first step of every unrolled
+    // iteration wait for all outstanding copies, the next stage's included.
+    u32x4 kvf[NR];
+    [[maybe_unused]] u32x4 kvx[NX > 0 ? NX : 1];
+    {
+      const uint16_t* rp =
+          p_wave ? reinterpret_cast<const uint16_t*>(p.k) + b * p.k_batch + (int64_t)(sr.k_start + keyc) * p.k_row +
+                       kvh * p.k_head
+                 : reinterpret_cast<const uint16_t*>(p.v) + b * p.v_batch + (int64_t)(sr.k_start + keyc) * p.v_row +
+                       kvh * p.v_head;
+#pragma unroll
+      for (int t = 0; t < NR; ++t) kvf[t] = *reinterpret_cast<const u32x4*>(rp + 16 * t + 8 * hl);
+#pragma unroll
+      for (int t = NR; t < DS; ++t) kvx[t - NR] = *reinterpret_cast<const u32x4*>(rp + 16 * t + 8 * hl);
+    }
     {
       const int h = kvh * G, q0 = qblk_lo * BQ;
       issue_rows(h, q0);
@@ -810,13 +800,11 @@ bwd_dkdv_pair_kernel(const BwdKernelParams p) {
       stage_rows(0);
       barrier_vmem_le<0>();
     }
-    if (p_wave) {
-      u32x4 kf[DS];
+    // Only this wave reads its slot, and its LDS accesses complete in order.
 #pragma unroll
-      for (int t = 0; t < DS; ++t)
-        kf[t] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.k) + b * p.k_batch +
-                                                (int64_t)(sr.k_start + keyc) * p.k_row + kvh * p.k_head +
-                                                16 * t + 8 * hl);
+    for (int x = 0; x < NX; ++x) lds_kx[(wave * NX + x) * 64 + lane] = kvx[x];
+    if (p_wave) {
+      const u32x4(&kf)[NR] = kvf;
       int h = kvh * G, q0 = qblk_lo * BQ;
       // Step r computes on stage ST = r % 3 and fills stage (r + 1) % 3.
       auto step = [&](auto stc, int r) __attribute__((always_inline)) {
@@ -899,12 +887,7 @@ bwd_dkdv_pair_kernel(const BwdKernelParams p) {
       if (r < n + 1) step(std::integral_constant<int, 0>{}, r);
       if (r + 1 < n + 1) step(std::integral_constant<int, 1>{}, r + 1);
     } else {
-      u32x4 vf[DS];
-#pragma unroll
-      for (int t = 0; t < DS; ++t)
-        vf[t] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.v) + b * p.v_batch +
-                                                (int64_t)(sr.k_start + keyc) * p.v_row + kvh * p.v_head +
-                                                16 * t + 8 * hl);
+      const u32x4(&vf)[NR] = kvf;
       int h = kvh * G, q0 = qblk_lo * BQ;  // position of step r
       int qp = q0;                          // position of step r - 1
       f32x16 db[QB];                        // dP of the blocks of a step
@@ -1103,7 +1086,15 @@ bwd_dq_kernel(const BwdKernelParams p) {
   }
   const int64_t li = b * p.lse_batch + (int64_t)head * p.lse_head + sr.q_start + rowc;
   const float lse2 = q_valid ? lse_to_exp2(p.lse[li]) : INFINITY;
-  const float dd = q_valid ? p.dsum[li] : 0.0f;
+  // The O rows of this lane's query (the dO fragments' chunks), for D below.
+  u32x4 of[DS];
+  {
+    const uint16_t* op = reinterpret_cast<const uint16_t*>(p.o) + b * p.o_batch +
+                         (int64_t)(sr.q_start + rowc) * p.o_row + head * p.o_head;
+#pragma unroll
+    for (int t = 0; t < DS; ++t) of[t] = *reinterpret_cast<const u32x4*>(op + 16 * t + 8 * hl);
+  }
+  float dd = 0.0f;
   float slope = 0.0f;
   if constexpr (ALIBI) slope = p.alibi[b * p.alibi_bstride + head] * p.alibi_inv_scale;
 
@@ -1215,8 +1206,29 @@ bwd_dq_kernel(const BwdKernelParams p) {
     __syncthreads();
   };
 
+  if (n > 0) issue(blk_lo, lds_k0, lds_v0);
+  // D of this lane's query, <dO, O> in fp32, formed while the first K/V tile
+  // is on its way: lanes l and l + 32 hold the two halves of the row, so their
+  // partial sums meet in one swap; both lanes add the same two values and
+  // agree bit for bit.  The dK/dV kernel, launched after this one, reads it.
+  {
+    float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int t = 0; t < DS; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x2 a = unpack2<Ty>(of[t][i]);
+        const f32x2 g = unpack2<Ty>(gf[t][i]);
+        part[i] = fmaf(a[1], g[1], fmaf(a[0], g[0], part[i]));
+      }
+    const float half = (part[0] + part[1]) + (part[2] + part[3]);
+    const float whole = half + __shfl_xor(half, 32);
+    if (q_valid) {
+      dd = whole;
+      if (hl == 0) p.dsum[li] = whole;
+    }
+  }
   if (n > 0) {
-    issue(blk_lo, lds_k0, lds_v0);
     wait_vmem();
     __syncthreads();
     int r = 0;
@@ -1254,22 +1266,20 @@ bwd_dq_kernel(const BwdKernelParams p) {
 // per workgroup); 4 = dK/dV at one wave per SIMD (4 waves: one pass at head_dim
 // 64 / 128, two walks at 256).
 
-// D first (both gradient kernels read it), then dK/dV, then dQ; a kernel
-// whose grid would be empty (no queries, or no keys) is not launched.
+// dQ first (it also forms D, which the dK/dV kernel reads), then dK/dV; a
+// kernel whose grid would be empty (no queries, or no keys) is not launched.
 template <class Ty, int D, bool SOFTCAP, bool ALIBI>
 hipError_t launch_bwd_t(const BwdKernelParams& p, hipStream_t stream) {
-  if (p.total_q > 0 && p.seqlen_q > 0) {
-    constexpr int RPB = 256 / (D / 8);
-    const int64_t rows = (int64_t)p.total_q * p.heads_q;
-    const dim3 grid((unsigned)((rows + RPB - 1) / RPB));
-    hipLaunchKernelGGL((bwd_dot_kernel<Ty, D>), grid, dim3(256), 0, stream, p);
-  }
   if constexpr (D > 128) {
     // D = 256: the paired dK/dV kernel with 32-query steps (each wave's one
     // gradient and one K / V row set fill its 256 registers; a few values
     // spill to scratch, still 29% faster than two walks at one wave per SIMD,
     // which debug override 4 selects), and dQ at one wave per SIMD -- the Q and
     // dO rows and the dQ accumulators alone take 256 registers.
+    if (p.seqlen_q > 0) {
+      const dim3 grid((unsigned)((p.seqlen_q + 127) / 128), p.heads_q, p.batch);
+      hipLaunchKernelGGL((bwd_dq_kernel<Ty, D, SOFTCAP, ALIBI, 4, 1>), grid, dim3(256), 0, stream, p);
+    }
     if (p.seqlen_k > 0) {
       const dim3 grid((unsigned)((p.seqlen_k + 127) / 128), p.heads_kv, p.batch);
       bool launched = false;
@@ -1282,11 +1292,21 @@ hipError_t launch_bwd_t(const BwdKernelParams& p, hipStream_t stream) {
       if (!launched)
         hipLaunchKernelGGL((bwd_dkdv_pair_kernel<Ty, D, SOFTCAP, ALIBI>), grid, dim3(512), 0, stream, p);
     }
-    if (p.seqlen_q > 0) {
-      const dim3 grid((unsigned)((p.seqlen_q + 127) / 128), p.heads_q, p.batch);
-      hipLaunchKernelGGL((bwd_dq_kernel<Ty, D, SOFTCAP, ALIBI, 4, 1>), grid, dim3(256), 0, stream, p);
-    }
   } else {
+    if (p.seqlen_q > 0) {
+      // 256 queries per workgroup (8 waves, two per SIMD; half the K/V re-reads
+      // from L2) when that grid gives every CU two workgroups, else 128
+      // (twice the workgroups); the debug build's variant 2 forces 256, 3 forces 128.
+      const int64_t wgs256 = (int64_t)((p.seqlen_q + 255) / 256) * p.heads_q * p.batch;
+      const int v = kDebugBuild ? bwd_variant() : 0;
+      if (v == 2 || (v != 3 && wgs256 >= 2 * (int64_t)compute_units())) {
+        const dim3 grid((unsigned)((p.seqlen_q + 255) / 256), p.heads_q, p.batch);
+        hipLaunchKernelGGL((bwd_dq_kernel<Ty, D, SOFTCAP, ALIBI, 8>), grid, dim3(512), 0, stream, p);
+      } else {
+        const dim3 grid((unsigned)((p.seqlen_q + 127) / 128), p.heads_q, p.batch);
+        hipLaunchKernelGGL((bwd_dq_kernel<Ty, D, SOFTCAP, ALIBI>), grid, dim3(256), 0, stream, p);
+      }
+    }
     if (p.seqlen_k > 0) {
       // Default: the paired kernel (eight waves, two per SIMD; 128 keys per
       // workgroup).  Debug overrides: 1 = two passes at eight waves (256 keys),
@@ -1306,20 +1326,6 @@ hipError_t launch_bwd_t(const BwdKernelParams& p, hipStream_t stream) {
       if (!launched) {
         const dim3 grid((unsigned)((p.seqlen_k + 127) / 128), p.heads_kv, p.batch);
         hipLaunchKernelGGL((bwd_dkdv_pair_kernel<Ty, D, SOFTCAP, ALIBI>), grid, dim3(512), 0, stream, p);
-      }
-    }
-    if (p.seqlen_q > 0) {
-      // 256 queries per workgroup (8 waves, two per SIMD; half the K/V re-reads
-      // from L2) when that grid gives every CU two workgroups, else 128
-      // (twice the workgroups); the debug build's variant 2 forces 256, 3 forces 128.
-      const int64_t wgs256 = (int64_t)((p.seqlen_q + 255) / 256) * p.heads_q * p.batch;
-      const int v = kDebugBuild ? bwd_variant() : 0;
-      if (v == 2 || (v != 3 && wgs256 >= 2 * (int64_t)compute_units())) {
-        const dim3 grid((unsigned)((p.seqlen_q + 255) / 256), p.heads_q, p.batch);
-        hipLaunchKernelGGL((bwd_dq_kernel<Ty, D, SOFTCAP, ALIBI, 8>), grid, dim3(512), 0, stream, p);
-      } else {
-        const dim3 grid((unsigned)((p.seqlen_q + 127) / 128), p.heads_q, p.batch);
-        hipLaunchKernelGGL((bwd_dq_kernel<Ty, D, SOFTCAP, ALIBI>), grid, dim3(256), 0, stream, p);
       }
     }
   }
