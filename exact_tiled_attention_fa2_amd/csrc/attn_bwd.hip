@@ -1085,7 +1085,8 @@ bwd_dq_kernel(const BwdKernelParams p) {
     }
   }
   const int64_t li = b * p.lse_batch + (int64_t)head * p.lse_head + sr.q_start + rowc;
-  const float lse2 = q_valid ? lse_to_exp2(p.lse[li]) : INFINITY;
+  const float lse_row = p.lse[li];  // unconditional (rowc is a valid row): no wait before the loads below
+  const float lse2 = q_valid ? lse_to_exp2(lse_row) : INFINITY;
   // The O rows of this lane's query (the dO fragments' chunks), for D below.
   u32x4 of[DS];
   {
@@ -1207,10 +1208,10 @@ bwd_dq_kernel(const BwdKernelParams p) {
   };
 
   if (n > 0) issue(blk_lo, lds_k0, lds_v0);
-  // D of this lane's query, <dO, O> in fp32, formed while the first K/V tile
-  // is on its way: lanes l and l + 32 hold the two halves of the row, so their
-  // partial sums meet in one swap; both lanes add the same two values and
-  // agree bit for bit.  The dK/dV kernel, launched after this one, reads it.
+  wait_vmem();  // Q, dO, O and the first K/V tile: one latency for all of them
+  // D of this lane's query, <dO, O> in fp32: lanes l and l + 32 hold the two
+  // halves of the row, so their partial sums meet in one swap; both lanes add
+  // the same two values and agree bit for bit.
   {
     float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -1225,12 +1226,13 @@ bwd_dq_kernel(const BwdKernelParams p) {
     const float whole = half + __shfl_xor(half, 32);
     if (q_valid) {
       dd = whole;
-      if (hl == 0) p.dsum[li] = whole;
+      if (hl == 0) p.dsum[li] = whole;  // for the dK/dV kernel
     }
   }
   if (n > 0) {
-    wait_vmem();
-    __syncthreads();
+    // The copies have landed (wait above); only the D store may still be in
+    // flight, and nothing in this kernel reads it.
+    barrier_vmem_le<1>();
     int r = 0;
     for (; r + 2 <= n; r += 2) {
       step(std::integral_constant<int, 0>{}, r);
