@@ -443,7 +443,6 @@ int attn_bwd(const attn_bwd_args* a, void* workspace, size_t workspace_bytes, vo
   p.lse_head = a->seqlen_q;
   p.batch = a->batch; p.seqlen_q = a->seqlen_q; p.seqlen_k = a->seqlen_k;
   p.heads_q = a->heads_q; p.heads_kv = a->heads_kv; p.group = a->heads_q / a->heads_kv;
-  p.total_q = (int32_t)std::min<int64_t>((int64_t)a->batch * a->seqlen_q, INT32_MAX);
   if ((int64_t)a->batch * a->seqlen_q > INT32_MAX) return ATTN_E_SHAPE;
   resolve_bwd_opts(a->opts, a->head_dim, p);
   return launch_status(attn::launch_bwd(p, a->dtype, a->head_dim, (hipStream_t)stream));
@@ -501,7 +500,6 @@ int attn_bwd_varlen(const attn_bwd_varlen_args* a, void* workspace, size_t works
   p.lse_head = a->total_q;
   p.batch = a->batch; p.seqlen_q = a->max_seqlen_q; p.seqlen_k = a->max_seqlen_k;
   p.heads_q = a->heads_q; p.heads_kv = a->heads_kv; p.group = a->heads_q / a->heads_kv;
-  p.total_q = a->total_q;
   resolve_bwd_opts(a->opts, a->head_dim, p);
   return launch_status(attn::launch_bwd(p, a->dtype, a->head_dim, (hipStream_t)stream));
 }

@@ -68,7 +68,7 @@ struct BwdKernelParams {
   const void* o;
   const void* dout;
   const float* lse;
-  float* dsum;          // workspace, written by the dot kernel
+  float* dsum;          // workspace: D, written by the dQ kernel, read by the dK/dV kernel
   void* dq;
   void* dk;
   void* dv;
@@ -84,7 +84,6 @@ struct BwdKernelParams {
   int64_t dv_batch, dv_row, dv_head;
   int64_t lse_batch, lse_head;
   int32_t batch, seqlen_q, seqlen_k, heads_q, heads_kv, group;
-  int32_t total_q;       // rows of the dot kernel's sweep: batch * seqlen_q (dense) or total_q (varlen)
   int32_t window_left, window_right;  // causal folded into window_right
   float scale;           // softmax scale (dQ, dK = scale * sum of dS products)
   float scale_log2;      // raw (or capped) score -> exp2 argument, as in the forward
