@@ -793,6 +793,11 @@ bwd_dkdv_pair_kernel(const BwdKernelParams p) {
 #pragma unroll
       for (int t = NR; t < DS; ++t) kvx[t - NR] = *reinterpret_cast<const u32x4*>(rp + 16 * t + 8 * hl);
     }
+    // The ALiBi slope of the first step's query head, loaded before the same
+    // wait; each step then loads the next step's slope before its copies, so
+    // no slope load is outstanding behind them when the scores need it.
+    [[maybe_unused]] float slope_raw = 0.0f;
+    if constexpr (ALIBI) slope_raw = p.alibi[b * p.alibi_bstride + kvh * G];
     {
       const int h = kvh * G, q0 = qblk_lo * BQ;
       issue_rows(h, q0);
@@ -812,7 +817,9 @@ bwd_dkdv_pair_kernel(const BwdKernelParams p) {
         constexpr int FILL = (ST + 1) % 3;
         int h1 = h, q1 = q0;
         advance(h1, q1);
+        [[maybe_unused]] float slope_raw_next = 0.0f;
         if (r + 1 < n) {
+          if constexpr (ALIBI) slope_raw_next = p.alibi[b * p.alibi_bstride + h1];
           issue_rows(h1, q1);
           issue(h1, q1, qbuf(std::integral_constant<int, FILL>{}), gbuf(std::integral_constant<int, FILL>{}));
         }
@@ -820,7 +827,7 @@ bwd_dkdv_pair_kernel(const BwdKernelParams p) {
           const char* q_cur = qbuf(stc);
           const char* g_cur = gbuf(stc);
           float slope = 0.0f;
-          if constexpr (ALIBI) slope = p.alibi[b * p.alibi_bstride + h] * p.alibi_inv_scale;
+          if constexpr (ALIBI) slope = slope_raw * p.alibi_inv_scale;
           const bool full = full_step(q0);
           // S of every 32-query block first, then each block's P, hand-over and dV.
           f32x16 sb[QB];
@@ -877,6 +884,7 @@ bwd_dkdv_pair_kernel(const BwdKernelParams p) {
         barrier_vmem_le<0>();
         h = h1;
         q0 = q1;
+        if constexpr (ALIBI) slope_raw = slope_raw_next;
       };
       int r = 0;
       for (; r + 3 <= n + 1; r += 3) {
