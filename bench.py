@@ -274,7 +274,7 @@ def bench_bwd(name, steps, warmup, torch, eng, W):
     peak = PEAK_MFMA_TFLOPS[c["dtype"]]
     return {"workload": name, "ms_per_step": round(ms, 4), "value": round(tflops, 2), "unit": "TFLOP/s",
             "frac_of_mfma_peak": round(tflops / peak, 4), "peak": peak, "flops_per_step": flops,
-            "note": "backward (D, dK/dV, dQ kernels); algorithmic FLOPs = 10*D per visible pair "
+            "note": "backward (dQ kernel, which also forms D, then dK/dV); algorithmic FLOPs = 10*D per visible pair "
                     "(five tile products); the kernels run seven (S and dP formed twice, no atomics)"}
 
 
