@@ -13,7 +13,7 @@ workload as a secondary measurement with its own fraction of roofline
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                   [--warmup-floor-ms F] [--no-cpu-baseline] [--no-secondary]
-                  [--mode copy|gemm]
+                  [--mode copy|gemm|mfma]
 
 Warm-up: W untimed steps, then more untimed steps until at least F ms
 (default 200) of wall time has gone into them -- the GPU clock settles only
@@ -24,6 +24,8 @@ the calibration kernel for the HBM byte counters (FETCH_SIZE / WRITE_SIZE).
 and wide shapes) with the same warm-up: the matrix-core rate this board
 sustains once its clock has settled under full load, context for the
 fraction of the published peak (not a bound the attention kernel is held to).
+``--mode mfma`` does the same with nothing but back-to-back MFMAs (the debug
+build's calibration kernel), on random and on zero operands.
 """
 
 import argparse
@@ -315,6 +317,39 @@ def run_copy(steps, warmup, torch):
                       "GBps_read_plus_write": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
+def run_mfma(steps, warmup, torch):
+    """The matrix-core rate this board sustains with nothing but back-to-back MFMAs (debug build's
+    calibration kernel; no memory traffic, no other vector work), on random and on zero operands."""
+    import ctypes
+    from exact_tiled_attention_fa2_amd import debug
+    h = debug.debug_lib()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks, iters = 3 * cus, 20000  # 129 registers per lane: three waves per SIMD, one full round
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    for name, tdt, code in (("bf16", torch.bfloat16, 1), ("fp16", torch.float16, 0)):
+        for fill in ("random", "zero"):
+            g = torch.Generator(device="cuda")
+            g.manual_seed(7)
+            ops = (torch.randn(4096, device="cuda", generator=g) if fill == "random"
+                   else torch.zeros(4096, device="cuda")).to(tdt)
+
+            def step():
+                rc = h.attn_debug_calib_mfma(code, ctypes.c_void_p(ops.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                                             blocks, iters, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+                if rc != 0:
+                    raise RuntimeError(f"attn_debug_calib_mfma returned {rc}")
+
+            ms = time_region(step, steps, warmup, torch)
+            flops = float(blocks) * 4 * iters * 16 * 32768
+            tf = flops / (ms * 1e-3) / 1e12
+            print(json.dumps({"mode": "mfma", "dtype": name, "operands": fill, "workgroups": blocks, "iters": iters,
+                              "ms": round(ms, 4), "tflops": round(tf, 1),
+                              "frac_of_published_peak": round(tf / PEAK_MFMA_TFLOPS[name], 4),
+                              "finite": bool(torch.isfinite(out).all().item()),
+                              "note": "32x32x16 MFMAs only, four independent accumulators per wave"}),
+                  flush=True)
+
+
 def run_gemm(steps, warmup, torch):
     for dt in (torch.float16, torch.bfloat16):
         for m, n, k in ((8192, 8192, 8192), (16384, 16384, 8192), (8192, 8192, 16384)):
@@ -357,7 +392,7 @@ def main():
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--mode", default="attn", choices=["attn", "copy", "gemm", "pages-latency"])
+    ap.add_argument("--mode", default="attn", choices=["attn", "copy", "gemm", "mfma", "pages-latency"])
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -381,6 +416,9 @@ def main():
         return
     if args.mode == "gemm":
         run_gemm(args.steps, args.warmup, torch)
+        return
+    if args.mode == "mfma":
+        run_mfma(args.steps, args.warmup, torch)
         return
     if args.mode == "pages-latency":
         run_pages_latency(args.steps, args.warmup, torch, eng, W)

@@ -5,8 +5,9 @@ Two shared objects are built next to this file from the same sources:
 
 * ``libattn_mi355x.so`` -- the release library the binding loads;
 * ``libattn_mi355x_debug.so`` -- the same entry points plus those of
-  ``include/attn_mi355x_debug.h`` (tile-shape overrides and per-row
-  rescale counters), compiled with ``ATTN_DEBUG_BUILD``.
+  ``include/attn_mi355x_debug.h`` (tile-shape overrides, per-row rescale
+  counters and a matrix-core rate calibration), compiled with
+  ``ATTN_DEBUG_BUILD`` (``attn_calib.hip`` compiles to nothing without it).
 
 Each kernel source is compiled once per 16-bit type (``ATTN_TU_DTYPE``) so
 that the translation units build in parallel.
@@ -28,7 +29,7 @@ DEBUG_LIB_PATH = os.path.join(PKG_DIR, DEBUG_LIB_NAME)
 # (source, extra defines) of one library; the kernel sources once per dtype.
 UNITS = [("attn_kernels.hip", ["-DATTN_TU_DTYPE=0"]), ("attn_kernels.hip", ["-DATTN_TU_DTYPE=1"]),
          ("attn_bwd.hip", ["-DATTN_TU_DTYPE=0"]), ("attn_bwd.hip", ["-DATTN_TU_DTYPE=1"]),
-         ("attn_api.cpp", [])]
+         ("attn_api.cpp", []), ("attn_calib.hip", [])]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

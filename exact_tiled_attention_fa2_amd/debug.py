@@ -1,8 +1,9 @@
 """ctypes access to the debug build, libattn_mi355x_debug.so (tests and sweeps).
 
 The debug build has every entry point of the release library plus those of
-``include/attn_mi355x_debug.h``: tile-shape overrides and ``attn_fwd_stats``,
-the forward with per-row counters of the rescale-threshold rule.  Nothing in
+``include/attn_mi355x_debug.h``: tile-shape overrides, ``attn_fwd_stats``,
+the forward with per-row counters of the rescale-threshold rule, and
+``attn_debug_calib_mfma``, a matrix-core rate calibration.  Nothing in
 the product path imports this module.
 
 ``forced_variants(fwd, dec, bwd)`` routes the binding's entry points to the
@@ -35,6 +36,9 @@ def debug_lib():
         h.attn_debug_last_block_k.restype = ctypes.c_int32
         h.attn_fwd_stats.argtypes = [ctypes.POINTER(binding.FwdArgs), ctypes.c_void_p, ctypes.c_void_p]
         h.attn_fwd_stats.restype = ctypes.c_int
+        h.attn_debug_calib_mfma.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                            ctypes.c_int32, ctypes.c_void_p]
+        h.attn_debug_calib_mfma.restype = ctypes.c_int
         _DEBUG = h
     return _DEBUG
 

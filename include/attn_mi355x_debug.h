@@ -11,8 +11,9 @@
  * section 1.2: the rescale of O and the row sum is skipped while the row max
  * rises by at most the threshold, and the max then lags, so P stays at or
  * below exp2(threshold) = 256; release page "FA2 2.9.0 Kernel Changes in
- * v1.2", section 3: the first KV step never skips), and to run the tile
- * shapes the release library's per-shape choice does not pick.
+ * v1.2", section 3: the first KV step never skips), to run the tile
+ * shapes the release library's per-shape choice does not pick, and to
+ * measure the matrix-core rate the board sustains.
  */
 #ifndef ATTN_MI355X_DEBUG_H
 #define ATTN_MI355X_DEBUG_H
@@ -58,6 +59,26 @@ int32_t attn_debug_last_block_k(void);
  * Returns ATTN_E_NULL / ATTN_E_ALIGN for a bad row_stats, else as attn_fwd.
  */
 int attn_fwd_stats(const attn_fwd_args* args, uint32_t* row_stats, void* stream);
+
+/*
+ * Matrix-core rate calibration; no attention work.  Launches `blocks`
+ * workgroups of 256 threads (4 waves); every wave issues `iters` x 16 dense
+ * 32x32x16 MFMAs of `dtype` (ATTN_DTYPE_F16 / _BF16) into four independent
+ * accumulators, on operands it reads once from `operands`, and each thread
+ * writes the sum of its accumulators to `out` (so the work is kept).
+ *   operands: device, 16-byte aligned, 8 KiB: 64 lanes x 8 16-byte chunks,
+ *     lane-major; chunks 0-3 are a lane's A fragments, 4-7 its B fragments
+ *     (16-bit values of `dtype`; random values or zeros, which draw less
+ *     power).  Read only.
+ *   out: device float [blocks * 256], 4-byte aligned; overwritten.
+ * Work per call: blocks * 4 * iters * 16 * 32768 FLOP.  Asynchronous on
+ * `stream`.  Returns ATTN_E_NULL, ATTN_E_ALIGN, ATTN_E_SHAPE (blocks or
+ * iters < 1), ATTN_E_UNSUPPORTED (unknown dtype), ATTN_E_LAUNCH, else
+ * ATTN_OK.  Used for the board's sustained matrix-core rate under its power
+ * limit, the context for the published peak the kernels are priced against.
+ */
+int attn_debug_calib_mfma(int32_t dtype, const void* operands, float* out, int32_t blocks, int32_t iters,
+                          void* stream);
 
 #ifdef __cplusplus
 }
