@@ -76,10 +76,16 @@ DENSE = [
     (86, 1, 300, 100, 2, 2, 128, "bf16", dict(causal=True)),          # rows with no key
     (87, 1, 64, 64, 2, 1, 128, "fp16", dict(causal=False, window=(0, 0))),
     (88, 2, 97, 161, 6, 3, 64, "bf16", dict(causal=False, softcap=5.0, alibi=True)),
+    # ALiBi over many steps whose query head changes within a dK/dV walk (the slope of the next
+    # step is loaded one step ahead)
+    (89, 1, 700, 700, 8, 2, 128, "bf16", dict(causal=True, alibi=True)),
     # head_dim 256 (32-query steps in the paired dK/dV kernel; dQ at one wave per SIMD)
     (181, 1, 257, 257, 4, 2, 256, "fp16", dict(causal=True)),
     (182, 2, 190, 300, 4, 1, 256, "bf16", dict(causal=False, softcap=20.0, alibi=True)),
     (183, 1, 300, 200, 2, 2, 256, "fp16", dict(causal=True, window=(64, 0))),   # rows with no key
+    # long walks at head_dim 256 (K / V fragments partly in LDS) with every score transform
+    (184, 1, 1100, 1100, 8, 2, 256, "bf16", dict(causal=True, softcap=30.0, alibi=True)),
+    (185, 1, 900, 1300, 4, 4, 256, "fp16", dict(causal=False, alibi=True)),
 ]
 
 
